@@ -1,0 +1,113 @@
+"""fp64 CPU oracle for the group-sparse FFN (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. It loads `liboracle.so`, built from `wide_oracle.c` by
+`build_oracle()` with plain gcc (no HIP), and exposes numpy-level wrappers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wide_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math so no reassociation)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build_oracle(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_reorder.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.oracle_reorder.restype = ctypes.c_int
+        lib.oracle_ffn.argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, i64, p, p]
+        lib.oracle_ffn.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_f32(x) -> np.ndarray:
+    """Exact float32 copy of a float tensor/array (bf16 widens exactly)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu").float().numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _as_u8(m) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(m, torch.Tensor):
+            m = m.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(m, dtype=np.uint8))
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def reorder(mask, tile: int):
+    """Per-group stable partition -> (perm [ng, T] int32, counts [ng], padded [ng])."""
+    m = _as_u8(mask)
+    T, ng = m.shape
+    perm = np.empty((ng, T), dtype=np.int32)
+    counts = np.empty(ng, dtype=np.int32)
+    padded = np.empty(ng, dtype=np.int32)
+    rc = _load().oracle_reorder(_ptr(m), T, ng, tile, _ptr(perm), _ptr(counts), _ptr(padded))
+    if rc != 0:
+        raise ValueError(f"oracle_reorder rejected its arguments (rc={rc})")
+    return perm, counts, padded
+
+
+def ffn(X, Wg, Wu, Wd, mask, G: int, rows=None):
+    """Masked SwiGLU FFN in fp64 -> (H [n, d_ff], Y [n, d]) for all tokens or `rows`."""
+    x, wg, wu, wd = _as_f32(X), _as_f32(Wg), _as_f32(Wu), _as_f32(Wd)
+    m = _as_u8(mask)
+    T, d = x.shape
+    d_ff = wg.shape[0]
+    if wg.shape != (d_ff, d) or wu.shape != (d_ff, d) or wd.shape != (d, d_ff):
+        raise ValueError("weight shapes must be Wg,Wu [d_ff,d] and Wd [d,d_ff]")
+    if m.shape != (T, d_ff // G):
+        raise ValueError("mask must be [T, d_ff/G]")
+    if rows is None:
+        r = None
+        n = T
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = r.shape[0]
+    H = np.empty((n, d_ff), dtype=np.float64)
+    Y = np.empty((n, d), dtype=np.float64)
+    rc = _load().oracle_ffn(_ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(m), T, d, d_ff, G,
+                            None if r is None else _ptr(r), n, _ptr(H), _ptr(Y))
+    if rc != 0:
+        raise ValueError(f"oracle_ffn rejected its arguments (rc={rc})")
+    return H, Y

@@ -1,0 +1,117 @@
+/*
+ * fp64 CPU oracle for WIDE's token-wise group-sparse SwiGLU FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library calls, links or
+ * loads this file; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do. It shares no code, header or table with the HIP path.
+ *
+ * What it computes is the plain definition, written out with no blocking,
+ * fusion or reordering:
+ *
+ *   Groups: the FFN intermediate dimension d_ff is cut into contiguous groups
+ *   of G channels; group g holds channels [g*G, (g+1)*G). One binary mask
+ *   matrix M[T, ngroups] covers the whole FFN layer, and a token either keeps
+ *   or skips each group.
+ *     (WIDE, ai.info summary, "Methodology in Plain English" / "What gets
+ *      pruned"; WIDE paper, Sec. 3.1 "Preliminaries")
+ *
+ *   Per token t and channel c in group g:
+ *     H[t,c] = silu(X[t,:].Wg[c,:]) * (X[t,:].Wu[c,:])   if M[t,g] != 0
+ *     H[t,c] = 0                                        otherwise (select)
+ *   Y[t,n] = sum_c Wd[n,c] * H[t,c]
+ *   with silu(a) = a / (1 + exp(-a)), no biases. Weights are stored [out, in]
+ *   (C = A B^T, A [M,K], B [N,K]: WIDE paper Sec. 3.2 and App. B
+ *   "Implementation of GEMM-MN"), and the pruned projections are gate/up on the
+ *   N axis and down on the K axis (App. B, GEMM-MN and GEMM-K).
+ *
+ *   Mask reordering: for every group, the tokens are sorted so that active
+ *   rows form a contiguous prefix (ai.info summary, "How the speedups are
+ *   obtained"; WIDE paper Sec. 1, "tile-aligned prefixes"). The reading used
+ *   here is a stable partition of [0, T): active tokens in ascending order,
+ *   then inactive tokens in ascending order; counts[g] is the number of
+ *   active tokens and padded[g] = ceil(counts[g] / tile) * tile.
+ *
+ * Inputs are float32 arrays whose values are exact (bf16 values are exactly
+ * representable in float32); every product and sum is taken in double.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+
+/* Stable partition of each mask column into active-then-inactive tokens. */
+int oracle_reorder(const uint8_t* mask, int64_t T, int64_t ngroups, int64_t tile,
+                   int32_t* perm, int32_t* counts, int32_t* padded) {
+  if (!mask || !perm || !counts || !padded || T < 0 || ngroups <= 0 || tile <= 0)
+    return ORACLE_BAD_ARG;
+  for (int64_t g = 0; g < ngroups; ++g) {
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; ++t)
+      if (mask[t * ngroups + g] != 0) perm[g * T + n++] = (int32_t)t;
+    int64_t count = n;
+    for (int64_t t = 0; t < T; ++t)
+      if (mask[t * ngroups + g] == 0) perm[g * T + n++] = (int32_t)t;
+    counts[g] = (int32_t)count;
+    padded[g] = (int32_t)(((count + tile - 1) / tile) * tile);
+  }
+  return ORACLE_OK;
+}
+
+static double silu(double a) { return a / (1.0 + exp(-a)); }
+
+/*
+ * Masked SwiGLU FFN for the tokens listed in rows[0..nrows) (rows == NULL
+ * means tokens 0..nrows-1). Output row r of H ([nrows, d_ff]) and of Y
+ * ([nrows, d]) belongs to token rows[r]. H is required: the function
+ * allocates nothing and forms Y from the H row it has just written.
+ */
+int oracle_ffn(const float* X, const float* Wg, const float* Wu, const float* Wd,
+               const uint8_t* mask, int64_t T, int64_t d, int64_t d_ff, int64_t G,
+               const int64_t* rows, int64_t nrows, double* H, double* Y) {
+  if (!X || !Wg || !Wu || !Wd || !mask || !H || !Y) return ORACLE_BAD_ARG;
+  if (T < 0 || d <= 0 || d_ff <= 0 || G <= 0 || d_ff % G != 0 || nrows < 0)
+    return ORACLE_BAD_ARG;
+  const int64_t ng = d_ff / G;
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t t = rows ? rows[r] : r;
+    if (t < 0 || t >= T) return ORACLE_BAD_ARG;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t t = rows ? rows[r] : r;
+    const float* x = X + t * d;
+    double* h = H + r * d_ff;
+    for (int64_t c = 0; c < d_ff; ++c) {
+      const int64_t g = c / G;
+      if (mask[t * ng + g] != 0) {
+        double a = 0.0, b = 0.0;
+        for (int64_t k = 0; k < d; ++k) {
+          a += (double)x[k] * (double)Wg[c * d + k];
+          b += (double)x[k] * (double)Wu[c * d + k];
+        }
+        h[c] = silu(a) * b;
+      } else {
+        h[c] = 0.0;
+      }
+    }
+    double* y = Y + r * d;
+    for (int64_t n = 0; n < d; ++n) {
+      double s = 0.0;
+      for (int64_t c = 0; c < d_ff; ++c) s += (double)Wd[n * d_ff + c] * h[c];
+      y[n] = s;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
