@@ -1,0 +1,124 @@
+"""Group-sparse (token-wise dynamic-width) SwiGLU FFN for MI355X.
+
+Thin Python binding over libwide.so: it checks devices, dtypes and shapes,
+allocates outputs and workspace with torch, and passes raw device pointers
+and torch's current HIP stream to the C ABI. Every step of the computation
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (WIDE_BF16, WIDE_DECODE_T_LIMIT, WIDE_F32, WIDE_FLAG_FORCE_DECODE,
+                   WIDE_FLAG_FORCE_PREFILL, WIDE_STAGE_DECODE_DOWN, WIDE_STAGE_DECODE_GATE_UP,
+                   WIDE_STAGE_DOWN, WIDE_STAGE_GATE_UP, WIDE_STAGE_REORDER, WIDE_TOKEN_TILE,
+                   WideError)
+
+__all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decode_max_t",
+           "FfnCall", "WideError", "WIDE_TOKEN_TILE", "WIDE_DECODE_T_LIMIT",
+           "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
+           "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
+           "WIDE_STAGE_DECODE_DOWN"]
+
+_DTYPES = {torch.bfloat16: WIDE_BF16, torch.float32: WIDE_F32}
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_cuda(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def decode_max_t() -> int:
+    return int(_lib.load().wide_decode_max_t())
+
+
+def workspace_size(T: int, d: int, d_ff: int, G: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().wide_ffn_workspace_size(T, d, d_ff, G, _DTYPES[dtype]))
+
+
+def reorder_masks(mask: torch.Tensor, tile: int = WIDE_TOKEN_TILE):
+    """Per-group stable active-first partition -> (perm [ng, T], counts [ng], padded [ng]) int32."""
+    _need_cuda("mask", mask)
+    if mask.dtype != torch.uint8 or mask.dim() != 2:
+        raise ValueError("mask must be a 2-D uint8 tensor [T, ngroups]")
+    T, ng = mask.shape
+    perm = torch.empty((ng, T), dtype=torch.int32, device=mask.device)
+    counts = torch.empty(ng, dtype=torch.int32, device=mask.device)
+    padded = torch.empty(ng, dtype=torch.int32, device=mask.device)
+    _lib.check(_lib.load().wide_reorder_masks(mask.data_ptr(), T, ng, tile, perm.data_ptr(),
+                                              counts.data_ptr(), padded.data_ptr(),
+                                              _stream_ptr(mask.device)))
+    return perm, counts, padded
+
+
+class FfnCall:
+    """Validated arguments of one FFN call, with outputs and workspace allocated once.
+
+    `run()` enqueues wide_ffn_forward; `stage(s)` enqueues one stage of it
+    with the same arguments (used to time the kernels separately).
+    """
+
+    def __init__(self, X, Wg, Wu, Wd, mask, G: int, return_h: bool = False, flags: int = 0,
+                 Y: Optional[torch.Tensor] = None, H: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+        for name, t in (("X", X), ("Wgate", Wg), ("Wup", Wu), ("Wdown", Wd), ("mask", mask)):
+            _need_cuda(name, t)
+        if X.dtype not in _DTYPES or any(w.dtype != X.dtype for w in (Wg, Wu, Wd)):
+            raise ValueError("X and the weights must share one dtype, bfloat16 or float32")
+        if mask.dtype != torch.uint8:
+            raise ValueError("mask must be uint8")
+        T, d = X.shape
+        d_ff = Wg.shape[0]
+        if Wg.shape != (d_ff, d) or Wu.shape != (d_ff, d) or Wd.shape != (d, d_ff):
+            raise ValueError("expected Wgate, Wup [d_ff, d] and Wdown [d, d_ff]")
+        if d_ff % G != 0 or mask.shape != (T, d_ff // G):
+            raise ValueError("mask must be [T, d_ff // G] with G dividing d_ff")
+        dev = X.device
+        self.args = (X, Wg, Wu, Wd, mask)
+        self.T, self.d, self.d_ff, self.G = T, d, d_ff, G
+        self.dtype = _DTYPES[X.dtype]
+        self.flags = flags
+        self.Y = Y if Y is not None else torch.empty((T, d), dtype=X.dtype, device=dev)
+        self.H = H if H is not None else (torch.empty((T, d_ff), dtype=X.dtype, device=dev)
+                                          if return_h else None)
+        if self.H is not None:
+            _need_cuda("H", self.H)
+        nbytes = workspace_size(T, d, d_ff, G, X.dtype)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self.ws_bytes = workspace.numel() * workspace.element_size()
+
+    def _ffn_args(self):
+        X, Wg, Wu, Wd, mask = self.args
+        return (X.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), mask.data_ptr(), self.T,
+                self.d, self.d_ff, self.G, self.dtype, self.Y.data_ptr(),
+                None if self.H is None else self.H.data_ptr(), self.workspace.data_ptr(),
+                self.ws_bytes, self.flags, _stream_ptr(X.device))
+
+    def run(self):
+        _lib.check(_lib.load().wide_ffn_forward(*self._ffn_args()))
+        return self.Y
+
+    def stage(self, stage: int):
+        _lib.check(_lib.load().wide_ffn_stage(stage, *self._ffn_args()))
+
+
+def ffn_forward(X, Wg, Wu, Wd, mask, G: int, return_h: bool = False, flags: int = 0):
+    """Masked SwiGLU FFN -> Y (and H with exact zeros at masked channels if return_h)."""
+    call = FfnCall(X, Wg, Wu, Wd, mask, G, return_h=return_h, flags=flags)
+    Y = call.run()
+    return (Y, call.H) if return_h else Y
+
+
+def ffn_stage(stage: int, call: FfnCall) -> None:
+    call.stage(stage)

@@ -1,0 +1,84 @@
+// Internal declarations shared by the HIP translation units of libwide.so:
+// device helpers (bf16 rounding, silu, MFMA operand types, LDS swizzle) and
+// the host-side launchers that wide_api.cpp calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wide {
+
+// ---------------------------------------------------------------- device helpers
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> bfloat16 bits (quiet NaN kept a NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// silu(a) * b with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32).
+// For a -> -inf, exp2 overflows to +inf and the reciprocal gives 0, so the
+// result is a signed zero, never NaN.
+__device__ __forceinline__ float silu_mul(float a, float b) {
+  const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);
+  return a * __builtin_amdgcn_rcpf(1.0f + e) * b;
+}
+
+// Pack two floats into two bf16 in one 32-bit word (low = first).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// LDS tiles hold rows of 64 bf16 (128 bytes = 8 chunks of 16 bytes). Chunk c
+// of row r is stored at chunk position c ^ (r & 7): eight consecutive rows
+// reading the same logical chunk then hit eight different 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+}  // namespace wide
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; none allocates or synchronises.
+
+namespace wide {
+
+// Mask reorder (+ optional packed mask bits [ngroups, ceil(T/32)] uint32).
+hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t* perm,
+                          int32_t* counts, int32_t* padded, uint32_t* maskbits,
+                          hipStream_t stream);
+
+// bf16 prefill gate/up over the reordered tokens (tile = 256 tokens).
+hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                               const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
+                               int G, uint16_t* H, bool zero_inactive, hipStream_t stream);
+
+// bf16 prefill down projection (output-stationary, mask-bit predicated).
+hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
+                            int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
+
+// bf16 decode GEMVs (T <= 16).
+hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                      const uint8_t* mask, int T, int d, int d_ff, int G,
+                                      uint16_t* H, bool zero_inactive, hipStream_t stream);
+hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
+                                   int T, int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
+
+// fp32 prefill kernels (VALU, same structure as the bf16 ones).
+hipError_t launch_gate_up_f32(const float* X, const float* Wg, const float* Wu,
+                              const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
+                              int G, float* H, bool zero_inactive, hipStream_t stream);
+hipError_t launch_down_f32(const float* H, const float* Wd, const uint32_t* maskbits, int T, int d,
+                           int d_ff, int G, float* Y, hipStream_t stream);
+
+}  // namespace wide

@@ -1,0 +1,119 @@
+// Mask reorder: per-group stable partition of the tokens into an active
+// prefix and an inactive tail (ai.info summary, "How the speedups are
+// obtained"; WIDE paper Sec. 1, tile-aligned prefixes).
+//
+// One workgroup of 1024 threads (16 waves of 64) per group. Pass 1 counts the
+// active tokens of the column; pass 2 walks the column in chunks of 1024
+// tokens: a 64-bit wave ballot gives each lane its rank among the wave's
+// active lanes (mbcnt), an LDS scan over the 16 wave totals gives each wave
+// its base, and running totals carry the bases across chunks. Active tokens
+// go to perm[g][run_act + rank], inactive ones to perm[g][count + run_in +
+// rank']. The same ballots, written out as 32-bit words, are the packed mask
+// bits [ngroups, ceil(T/32)] that the down kernel predicates on.
+#include "common.h"
+
+namespace wide {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t ballot) {
+  // number of set bits of `ballot` in lanes below this one
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
+}
+
+__global__ __launch_bounds__(kThreads) void reorder_kernel(const uint8_t* __restrict__ mask, int T,
+                                                            int ng, int tile,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ padded,
+                                                            uint32_t* __restrict__ maskbits,
+                                                            int words) {
+  __shared__ int s_act[kWaves];
+  __shared__ int s_val[kWaves];
+  __shared__ int s_count;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // pass 1: popcount of the column
+  int local = 0;
+  for (int t = tid; t < T; t += kThreads) local += mask[(size_t)t * ng + g] != 0;
+  for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off, 64);
+  if (lane == 0) s_act[wave] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0;
+    for (int w = 0; w < kWaves; ++w) c += s_act[w];
+    s_count = c;
+  }
+  __syncthreads();
+  const int count = s_count;
+
+  // pass 2: place
+  int32_t* __restrict__ prow = perm + (size_t)g * T;
+  int run_act = 0, run_in = 0;
+  for (int t0 = 0; t0 < T; t0 += kThreads) {
+    const int t = t0 + tid;
+    const bool valid = t < T;
+    const bool act = valid && mask[(size_t)t * ng + g] != 0;
+    const uint64_t b_act = __ballot(act);
+    const uint64_t b_val = __ballot(valid);
+    __syncthreads();  // previous chunk's readers of s_act/s_val are done
+    if (lane == 0) {
+      s_act[wave] = __popcll(b_act);
+      s_val[wave] = __popcll(b_val);
+    }
+    __syncthreads();
+    int base_act = 0, base_val = 0, tot_act = 0, tot_val = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int a = s_act[w], v = s_val[w];
+      if (w < wave) {
+        base_act += a;
+        base_val += v;
+      }
+      tot_act += a;
+      tot_val += v;
+    }
+    if (valid) {
+      const int ra = (int)lane_rank(b_act);
+      const int rv = (int)lane_rank(b_val);  // == lane for valid lanes
+      if (act) {
+        prow[run_act + base_act + ra] = t;
+      } else {
+        const int base_in = base_val - base_act;
+        prow[count + run_in + base_in + (rv - ra)] = t;
+      }
+    }
+    if (maskbits != nullptr && lane < 2) {
+      const int tw = t0 + wave * 64;  // first token of this wave, a multiple of 64
+      const int word = tw / 32 + lane;
+      if (tw < T && word < words)
+        maskbits[(size_t)g * words + word] = (uint32_t)(b_act >> (32 * lane));
+    }
+    run_act += tot_act;
+    run_in += tot_val - tot_act;
+  }
+  if (tid == 0) {
+    counts[g] = count;
+    padded[g] = (int)(((long long)count + tile - 1) / tile) * tile;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t* perm,
+                          int32_t* counts, int32_t* padded, uint32_t* maskbits,
+                          hipStream_t stream) {
+  const int words = (T + 31) / 32;
+  hipLaunchKernelGGL(reorder_kernel, dim3(ng), dim3(kThreads), 0, stream, mask, T, ng, tile, perm,
+                     counts, padded, maskbits, words);
+  return hipGetLastError();
+}
+
+}  // namespace wide

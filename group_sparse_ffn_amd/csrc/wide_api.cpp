@@ -1,0 +1,280 @@
+// C ABI of libwide.so: argument validation, workspace layout, path dispatch
+// and kernel launches. Everything is enqueued on the caller's stream; no call
+// allocates, frees, synchronises or reads device memory on the host.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+#include "wide.h"
+
+#define WIDE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+wide_status_t fail(wide_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+wide_status_t ok() {
+  g_last_error.clear();
+  return WIDE_OK;
+}
+
+wide_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return WIDE_OK;
+  return fail(WIDE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t elt_size(wide_dtype_t dt) { return dt == WIDE_BF16 ? 2 : 4; }
+
+// Workspace layout (each region 256-byte aligned):
+//   perm     int32  [ngroups, T]
+//   counts   int32  [ngroups]
+//   padded   int32  [ngroups]
+//   maskbits uint32 [ngroups, ceil(T/32)]
+//   H        dtype  [T, d_ff]   (used when the caller passes no H_out)
+struct Layout {
+  size_t perm, counts, padded, maskbits, h, total;
+};
+
+Layout layout(int64_t T, int64_t d_ff, int64_t G, wide_dtype_t dt) {
+  const int64_t ng = d_ff / G;
+  const int64_t words = (T + 31) / 32;
+  Layout L{};
+  size_t off = 0;
+  L.perm = off;
+  off = round_up(off + (size_t)(ng * T) * 4, 256);
+  L.counts = off;
+  off = round_up(off + (size_t)ng * 4, 256);
+  L.padded = off;
+  off = round_up(off + (size_t)ng * 4, 256);
+  L.maskbits = off;
+  off = round_up(off + (size_t)(ng * words) * 4, 256);
+  L.h = off;
+  off = round_up(off + (size_t)(T * d_ff) * elt_size(dt), 256);
+  L.total = off;
+  return L;
+}
+
+int decode_max_t_value() {
+  static const int v = [] {
+    const char* s = std::getenv("WIDE_DECODE_MAX_T");
+    if (s == nullptr || *s == '\0') return (int)WIDE_DECODE_T_LIMIT;
+    char* end = nullptr;
+    long x = std::strtol(s, &end, 10);
+    if (end == s || x < 0) return (int)WIDE_DECODE_T_LIMIT;
+    return (int)(x > WIDE_DECODE_T_LIMIT ? WIDE_DECODE_T_LIMIT : x);
+  }();
+  return v;
+}
+
+struct Args {
+  const void* X;
+  const void* Wg;
+  const void* Wu;
+  const void* Wd;
+  const uint8_t* mask;
+  int32_t T, d, d_ff, G;
+  wide_dtype_t dt;
+  void* Y;
+  void* H_out;
+  void* ws;
+  size_t ws_bytes;
+  uint32_t flags;
+  hipStream_t stream;
+};
+
+// Host-side checks shared by wide_ffn_forward and wide_ffn_stage. Sets
+// *decode to the path the call takes.
+wide_status_t validate(const Args& a, bool* decode) {
+  if (!a.Wg || !a.Wu || !a.Wd) return fail(WIDE_ERR_NULL, "Wgate, Wup and Wdown must be non-NULL");
+  // X, mask and Y have T rows: with T == 0 they may be NULL (nothing is read or written).
+  if (a.T != 0 && (!a.X || !a.mask || !a.Y))
+    return fail(WIDE_ERR_NULL, "X, mask and Y must be non-NULL when T > 0");
+  if (a.dt != WIDE_F32 && a.dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)a.dt);
+  if (a.T < 0 || a.d <= 0 || a.d_ff <= 0 || a.G <= 0)
+    return fail(WIDE_ERR_SHAPE, "need T >= 0 and d, d_ff, G >= 1 (T=%d d=%d d_ff=%d G=%d)", a.T, a.d,
+                a.d_ff, a.G);
+  if (a.d_ff % a.G != 0) return fail(WIDE_ERR_SHAPE, "d_ff=%d is not a multiple of G=%d", a.d_ff, a.G);
+  if (a.d % 64 != 0 || a.d_ff % 64 != 0 || a.G % 16 != 0)
+    return fail(WIDE_ERR_UNSUPPORTED, "kernels need d %% 64 == 0, d_ff %% 64 == 0, G %% 16 == 0 (d=%d d_ff=%d G=%d)",
+                a.d, a.d_ff, a.G);
+  if (a.d_ff > 65536) return fail(WIDE_ERR_UNSUPPORTED, "kernels need d_ff <= 65536 (d_ff=%d)", a.d_ff);
+  if ((int64_t)a.T * a.d_ff > INT32_MAX || (int64_t)a.T * a.d > INT32_MAX ||
+      (int64_t)a.d * a.d_ff > INT32_MAX)
+    return fail(WIDE_ERR_UNSUPPORTED, "T*d_ff, T*d and d*d_ff must stay below 2^31");
+  if (!aligned16(a.X) || !aligned16(a.Wg) || !aligned16(a.Wu) || !aligned16(a.Wd) ||
+      !aligned16(a.Y) || (a.H_out && !aligned16(a.H_out)))
+    return fail(WIDE_ERR_ALIGN, "X, W*, Y and H_out must be 16-byte aligned");
+  if ((a.flags & WIDE_FLAG_FORCE_PREFILL) && (a.flags & WIDE_FLAG_FORCE_DECODE))
+    return fail(WIDE_ERR_SHAPE, "FORCE_PREFILL and FORCE_DECODE are exclusive");
+  if (a.flags & ~(WIDE_FLAG_FORCE_PREFILL | WIDE_FLAG_FORCE_DECODE))
+    return fail(WIDE_ERR_SHAPE, "unknown flag bits 0x%x", a.flags);
+  bool dec = a.dt == WIDE_BF16 && a.T <= decode_max_t_value();
+  if (a.flags & WIDE_FLAG_FORCE_PREFILL) dec = false;
+  if (a.flags & WIDE_FLAG_FORCE_DECODE) {
+    if (a.dt != WIDE_BF16 || a.T > WIDE_DECODE_T_LIMIT)
+      return fail(WIDE_ERR_UNSUPPORTED, "the decode path needs bf16 and T <= %d", WIDE_DECODE_T_LIMIT);
+    dec = true;
+  }
+  const Layout L = layout(a.T, a.d_ff, a.G, a.dt);
+  if (!a.ws) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if ((reinterpret_cast<uintptr_t>(a.ws) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (a.ws_bytes < L.total)
+    return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", a.ws_bytes, L.total);
+  *decode = dec;
+  return WIDE_OK;
+}
+
+wide_status_t run_stage(wide_stage_t stage, const Args& a) {
+  const Layout L = layout(a.T, a.d_ff, a.G, a.dt);
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
+  uint32_t* maskbits = reinterpret_cast<uint32_t*>(ws + L.maskbits);
+  void* H = a.H_out ? a.H_out : static_cast<void*>(ws + L.h);
+  const bool zero_h = a.H_out != nullptr;
+  const int ng = a.d_ff / a.G;
+  hipError_t e = hipSuccess;
+  switch (stage) {
+    case WIDE_STAGE_REORDER:
+      e = wide::launch_reorder(a.mask, a.T, ng, WIDE_TOKEN_TILE, perm, counts, padded, maskbits,
+                               a.stream);
+      return hip_status(e, "mask reorder launch");
+    case WIDE_STAGE_GATE_UP:
+      if (a.dt == WIDE_BF16)
+        e = wide::launch_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
+                                      (const uint16_t*)a.Wu, perm, counts, a.T, a.d, a.d_ff, a.G,
+                                      (uint16_t*)H, zero_h, a.stream);
+      else
+        e = wide::launch_gate_up_f32((const float*)a.X, (const float*)a.Wg, (const float*)a.Wu,
+                                     perm, counts, a.T, a.d, a.d_ff, a.G, (float*)H, zero_h,
+                                     a.stream);
+      return hip_status(e, "gate/up launch");
+    case WIDE_STAGE_DOWN:
+      if (a.dt == WIDE_BF16)
+        e = wide::launch_down_bf16((const uint16_t*)H, (const uint16_t*)a.Wd, maskbits, a.T, a.d,
+                                   a.d_ff, a.G, (uint16_t*)a.Y, a.stream);
+      else
+        e = wide::launch_down_f32((const float*)H, (const float*)a.Wd, maskbits, a.T, a.d, a.d_ff,
+                                  a.G, (float*)a.Y, a.stream);
+      return hip_status(e, "down launch");
+    case WIDE_STAGE_DECODE_GATE_UP:
+      e = wide::launch_decode_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
+                                           (const uint16_t*)a.Wu, a.mask, a.T, a.d, a.d_ff, a.G,
+                                           (uint16_t*)H, zero_h, a.stream);
+      return hip_status(e, "decode gate/up launch");
+    case WIDE_STAGE_DECODE_DOWN:
+      e = wide::launch_decode_down_bf16((const uint16_t*)H, (const uint16_t*)a.Wd, a.mask, a.T, a.d,
+                                        a.d_ff, a.G, (uint16_t*)a.Y, a.stream);
+      return hip_status(e, "decode down launch");
+  }
+  return fail(WIDE_ERR_SHAPE, "unknown stage %d", (int)stage);
+}
+
+}  // namespace
+
+WIDE_API wide_status_t wide_reorder_masks(const uint8_t* mask, int32_t T, int32_t ngroups,
+                                          int32_t tile, int32_t* perm, int32_t* counts,
+                                          int32_t* padded, void* stream) {
+  if (!counts || !padded) return fail(WIDE_ERR_NULL, "counts and padded must be non-NULL");
+  if (T != 0 && (!mask || !perm))
+    return fail(WIDE_ERR_NULL, "mask and perm must be non-NULL when T > 0");
+  if (T < 0 || ngroups < 1 || tile < 1)
+    return fail(WIDE_ERR_SHAPE, "need T >= 0, ngroups >= 1, tile >= 1 (T=%d ngroups=%d tile=%d)", T,
+                ngroups, tile);
+  if ((int64_t)T * ngroups > INT32_MAX)
+    return fail(WIDE_ERR_SHAPE, "T*ngroups must stay below 2^31");
+  const hipError_t e = wide::launch_reorder(mask, T, ngroups, tile, perm, counts, padded, nullptr,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "mask reorder launch");
+  return ok();
+}
+
+WIDE_API size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G,
+                                        wide_dtype_t dtype) {
+  if (T < 0 || d <= 0 || d_ff <= 0 || G <= 0 || d_ff % G != 0) return 0;
+  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return 0;
+  return layout(T, d_ff, G, dtype).total;
+}
+
+WIDE_API wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup,
+                                        const void* Wdown, const uint8_t* mask, int32_t T,
+                                        int32_t d, int32_t d_ff, int32_t G, wide_dtype_t dtype,
+                                        void* Y, void* H_out, void* workspace,
+                                        size_t workspace_bytes, uint32_t flags, void* stream) {
+  const Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, dtype, Y, H_out, workspace,
+               workspace_bytes, flags, static_cast<hipStream_t>(stream)};
+  bool dec = false;
+  wide_status_t st = validate(a, &dec);
+  if (st != WIDE_OK) return st;
+  if (T == 0) return ok();
+  const wide_stage_t prefill[] = {WIDE_STAGE_REORDER, WIDE_STAGE_GATE_UP, WIDE_STAGE_DOWN};
+  const wide_stage_t decode[] = {WIDE_STAGE_DECODE_GATE_UP, WIDE_STAGE_DECODE_DOWN};
+  const wide_stage_t* stages = dec ? decode : prefill;
+  const int n = dec ? 2 : 3;
+  for (int i = 0; i < n; ++i) {
+    st = run_stage(stages[i], a);
+    if (st != WIDE_OK) return st;
+  }
+  return ok();
+}
+
+WIDE_API wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const void* Wgate,
+                                      const void* Wup, const void* Wdown, const uint8_t* mask,
+                                      int32_t T, int32_t d, int32_t d_ff, int32_t G,
+                                      wide_dtype_t dtype, void* Y, void* H_out, void* workspace,
+                                      size_t workspace_bytes, uint32_t flags, void* stream) {
+  const Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, dtype, Y, H_out, workspace,
+               workspace_bytes, flags, static_cast<hipStream_t>(stream)};
+  bool dec = false;
+  wide_status_t st = validate(a, &dec);
+  if (st != WIDE_OK) return st;
+  const bool is_dec_stage = stage == WIDE_STAGE_DECODE_GATE_UP || stage == WIDE_STAGE_DECODE_DOWN;
+  if (stage < WIDE_STAGE_REORDER || stage > WIDE_STAGE_DECODE_DOWN)
+    return fail(WIDE_ERR_SHAPE, "unknown stage %d", (int)stage);
+  if (is_dec_stage != dec)
+    return fail(WIDE_ERR_UNSUPPORTED, "stage %d is not on the %s path these arguments take",
+                (int)stage, dec ? "decode" : "prefill");
+  if (T == 0) return ok();
+  st = run_stage(stage, a);
+  if (st != WIDE_OK) return st;
+  return ok();
+}
+
+WIDE_API const char* wide_status_string(wide_status_t s) {
+  switch (s) {
+    case WIDE_OK: return "ok";
+    case WIDE_ERR_NULL: return "null pointer argument";
+    case WIDE_ERR_SHAPE: return "invalid size or argument";
+    case WIDE_ERR_DTYPE: return "unknown dtype";
+    case WIDE_ERR_ALIGN: return "misaligned pointer";
+    case WIDE_ERR_WORKSPACE: return "workspace missing or too small";
+    case WIDE_ERR_UNSUPPORTED: return "unsupported by these kernels";
+    case WIDE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+WIDE_API const char* wide_last_error(void) { return g_last_error.c_str(); }
+
+WIDE_API int32_t wide_decode_max_t(void) { return decode_max_t_value(); }

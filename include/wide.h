@@ -1,0 +1,179 @@
+/*
+ * wide.h - C ABI of libwide.so, a group-sparse (token-wise dynamic-width)
+ * SwiGLU FFN for AMD Instinct MI355X (gfx950).
+ *
+ * The method: WIDE ("Boosting Adaptive LLM Inference via Token-level Dynamic
+ * Width Pruning"). The FFN intermediate dimension d_ff is cut into contiguous
+ * groups of G channels and every token keeps or skips each group; one mask
+ * matrix covers the whole FFN layer (ai.info summary, "Methodology in Plain
+ * English"; WIDE paper, Sec. 3.1 "Preliminaries"). Skipped groups are turned
+ * into skipped work in the gate/up projection (N axis, App. B
+ * "Implementation of GEMM-MN") and in the down projection (K axis, App. B
+ * "Implementation of GEMM-K").
+ *
+ * Computed definition, for token t, channel c in group g = c / G:
+ *   H[t,c] = silu(X[t,:] . Wgate[c,:]) * (X[t,:] . Wup[c,:])  if mask[t,g] != 0
+ *   H[t,c] = 0                                                otherwise
+ *   Y[t,n] = sum_c Wdown[n,c] * H[t,c]            silu(a) = a / (1 + exp(-a))
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers (hipMalloc'd or equivalent),
+ *     row-major and contiguous, 16-byte aligned. The caller owns every
+ *     buffer; the library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the null stream). All work is
+ *     enqueued on it and the call returns before the work completes. No
+ *     call reads device memory on the host or decides anything from mask
+ *     contents on the host, so every call can be captured in a hipGraph.
+ *   - Arguments are validated on the host before anything is enqueued. A
+ *     failed check returns a status code and enqueues nothing; the message is
+ *     kept per host thread and returned by wide_last_error(). A failed launch
+ *     returns WIDE_ERR_HIP. No C++ exception crosses the ABI.
+ *   - Masks are uint8 [T, ngroups], nonzero = the token executes the group.
+ *     (The pages' router emits class 0 = execute; whoever builds the mask
+ *     inverts that.)
+ */
+#ifndef WIDE_H
+#define WIDE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WIDE_OK = 0,
+  WIDE_ERR_NULL = 1,        /* a required pointer is NULL */
+  WIDE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  WIDE_ERR_DTYPE = 3,       /* unknown dtype */
+  WIDE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  WIDE_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than wide_ffn_workspace_size() */
+  WIDE_ERR_UNSUPPORTED = 6, /* valid for the definition but not for these kernels */
+  WIDE_ERR_HIP = 7          /* a HIP launch failed (detail in wide_last_error()) */
+} wide_status_t;
+
+typedef enum {
+  WIDE_F32 = 0,  /* X, W*, H and Y are float32; fp32 arithmetic throughout */
+  WIDE_BF16 = 1  /* X, W*, H and Y are bfloat16; fp32 accumulation, H and Y rounded once (RNE) */
+} wide_dtype_t;
+
+/* Token tile of the gate/up kernel: the tile that wide_ffn_forward's reorder
+ * aligns the per-group counts to. */
+#define WIDE_TOKEN_TILE 256
+
+/* Largest token count the bf16 decode kernels take in one pass. */
+#define WIDE_DECODE_T_LIMIT 16
+
+/* Flags for wide_ffn_forward / wide_ffn_stage. */
+#define WIDE_FLAG_FORCE_PREFILL 0x1u /* never take the decode path */
+#define WIDE_FLAG_FORCE_DECODE 0x2u  /* take the decode path (needs bf16 and T <= 16) */
+
+/*
+ * wide_reorder_masks - per-group stable partition of the mask columns.
+ *
+ * For every group g the tokens are reordered so that the active ones form a
+ * contiguous prefix (ai.info summary, "How the speedups are obtained": sorting
+ * each routing column gives a contiguous active prefix with at most one
+ * boundary tile per group; WIDE paper Sec. 1, "tile-aligned prefixes").
+ * The order is stable: perm[g, 0:counts[g]] lists the active tokens in
+ * ascending order, perm[g, counts[g]:T] the inactive ones in ascending order.
+ *
+ *   mask    [T, ngroups] uint8, device, read only.
+ *   perm    [ngroups, T] int32, device, written (a permutation of 0..T-1 per row).
+ *   counts  [ngroups] int32, device, written: active tokens per group.
+ *   padded  [ngroups] int32, device, written: ceil(counts[g] / tile) * tile
+ *           (0 when counts[g] == 0; may exceed T, so consumers bound rows by counts).
+ *   T >= 0, ngroups >= 1, tile >= 1. T == 0 enqueues only the counts/padded
+ *   writes, and mask and perm may then be NULL.
+ * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_HIP.
+ */
+wide_status_t wide_reorder_masks(const uint8_t* mask, int32_t T, int32_t ngroups, int32_t tile,
+                                 int32_t* perm, int32_t* counts, int32_t* padded, void* stream);
+
+/*
+ * wide_ffn_workspace_size - bytes of device workspace wide_ffn_forward needs.
+ * Holds the per-group permutations, counts, packed mask bits and, when the
+ * caller passes no H_out, the intermediate H. Returns 0 for invalid sizes.
+ */
+size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G, wide_dtype_t dtype);
+
+/*
+ * wide_ffn_forward - the masked SwiGLU FFN defined at the top of this file.
+ *
+ *   X      [T, d]      device, dtype, read only.
+ *   Wgate  [d_ff, d]   device, dtype, read only ([out, in], as nn.Linear).
+ *   Wup    [d_ff, d]   device, dtype, read only.
+ *   Wdown  [d, d_ff]   device, dtype, read only.
+ *   mask   [T, d_ff/G] device, uint8, read only.
+ *   Y      [T, d]      device, dtype, written. Rows of tokens with no active
+ *                      group are exactly +0.0.
+ *   H_out  [T, d_ff]   device, dtype, optional (NULL = keep H in the workspace).
+ *                      When given, it receives H with exact +0.0 at every
+ *                      masked channel.
+ *   workspace          device, >= wide_ffn_workspace_size(...) bytes, 256-byte
+ *                      aligned; contents on entry are ignored.
+ *   flags              WIDE_FLAG_* (0 = choose the path from T).
+ *
+ * Prefill path (T > wide_decode_max_t(), or WIDE_FLAG_FORCE_PREFILL): mask
+ * reorder, then the gate/up kernel over each group's active prefix (tiles past
+ * the prefix exit, rows past it are not loaded, fragments past it are not
+ * multiplied; SiLU(gate)*up fused in the epilogue and scattered to H), then the
+ * down kernel, which owns each [token tile x output tile] of Y, accumulates
+ * over the groups in registers, skips every K-block whose groups are inactive
+ * for the whole token tile and loads H only for active (token, group) pairs.
+ * Decode path (bf16, T <= wide_decode_max_t()): no reorder (WIDE paper App. B:
+ * the T_q = 1 case checks routing directly); a gate/up GEMV and a down GEMV
+ * that stream only the weight rows/segments of groups active for some token.
+ *
+ * Sizes: T >= 0 (T == 0 enqueues nothing; X, mask and Y may then be NULL);
+ * d, d_ff, G >= 1 with d_ff % G == 0. The kernels also need
+ * d % 64 == 0, d_ff % 64 == 0 and G % 16 == 0 (else WIDE_ERR_UNSUPPORTED);
+ * T, d, d_ff, G and T*d_ff must fit in int32 arithmetic per kernel index.
+ * bf16 results differ from exact arithmetic by fp32 accumulation and the two
+ * roundings; the reduction order is fixed, so a call is deterministic.
+ * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_DTYPE, WIDE_ERR_ALIGN,
+ * WIDE_ERR_WORKSPACE, WIDE_ERR_UNSUPPORTED, WIDE_ERR_HIP.
+ */
+wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup, const void* Wdown,
+                               const uint8_t* mask, int32_t T, int32_t d, int32_t d_ff, int32_t G,
+                               wide_dtype_t dtype, void* Y, void* H_out, void* workspace,
+                               size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* Stages of wide_ffn_forward, for callers that time or interleave them. */
+typedef enum {
+  WIDE_STAGE_REORDER = 0,   /* prefill: mask reorder into the workspace */
+  WIDE_STAGE_GATE_UP = 1,   /* prefill: gate/up kernel -> H */
+  WIDE_STAGE_DOWN = 2,      /* prefill: down kernel -> Y */
+  WIDE_STAGE_DECODE_GATE_UP = 3, /* decode: gate/up GEMV -> H */
+  WIDE_STAGE_DECODE_DOWN = 4     /* decode: down GEMV -> Y */
+} wide_stage_t;
+
+/*
+ * wide_ffn_stage - enqueue one stage of wide_ffn_forward with the same
+ * arguments. Running the prefill stages 0,1,2 (or the decode stages 3,4) in
+ * order on one stream with one workspace is exactly wide_ffn_forward on that
+ * path; the path must be the one wide_ffn_forward would take for these
+ * arguments and flags (else WIDE_ERR_UNSUPPORTED). A stage reads what the
+ * previous stages left in the workspace (and in H_out when given).
+ */
+wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const void* Wgate, const void* Wup,
+                             const void* Wdown, const uint8_t* mask, int32_t T, int32_t d,
+                             int32_t d_ff, int32_t G, wide_dtype_t dtype, void* Y, void* H_out,
+                             void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* Static text for a status code. */
+const char* wide_status_string(wide_status_t status);
+
+/* Detail of the last failure on the calling host thread ("" if none). */
+const char* wide_last_error(void);
+
+/* Largest T that takes the decode path (WIDE_DECODE_T_LIMIT unless the
+ * environment variable WIDE_DECODE_MAX_T, read once, sets 0..16). */
+int32_t wide_decode_max_t(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WIDE_H */

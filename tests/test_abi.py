@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports exactly what
+include/wide.h declares, and rejects bad arguments on the host before any
+HIP call (so these calls are safe without a device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from group_sparse_ffn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wide.h")
+FAKE = 1 << 20  # a 256-byte aligned non-NULL address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return set(re.findall(r"\b(wide_[a-z_]+)\s*\(", src))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from group_sparse_ffn_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    declared = declared_functions()
+    assert declared == set(_lib.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert declared <= exported
+    assert {s for s in exported if s.startswith("wide_")} == declared
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def ffn_call(lib, **kw):
+    a = dict(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, mask=FAKE, T=64, d=256, d_ff=1024, G=64,
+             dtype=_lib.WIDE_BF16, Y=FAKE, H=None, ws=FAKE, ws_bytes=1 << 40, flags=0, stream=None)
+    a.update(kw)
+    return lib.wide_ffn_forward(a["X"], a["Wg"], a["Wu"], a["Wd"], a["mask"], a["T"], a["d"],
+                                a["d_ff"], a["G"], a["dtype"], a["Y"], a["H"], a["ws"],
+                                a["ws_bytes"], a["flags"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _lib.WIDE_ERR_NULL),
+    (dict(Wd=None, T=0), _lib.WIDE_ERR_NULL),
+    (dict(mask=None), _lib.WIDE_ERR_NULL),
+    (dict(Y=None), _lib.WIDE_ERR_NULL),
+    (dict(dtype=7), _lib.WIDE_ERR_DTYPE),
+    (dict(T=-1), _lib.WIDE_ERR_SHAPE),
+    (dict(d=0), _lib.WIDE_ERR_SHAPE),
+    (dict(G=0), _lib.WIDE_ERR_SHAPE),
+    (dict(d_ff=1000, G=64), _lib.WIDE_ERR_SHAPE),
+    (dict(d=96), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(d_ff=1040, G=40), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(d_ff=1024, G=8), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(d_ff=131072, G=128), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, d_ff=4096, G=128), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(X=FAKE + 8), _lib.WIDE_ERR_ALIGN),
+    (dict(H=FAKE + 4), _lib.WIDE_ERR_ALIGN),
+    (dict(ws=FAKE + 16), _lib.WIDE_ERR_ALIGN),
+    (dict(ws=None), _lib.WIDE_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), _lib.WIDE_ERR_WORKSPACE),
+    (dict(flags=3), _lib.WIDE_ERR_SHAPE),
+    (dict(flags=8), _lib.WIDE_ERR_SHAPE),
+    (dict(flags=_lib.WIDE_FLAG_FORCE_DECODE, T=17), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(flags=_lib.WIDE_FLAG_FORCE_DECODE, dtype=_lib.WIDE_F32, T=4), _lib.WIDE_ERR_UNSUPPORTED),
+])
+def test_forward_validation(lib, kw, status):
+    assert ffn_call(lib, **kw) == status
+    assert lib.wide_last_error().decode() != ""
+    assert lib.wide_status_string(status).decode() not in ("", "unknown status")
+
+
+def test_forward_t0_is_a_no_op(lib):
+    # valid arguments with T == 0 enqueue nothing and succeed
+    assert ffn_call(lib, T=0) == _lib.WIDE_OK
+    assert ffn_call(lib, T=0, X=None, mask=None, Y=None) == _lib.WIDE_OK
+    assert lib.wide_last_error().decode() == ""
+
+
+def test_stage_rejects_the_other_path(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 1024, 64, _lib.WIDE_BF16, FAKE, None, FAKE,
+            1 << 40, 0, None]
+    # T = 64 > decode limit -> prefill; a decode stage must be refused
+    assert lib.wide_ffn_stage(_lib.WIDE_STAGE_DECODE_DOWN, *args) == _lib.WIDE_ERR_UNSUPPORTED
+    args[5] = 4  # T = 4 -> decode; a prefill stage must be refused
+    assert lib.wide_ffn_stage(_lib.WIDE_STAGE_GATE_UP, *args) == _lib.WIDE_ERR_UNSUPPORTED
+    assert lib.wide_ffn_stage(9, *args) == _lib.WIDE_ERR_SHAPE
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 8, 2, 4, FAKE, FAKE, FAKE, None), _lib.WIDE_ERR_NULL),
+    ((FAKE, 0, 2, 4, FAKE, None, FAKE, None), _lib.WIDE_ERR_NULL),
+    ((FAKE, 8, 2, 4, None, FAKE, FAKE, None), _lib.WIDE_ERR_NULL),
+    ((FAKE, -1, 2, 4, FAKE, FAKE, FAKE, None), _lib.WIDE_ERR_SHAPE),
+    ((FAKE, 8, 0, 4, FAKE, FAKE, FAKE, None), _lib.WIDE_ERR_SHAPE),
+    ((FAKE, 8, 2, 0, FAKE, FAKE, FAKE, None), _lib.WIDE_ERR_SHAPE),
+    ((FAKE, 1 << 30, 8, 4, FAKE, FAKE, FAKE, None), _lib.WIDE_ERR_SHAPE),
+])
+def test_reorder_validation(lib, args, status):
+    assert lib.wide_reorder_masks(*args) == status
+
+
+def test_workspace_size(lib):
+    ws = lib.wide_ffn_workspace_size(16384, 4096, 14336, 128, _lib.WIDE_BF16)
+    ng, T = 112, 16384
+    need = ng * T * 4 + 2 * ng * 4 + ng * (T // 32) * 4 + T * 14336 * 2
+    assert need <= ws <= need + 5 * 256
+    assert lib.wide_ffn_workspace_size(16, 4096, 14336, 100, _lib.WIDE_BF16) == 0
+    assert lib.wide_ffn_workspace_size(16, 4096, 14336, 128, 5) == 0
+
+
+def test_decode_threshold_default(lib):
+    assert 0 <= lib.wide_decode_max_t() <= _lib.WIDE_DECODE_T_LIMIT
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.load()

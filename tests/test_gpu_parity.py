@@ -1,0 +1,282 @@
+"""HIP path vs the fp64 oracle on the GPU (run with -m gpu on an MI355X).
+
+Bars (written here, applied element by element):
+  * mask reorder: permutations, counts and padded counts bit-exact;
+  * H: exact zeros at every masked channel;
+  * Y: max|err| / max|ref| <= 2e-2 for bf16 inputs (fp32 accumulation),
+       <= 1e-5 for fp32 inputs;
+  * tokens with no active group, and the all-zero mask: Y exactly +0.0.
+Small cases compare every output; the full-size workloads compare a seeded
+sample of tokens (first, last, boundary-tile tokens and random ones) and check
+the exact-zero and determinism properties on every output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import group_sparse_ffn_amd as wide
+from group_sparse_ffn_amd import datagen as dg
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    # Name the case on the real stderr before any GPU work, so a run that dies
+    # still says which case it was in.
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+def to_dev(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def rel_err(y, ref):
+    y = y.detach().float().cpu().numpy().astype(np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(y - ref)) / (den if den > 0 else 1.0))
+
+
+def run_ffn(inp, G, **kw):
+    d = to_dev(inp)
+    Y, H = wide.ffn_forward(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], G, return_h=True, **kw)
+    torch.cuda.synchronize()
+    return Y, H
+
+
+def check_h_zeros(H, mask, G):
+    m = mask.to(DEV).bool().repeat_interleave(G, dim=1)
+    masked = H[~m]
+    assert masked.numel() == 0 or bool((masked == 0).all()), "nonzero H at a masked channel"
+
+
+# ----------------------------------------------------------------------------- reorder
+
+@pytest.mark.parametrize("T,ng,tile,kind", [
+    (64, 16, 256, "bernoulli"), (1, 3, 256, "bernoulli"), (1000, 37, 256, "bernoulli"),
+    (1025, 5, 7, "bernoulli"), (4096, 136, 256, "zipf"), (16384, 112, 256, "topk"),
+    (300, 8, 1, "ones"), (300, 8, 64, "zeros"), (0, 4, 256, "zeros"),
+])
+def test_reorder_bit_exact(T, ng, tile, kind):
+    if kind == "bernoulli":
+        m = dg.mask_bernoulli(T, ng, 0.4, seed=T + ng)
+    elif kind == "topk":
+        m = dg.mask_topk(T, ng, ng // 2, seed=2004)
+    elif kind == "zipf":
+        m = dg.mask_zipf(T, ng, 0.5, seed=5004)
+    elif kind == "ones":
+        m = np.ones((T, ng), np.uint8)
+    else:
+        m = np.zeros((T, ng), np.uint8)
+    perm, counts, padded = wide.reorder_masks(torch.from_numpy(m).to(DEV), tile)
+    rp, rc, rpad = oracle.reorder(m, tile)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(padded.cpu().numpy(), rpad)
+
+
+def test_reorder_nonzero_bytes_count_as_active():
+    m = dg.mask_bernoulli(500, 6, 0.5, seed=1) * np.uint8(200)
+    perm, counts, _ = wide.reorder_masks(torch.from_numpy(m).to(DEV), 256)
+    rp, rc, _ = oracle.reorder(m, 256)
+    assert np.array_equal(perm.cpu().numpy(), rp) and np.array_equal(counts.cpu().numpy(), rc)
+
+
+# ----------------------------------------------------------------------------- small FFN, every output
+
+SMALL = [
+    # (T, d, d_ff, G, dtype, density, flags)
+    (64, 256, 1024, 64, "f32", 0.5, 0),      # the tiny SwiGLU workload's shape
+    (700, 512, 2048, 128, "bf16", 0.5, 0),    # 3 token tiles (ragged), 2 output tiles
+    (700, 320, 1024, 64, "bf16", 0.3, 0),     # partial output tile (d % 256 != 0)
+    (513, 256, 1024, 32, "bf16", 0.7, 0),
+    (300, 192, 512, 16, "bf16", 0.5, 0),      # G = 16: several groups per K-block
+    (257, 128, 512, 256, "bf16", 0.5, 0),     # G = 256: two channel tiles per group
+    (40, 64, 128, 64, "bf16", 0.5, 0),        # minimal d
+    (1, 256, 1024, 128, "bf16", 0.5, wide.WIDE_FLAG_FORCE_PREFILL),
+    (16, 512, 1024, 128, "bf16", 0.5, wide.WIDE_FLAG_FORCE_PREFILL),
+    (200, 256, 512, 64, "f32", 0.6, 0),
+    (5, 128, 256, 16, "f32", 0.5, 0),
+]
+
+
+@pytest.mark.parametrize("T,d,d_ff,G,dtype,density,flags", SMALL)
+def test_ffn_small_all_outputs(T, d, d_ff, G, dtype, density, flags):
+    inp = dg.random_small(7 * T + G, T, d, d_ff, G, dtype, density, wscale=0.05)
+    Y, H = run_ffn(inp, G, flags=flags)
+    Href, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    assert rel_err(Y, Yref) <= TOL[dtype]
+    check_h_zeros(H, inp["mask"], G)
+    # H itself is also within the tolerance of the oracle's H
+    assert rel_err(H, Href) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("T,G", [(1, 128), (3, 128), (16, 128), (5, 16), (16, 32)])
+def test_decode_path_vs_oracle(T, G):
+    d, d_ff = 512, 2048
+    assert T <= wide.decode_max_t() or T <= wide.WIDE_DECODE_T_LIMIT
+    inp = dg.random_small(100 + T, T, d, d_ff, G, "bf16", 0.5, wscale=0.05)
+    Y, H = run_ffn(inp, G, flags=wide.WIDE_FLAG_FORCE_DECODE)
+    _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    assert rel_err(Y, Yref) <= TOL["bf16"]
+    check_h_zeros(H, inp["mask"], G)
+
+
+def test_decode_equals_prefill_within_tolerance_t16():
+    T, d, d_ff, G = 16, 1024, 2048, 128
+    inp = dg.random_small(77, T, d, d_ff, G, "bf16", 0.5, wscale=0.05)
+    Yd, _ = run_ffn(inp, G, flags=wide.WIDE_FLAG_FORCE_DECODE)
+    Yp, _ = run_ffn(inp, G, flags=wide.WIDE_FLAG_FORCE_PREFILL)
+    ref = Yp.float().cpu().numpy().astype(np.float64)
+    assert rel_err(Yd, ref) <= TOL["bf16"]
+
+
+def test_edge_masks_small():
+    T, d, d_ff, G = 300, 256, 1024, 64
+    inp = dg.random_small(5, T, d, d_ff, G, "bf16", 0.5, wscale=0.05)
+    ng = d_ff // G
+    m = inp["mask"].clone()
+    m[7, :] = 0                    # a token with no active group
+    m[:, 3] = 0                    # a group no token executes
+    m[:, 5] = 0
+    m[123, 5] = 1                  # a group exactly one token executes
+    inp["mask"] = m
+    for flags in (0, wide.WIDE_FLAG_FORCE_PREFILL):
+        Y, H = run_ffn(inp, G, flags=flags)
+        _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], m, G)
+        assert rel_err(Y, Yref) <= TOL["bf16"]
+        assert bool((Y[7] == 0).all()) and not bool(torch.signbit(Y[7].float()).any())
+        check_h_zeros(H, m, G)
+    # all-zero mask: Y and H exactly zero; all-ones: dense
+    inp["mask"] = torch.zeros((T, ng), dtype=torch.uint8)
+    Y, H = run_ffn(inp, G)
+    assert bool((Y == 0).all()) and bool((H == 0).all())
+    inp["mask"] = torch.ones((T, ng), dtype=torch.uint8)
+    Y, _ = run_ffn(inp, G)
+    _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    assert rel_err(Y, Yref) <= TOL["bf16"]
+
+
+def test_t0_is_a_no_op():
+    inp = dg.random_small(3, 0, 256, 512, 64, "bf16", 0.5)
+    d = to_dev(inp)
+    Y = wide.ffn_forward(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], 64)
+    assert Y.shape == (0, 256)
+
+
+def test_stages_equal_forward_and_are_deterministic():
+    T, d, d_ff, G = 600, 512, 1024, 128
+    inp = to_dev(dg.random_small(9, T, d, d_ff, G, "bf16", 0.5, wscale=0.05))
+    call = wide.FfnCall(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    Y1 = call.run().clone()
+    Y2 = call.run().clone()
+    call.Y.zero_()
+    for s in (wide.WIDE_STAGE_REORDER, wide.WIDE_STAGE_GATE_UP, wide.WIDE_STAGE_DOWN):
+        call.stage(s)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2), "two identical calls differ"
+    assert torch.equal(Y1, call.Y), "stages differ from forward"
+
+
+def test_hip_graph_replay_matches_eager():
+    T, d, d_ff, G = 512, 512, 1024, 64
+    inp = to_dev(dg.random_small(13, T, d, d_ff, G, "bf16", 0.5, wscale=0.05))
+    call = wide.FfnCall(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    eager = call.run().clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call.run()
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        call.Y.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.Y, eager), f"replay {i} differs from eager"
+    # the mask is read on the device at replay time: a new mask changes the result
+    inp["mask"].copy_(torch.zeros_like(inp["mask"]))
+    g.replay()
+    torch.cuda.synchronize()
+    assert bool((call.Y == 0).all())
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def sample_rows(T, counts_tile_boundaries, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1, T // 2}
+    rows.update(int(r) for r in counts_tile_boundaries)
+    rows.update(int(r) for r in rng.choice(T, size=min(n_random, T), replace=False))
+    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+def full_size_check(w, n_random, mask_kind=None):
+    inp = dg.make_inputs(w, mask_kind=mask_kind)
+    m = inp["mask"].numpy()
+    d = to_dev(inp)
+    call = wide.FfnCall(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], w.G, return_h=True)
+    Y = call.run()
+    torch.cuda.synchronize()
+    # tokens at the boundary tile of a few groups (last active token of the prefix)
+    perm, counts, _ = oracle.reorder(m, wide.WIDE_TOKEN_TILE)
+    bnd = [perm[g, c - 1] for g, c in enumerate(counts[:8]) if c > 0]
+    rows = sample_rows(w.T, bnd, n_random, seed=w.seed)
+    Hs, Ys = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], m, w.G, rows=rows)
+    err = rel_err(Y[torch.from_numpy(rows).to(DEV)], Ys)
+    assert err <= TOL[w.dtype], f"{w.name}: rel err {err}"
+    check_h_zeros(call.H, inp["mask"], w.G)
+    Y2 = call.run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2), "not deterministic at full size"
+    return Y
+
+
+def test_llama8b_prefill_full_size_sampled():
+    full_size_check(dg.LLAMA8B_PREFILL, n_random=48)
+
+
+@pytest.mark.parametrize("w", [dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16], ids=lambda w: w.name)
+def test_llama8b_decode_full_size(w):
+    full_size_check(w, n_random=16)
+
+
+def test_qwen14b_skewed_full_size_sampled():
+    full_size_check(dg.QWEN14B_SKEW, n_random=24)
+
+
+def test_qwen14b_all_zero_and_all_ones():
+    w = dg.QWEN14B_SKEW
+    Y = full_size_check(w, n_random=4, mask_kind="ones")
+    # all-ones equals the dense FFN: also compare with torch's dense GEMMs (fp32 on the GPU)
+    inp = dg.make_inputs(w, mask_kind="ones")
+    X = inp["X"].to(DEV).float()
+    rows = torch.arange(0, w.T, 97, device=DEV)
+    a = X[rows] @ inp["Wg"].to(DEV).float().t()
+    b = X[rows] @ inp["Wu"].to(DEV).float().t()
+    ref = ((a * torch.sigmoid(a)) * b) @ inp["Wd"].to(DEV).float().t()
+    err = (Y[rows].float() - ref).abs().max() / ref.abs().max()
+    assert float(err) <= TOL["bf16"]
+    inp = dg.make_inputs(w, mask_kind="zeros")
+    d = to_dev(inp)
+    Yz, Hz = wide.ffn_forward(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], w.G, return_h=True)
+    torch.cuda.synchronize()
+    assert bool((Yz == 0).all()) and bool((Hz == 0).all())
+
+
+@pytest.mark.parametrize("cell_G,T", [(16, 2048), (512, 2048), (128, 8192), (64, 1)])
+def test_llama3b_sweep_cells_sampled(cell_G, T):
+    cells = [c for c in dg.llama3b_sweep_cells() if c.G == cell_G and c.T == T]
+    for w in cells[1:3]:  # two sparsity levels per (G, T)
+        full_size_check(w, n_random=12)
