@@ -3,23 +3,25 @@
 //
 // The pages' GEMM-K runs each active K-group of a reordered token tile as its
 // own pipeline and scatters the partial outputs with atomic adds into a
-// zero-initialised buffer. On MI355X a measured fp32 global atomic add
-// sustains about 1.3 TB/s of payload whatever the footprint, and that design
-// issues one atomic per (active token, group, output column): about 15 GB at
-// the Llama3.1-8B prefill shape. So this kernel keeps the pages' skipping
-// predicates but owns its output tile instead:
+// zero-initialised buffer. On MI355X an fp32 global atomic add sustains about
+// 1.0-1.3 TB/s of payload whatever the footprint (one lane-operation per clock
+// per L2 channel), and that design issues one atomic per (active token, group,
+// output column): about 15 GB at the Llama3.1-8B prefill shape, over 10 ms.
+// So this kernel keeps the pages' group-level skipping but owns its outputs:
 //   * a workgroup owns Y[256 tokens (natural order), 256 output columns] and
-//     accumulates over the groups in registers; every output has one writer,
+//     accumulates over the K axis in registers; every output has one writer,
 //     no atomics, no zero-initialised buffer and a fixed summation order;
-//   * K-blocks (64 channels) whose groups are inactive for every token of the
-//     tile are skipped whole (copies, barriers and MFMAs): the K-block list is
-//     built once per workgroup from the packed mask bits;
-//   * H is loaded only for active (token, group) pairs; inactive pairs load
-//     zeros, so H needs no initialisation at masked channels.
-// Same data movement as the gate/up kernel: 16-byte loads one K-step ahead,
-// two XOR-swizzled LDS stages, v_mfma_f32_32x32x16_bf16 on 4 waves (2 x 2),
-// each wave 128 output columns x 128 tokens.
-#include "common.h"
+//   * 64-channel K-blocks whose groups are inactive for every token of the
+//     tile are skipped whole (copies, barriers and MFMAs); the list of live
+//     K-blocks is built once per workgroup from the packed mask bits;
+//   * H holds +0.0 at every (token, channel) whose group the token skips
+//     (written by the gate/up kernel), so inactive pairs contribute exactly 0.
+// Operands: MFMA A side = Wdown rows (output columns), B side = H rows
+// (tokens); the shared 8-wave mainloop streams both through LDS with
+// register-bypassing copies. Rows past d or T are zero-filled by
+// out-of-range buffer copies. The epilogue rounds once to bf16 (RNE) and
+// writes 16-byte row segments through an LDS staging tile.
+#include "mfma_core.h"
 
 namespace wide {
 
@@ -27,15 +29,16 @@ namespace {
 
 constexpr int kTile = 256;
 constexpr int kMaxSteps = 1024;  // d_ff / 64 limit (d_ff <= 65536)
+using DS = core::Shape<kTile, kTile, 2, 4>;
 
-__global__ __launch_bounds__(256, 1) void down_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void down_bf16_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint32_t* __restrict__ maskbits, int T, int d, int d_ff, int G, uint16_t* __restrict__ Y,
     int ntt, int nnt, int words) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTile * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kTile * 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[DS::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[DS::STAGE];
   __shared__ uint16_t s_steps[kMaxSteps];
-  __shared__ int s_wave_cnt[4];
+  __shared__ int s_wave_cnt[8];
 
   const int total = ntt * nnt;
   const int per_xcd = (total + 7) / 8;
@@ -45,13 +48,13 @@ __global__ __launch_bounds__(256, 1) void down_bf16_kernel(
   const int n0 = (L % nnt) * kTile;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w0 = t0 / 32;  // first mask word of this token tile
 
   // K-block admission: keep the 64-channel blocks with any active token.
   const int ksteps = d_ff / 64;
   int nst = 0;
-  for (int s0 = 0; s0 < ksteps; s0 += 256) {
+  for (int s0 = 0; s0 < ksteps; s0 += 512) {
     const int s = s0 + tid;
     bool any = false;
     if (s < ksteps) {
@@ -76,107 +79,73 @@ __global__ __launch_bounds__(256, 1) void down_bf16_kernel(
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
       s_steps[base + rank] = (uint16_t)s;
     }
-    for (int w = 0; w < 4; ++w) nst += s_wave_cnt[w];
+    for (int w = 0; w < 8; ++w) nst += s_wave_cnt[w];
     __syncthreads();
   }
 
-  const int kc = tid & 7;
-  const int rsub = tid >> 3;  // this thread stages rows rsub + 32*i, i = 0..7
-  // Row i of a thread is 32*i rows below row 0, so one base per operand does.
-  const uint16_t* pa0 = Wd + (size_t)(n0 + rsub) * d_ff + kc * 8;
-  const uint16_t* pb0 = H + (size_t)(t0 + rsub) * d_ff + kc * 8;
-  const size_t rstride = (size_t)32 * d_ff;
-  const int a_rows = d - n0 - rsub;  // row i valid iff 32*i < a_rows
-  const int b_rows = T - t0 - rsub;
-
-  u32x4 ra[8], rb[8];
-  auto load_step = [&](int k0) {
-    // mask bits of this thread's 8 token rows for the group of its chunk
-    const int gq = (k0 + kc * 8) / G;
-    const uint32_t* mw = maskbits + (size_t)gq * words + w0;
-    uint32_t bits[8];
+  // Copies: wave w fills 1 KB blocks w, w+8, w+16, w+24 of the Wdown rows
+  // and the same blocks of the H rows; rows past d or T get an out-of-range
+  // offset (zeros).
+  uint32_t voff_p[4], voff_q[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bits[i] = (w0 + i < words) ? mw[i] : 0u;
+  for (int i = 0; i < 4; ++i) {
+    const int b = wave + 8 * i;
+    const int chunk = core::copy_chunk(b, lane);
+    const int r = 8 * b + (lane >> 3);
+    voff_p[i] = (n0 + r < d) ? (uint32_t)((n0 + r) * d_ff + chunk * 8) * 2u : 0x80000000u;
+    voff_q[i] = (t0 + r < T) ? (uint32_t)((t0 + r) * d_ff + chunk * 8) * 2u : 0x80000000u;
+  }
+  const uint32_t w_bytes = (uint32_t)d * (uint32_t)d_ff * 2u;
+  const uint32_t h_bytes = (uint32_t)T * (uint32_t)d_ff * 2u;
+  auto issue = [&](int s, uint8_t* stage) {
+    const int k0 = (int)s_steps[s] * 64;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Wd + k0), 0, (int)(w_bytes - 2u * k0), 0x00020000);
+    const __amdgpu_buffer_rsrc_t hr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(H + k0), 0, (int)(h_bytes - 2u * k0), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = (32 * i < a_rows) ? *(const u32x4*)(pa0 + i * rstride + k0) : u32x4{0u, 0u, 0u, 0u};
-      const bool on = 32 * i < b_rows && ((bits[i] >> rsub) & 1u);
-      rb[i] = on ? *(const u32x4*)(pb0 + i * rstride + k0) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_step = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = rsub + 32 * i;
-      *(u32x4*)(&sA[s][swz(r, kc) * 8]) = ra[i];
-      *(u32x4*)(&sB[s][swz(r, kc) * 8]) = rb[i];
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave + 8 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void*)(stage + b * 1024), 16, voff_p[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (void*)(stage + DS::PBYTES + b * 1024), 16,
+                                               voff_q[i], 0, 0, 0);
     }
   };
 
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
+  const int wp = wave / DS::WQ;
+  const int wq = wave % DS::WQ;
+  core::Frags<DS> f;
+  core::mainloop<DS>(f, sA, sB, nst, wp, wq, lane, DS::FQ, issue);
+  __syncthreads();  // every wave is done with the stages: reuse them for the epilogue
 
-  f32x16 acc[4][4];
+  // Epilogue: staged as [256 tokens][256 columns] bf16 (512-byte rows, chunk
+  // c of row r at c ^ (r & 31)); token rows 0..127 in sA, 128..255 in sB.
+  const int lrow = lane & 31, lhalf = lane >> 5;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int j = 0; j < DS::FQ; ++j) {
+    const int r = wq * DS::QW + j * 32 + lrow;
+    uint8_t* row = (r < 128 ? sA : sB) + (r & 127) * 512;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
-
-  if (nst > 0) {
-    load_step(s_steps[0] * 64);
-    store_step(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nst; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nst) load_step(s_steps[it + 1] * 64);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = kk * 2 + lhalf;
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int row = wm * 128 + mi * 32 + lrow;
-        a[mi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sA[cur][swz(row, chunk) * 8]));
-      }
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int row = wn * 128 + ni * 32 + lrow;
-        b[ni] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sB[cur][swz(row, chunk) * 8]));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (it + 1 < nst) store_step(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: lane holds token (lane & 31) of each N fragment and output
-  // columns 8*(j/4) + 4*(lane/32) + (j%4) of each M fragment.
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int t = t0 + wn * 128 + ni * 32 + lrow;
-    if (t >= T) continue;
-    uint16_t* yrow = Y + (size_t)t * d;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int nb = n0 + wm * 128 + mi * 32;
-      if (nb >= d) continue;
+    for (int i = 0; i < DS::FP; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = 4 * q;
-        u32x2 v = {pack_bf16x2(acc[mi][ni][j], acc[mi][ni][j + 1]),
-                   pack_bf16x2(acc[mi][ni][j + 2], acc[mi][ni][j + 3])};
-        *(u32x2*)(yrow + nb + 8 * q + 4 * lhalf) = v;
+        const int nl = wp * DS::PW + i * 32 + 8 * q + 4 * lhalf;
+        const int c = nl >> 3, hh = (nl >> 2) & 1;
+        const u32x2 v = {pack_bf16x2(f.acc[i][j][4 * q], f.acc[i][j][4 * q + 1]),
+                         pack_bf16x2(f.acc[i][j][4 * q + 2], f.acc[i][j][4 * q + 3])};
+        *(u32x2*)(row + ((c ^ (r & 31)) << 4) + hh * 8) = v;
       }
     }
+  }
+  __syncthreads();
+  const int nrows = min(kTile, T - t0);
+  const int ncch = min(kTile, d - n0) / 8;  // 16-byte column chunks that exist
+  for (int e = tid; e < nrows * 32; e += 512) {
+    const int r = e >> 5, c = e & 31;
+    if (c >= ncch) continue;
+    const uint8_t* row = (r < 128 ? sA : sB) + (r & 127) * 512;
+    const u32x4 v = *(const u32x4*)(row + ((c ^ (r & 31)) << 4));
+    *(u32x4*)(Y + (size_t)(t0 + r) * d + n0 + c * 8) = v;
   }
 }
 
@@ -190,7 +159,7 @@ hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_
   const int words = (T + 31) / 32;
   const int total = ntt * nnt;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(down_bf16_kernel, dim3(per_xcd * 8), dim3(256), 0, stream, H, Wd, maskbits, T,
+  hipLaunchKernelGGL(down_bf16_kernel, dim3(per_xcd * 8), dim3(512), 0, stream, H, Wd, maskbits, T,
                      d, d_ff, G, Y, ntt, nnt, words);
   return hipGetLastError();
 }

@@ -3,52 +3,55 @@
 // N coordinate selects a routing group; admission, predicated computation and
 // a scatter epilogue).
 //
-// Workgroup tile: CW channels of one group (CW gate rows + CW up rows = the
-// MFMA M side, 2*CW <= 256) x 256 tokens taken from the group's reordered
-// token list (the MFMA N side), K = d in steps of 64. Skipping, as in the
-// pages' three levels, re-derived for gfx950:
-//   level 0: a workgroup whose 256-token tile starts at or past the group's
-//            active count exits before touching memory;
-//   level 1: token rows past the active count are never loaded (zeros go to
-//            LDS instead);
+// Workgroup tile: CW = min(G, 128) channels of one group and 256 positions of
+// the group's reordered token list. The MFMA A side holds the CW gate rows and
+// the CW up rows of those channels (per wave: its gate half first, then the
+// up half of the same channels, so one lane holds both accumulators of a
+// (channel, token) pair); the MFMA B side holds the gathered token rows of X.
+// The three skipping levels of the pages, re-derived for gfx950:
+//   level 0: a workgroup whose 256-position tile starts at or past the group's
+//            active count does no MFMA work at all;
+//   level 1: token rows past the active count are never fetched: their copies
+//            use an out-of-range buffer offset, which writes zeros to LDS
+//            without touching memory;
 //   level 2: 32-token MFMA fragments that lie wholly past the count are not
 //            multiplied.
-// The epilogue computes silu(gate) * up in fp32, rounds once to bf16 (RNE) and
-// scatters each token's row segment to H[token, channels].
-//
-// Data movement: 16-byte global loads into registers one K-step ahead, two
-// LDS stages (XOR-swizzled 128-byte rows), one barrier per K-step,
-// v_mfma_f32_32x32x16_bf16 on 4 waves. The gate and up rows of the same
-// channels are interleaved in LDS so that each lane holds both accumulators of
-// a (channel, token) pair and the epilogue needs no data exchange.
-#include "common.h"
+// Epilogue: silu(gate) * up in fp32, rounded once to bf16 (RNE), staged
+// through LDS and scattered as 16-byte row segments to H[token, channels].
+// Every (token, channel) of the group that the token skips is written as +0.0,
+// so H holds the full masked intermediate and the down projection can read it
+// densely.
+#include "mfma_core.h"
 
 namespace wide {
 
 namespace {
 
-template <int CW>
-struct MnCfg {
-  static constexpr int kRows = 2 * CW;               // gate + up rows in the tile
-  static constexpr int kWM = (CW == 128) ? 2 : 1;    // waves along M
-  static constexpr int kWN = 4 / kWM;                // waves along N (tokens)
-  static constexpr int kRowsPerWave = kRows / kWM;   // gate half + up half
-  static constexpr int kFM = kRowsPerWave / 32;      // 32-row MFMA fragments per wave
-  static constexpr int kFN = 256 / kWN / 32;         // 32-token fragments per wave
-  static constexpr int kAChunks = kRows * 8 / 256;   // 16-byte A chunks per thread per step
-};
-
 constexpr int kTokTile = 256;
 
 template <int CW>
-__global__ __launch_bounds__(256, 1) void gate_up_bf16_kernel(
+struct MnShape {
+  static constexpr int TP = 2 * CW;
+  static constexpr int WP = (TP >= 256) ? 2 : 1;
+  static constexpr int WQ = 8 / WP;
+  using S = core::Shape<TP, kTokTile, WP, WQ>;
+  static constexpr int PBLK = S::PBLOCKS, QBLK = S::QBLOCKS;
+  static constexpr int NBLK = PBLK + QBLK;
+  static constexpr int MAXB = (NBLK + 7) / 8;  // copy blocks per wave (upper bound)
+  static constexpr int HALF = S::PW / 2;       // channels per wave
+};
+
+// The body is a device function template called from one plain kernel per
+// channel width (a kernel template that passes a local lambda to the mainloop
+// loses its host launch stub with this toolchain).
+template <int CW>
+__device__ __forceinline__ void gate_up_body(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ Wu, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, int T, int d, int d_ff, int G, uint16_t* __restrict__ H,
-    int zero_inactive, int ntok_tiles, int nct, int total) {
-  using C = MnCfg<CW>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::kRows * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kTokTile * 64];
+    int ntok_tiles, int nct, int total, uint8_t* sA, uint8_t* sB, int* s_tok) {
+  using C = MnShape<CW>;
+  using S = typename C::S;
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so give
   // each XCD a contiguous range of (channel block, token tile) pairs; the
@@ -63,178 +66,155 @@ __global__ __launch_bounds__(256, 1) void gate_up_bf16_kernel(
   const int count = counts[g];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int32_t* __restrict__ prow = perm + (size_t)g * T + tile0;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ch0 = g * G + ct * CW;  // first channel of this tile
+  const int32_t* __restrict__ prow = perm + (size_t)g * T + tile0;
+  const int nrows = min(kTokTile, T - tile0);  // positions that exist
+  const int nact = max(0, min(nrows, count - tile0));  // active positions
 
-  if (tile0 >= count) {
-    // level 0: nothing active here. Only when H must hold exact zeros at
-    // masked channels do the inactive tokens of this tile get written.
-    if (!zero_inactive) return;
-    const int r = tid;
-    if (tile0 + r < T) {
-      u32x4* dst = (u32x4*)(H + (size_t)prow[r] * d_ff + ch0);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int c = 0; c < CW / 8; ++c) dst[c] = z;
-    }
-    return;
-  }
-
-  const int kc = tid & 7;  // this thread's 16-byte chunk within a 64-wide K step
-
-  // A (weight) rows this thread stages: LDS row r -> gate/up row of channel.
-  // Element offsets (they fit in 32 bits: d_ff*d and T*d stay below 2^31).
-  int oa[C::kAChunks];
-  bool agate[C::kAChunks];
-#pragma unroll
-  for (int i = 0; i < C::kAChunks; ++i) {
-    const int r = (tid + 256 * i) >> 3;
-    const int wmi = r / C::kRowsPerWave;
-    const int within = r % C::kRowsPerWave;
-    constexpr int half = C::kRowsPerWave / 2;
-    agate[i] = within < half;
-    const int ch = ch0 + wmi * half + (agate[i] ? within : within - half);
-    oa[i] = ch * d + kc * 8;
-  }
-  // B (token) rows this thread stages; level 1: rows past the count get -1.
-  int ob[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    ob[i] = (tile0 + r < count) ? prow[r] * d + kc * 8 : -1;
-  }
-
-  u32x4 ra[C::kAChunks];
-  u32x4 rb[8];
-  auto load_step = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::kAChunks; ++i)
-      ra[i] = *(const u32x4*)((agate[i] ? Wg : Wu) + oa[i] + k0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = (ob[i] >= 0) ? *(const u32x4*)(X + ob[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto store_step = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < C::kAChunks; ++i) {
-      const int r = (tid + 256 * i) >> 3;
-      *(u32x4*)(&sA[s][swz(r, kc) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *(u32x4*)(&sB[s][swz(r, kc) * 8]) = rb[i];
-    }
-  };
-
-  const int wm = wave / C::kWN;
-  const int wn = wave % C::kWN;
-  // level 2: fragments of this wave that hold at least one active token
-  const int wtok0 = tile0 + wn * C::kFN * 32;
-  int nact = (count - wtok0 + 31) / 32;
-  nact = nact < 0 ? 0 : (nact > C::kFN ? C::kFN : nact);
-
-  f32x16 acc[C::kFM][C::kFN];
-#pragma unroll
-  for (int mi = 0; mi < C::kFM; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < C::kFN; ++ni)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
-
-  const int nsteps = d / 64;
-  load_step(0);
-  store_step(0);
+  if (tid < kTokTile) s_tok[tid] = tid < nrows ? prow[tid] : 0;
   __syncthreads();
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    if (step + 1 < nsteps) load_step((step + 1) * 64);
-    if (nact > 0) {
+
+  // Zeros for the positions of this tile whose token skips the group.
+  {
+    constexpr int kChunks = CW / 8;  // 16-byte chunks per row segment
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int e = nact * kChunks + tid; e < nrows * kChunks; e += 512) {
+      const int r = e / kChunks, c = e % kChunks;
+      *(u32x4*)(H + (size_t)s_tok[r] * d_ff + ch0 + c * 8) = z;
+    }
+  }
+  if (nact == 0) return;  // level 0
+
+  // ---- copies: blocks [0, PBLK) are weight rows, [PBLK, NBLK) token rows.
+  // Wave w issues blocks w, w+8, ...; lane offsets are fixed per block.
+  uint32_t voff[C::MAXB];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int chunk = kk * 2 + lhalf;
-        bf16x8 a[C::kFM], b[C::kFN];
+  for (int i = 0; i < C::MAXB; ++i) {
+    const int b = wave + 8 * i;
+    const int chunk = core::copy_chunk(b, lane);
+    if (b < C::PBLK) {
+      // LDS row r -> (wave wp = r / PW, half) -> channel row of Wg or Wu
+      const int r = 8 * b + (lane >> 3);
+      const int within = r % S::PW;
+      const int chan = ch0 + (r / S::PW) * C::HALF + (within % C::HALF);
+      voff[i] = (uint32_t)(chan * d + chunk * 8) * 2u;
+    } else if (b < C::NBLK) {
+      const int r = 8 * (b - C::PBLK) + (lane >> 3);
+      voff[i] = r < nact ? (uint32_t)(s_tok[r] * d + chunk * 8) * 2u : 0x80000000u;
+    } else {
+      voff[i] = 0;
+    }
+  }
+  const uint32_t x_bytes = (uint32_t)T * (uint32_t)d * 2u;
+  auto issue = [&](int s, uint8_t* stage) {
+    const int k0 = s * core::kBK;
+    // token rows: out-of-range offsets fill zeros (level 1)
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(X + k0), 0, (int)(x_bytes - 2u * k0), 0x00020000);
 #pragma unroll
-        for (int mi = 0; mi < C::kFM; ++mi) {
-          const int row = wm * C::kRowsPerWave + mi * 32 + lrow;
-          a[mi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sA[cur][swz(row, chunk) * 8]));
-        }
-#pragma unroll
-        for (int ni = 0; ni < C::kFN; ++ni) {
-          const int row = wn * C::kFN * 32 + ni * 32 + lrow;
-          b[ni] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sB[cur][swz(row, chunk) * 8]));
-        }
-#pragma unroll
-        for (int ni = 0; ni < C::kFN; ++ni) {
-          if (ni < nact) {
-#pragma unroll
-            for (int mi = 0; mi < C::kFM; ++mi)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-          }
-        }
+    for (int i = 0; i < C::MAXB; ++i) {
+      const int b = wave + 8 * i;
+      if (b < C::PBLK) {
+        const int r0 = 8 * b;
+        const bool gate = (r0 % S::PW) < C::HALF;
+        const uint16_t* base = (gate ? Wg : Wu) + k0;
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)base + voff[i]),
+                                         (void*)(stage + b * 1024), 16, 0, 0);
+      } else if (b < C::NBLK) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void*)(stage + b * 1024), 16, voff[i], 0, 0,
+                                                 0);
       }
     }
-    if (step + 1 < nsteps) store_step(cur ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // Epilogue: lane holds token (lane & 31) of each N fragment and, per M
-  // fragment, rows 8*(j/4) + 4*(lane/32) + (j%4) for j = 0..15.
-  constexpr int half = C::kRowsPerWave / 2;
+  const int wp = wave / S::WQ;
+  const int wq = wave % S::WQ;
+  // level 2: this wave's 32-token fragments that hold an active position
+  const int nq = max(0, min(S::FQ, (nact - wq * S::QW + 31) / 32));
+  core::Frags<S> f;
+  core::mainloop<S>(f, sA, sB, d / core::kBK, wp, wq, lane, nq, issue);
+  __syncthreads();  // every wave is done with the stages: reuse them for the epilogue
+
+  // ---- epilogue: silu(gate) * up -> bf16, staged as [256 positions][CW] in LDS.
+  constexpr int kRowB = CW * 2;      // bytes per staged row
+  constexpr int kCpr = CW / 8;       // 16-byte chunks per staged row
+  uint8_t* stg = sA;                 // 256 * kRowB <= 64 KB fits in one stage
+  const int lrow = lane & 31, lhalf = lane >> 5;
 #pragma unroll
-  for (int ni = 0; ni < C::kFN; ++ni) {
-    const int i = wtok0 + ni * 32 + lrow;  // position in the group's token list
-    if (i >= T) continue;
-    const bool act = i < count;
-    if (!act && !zero_inactive) continue;
-    uint16_t* hrow = H + (size_t)prow[i - tile0] * d_ff + ch0 + wm * half;
-    if constexpr (C::kFM >= 2) {
+  for (int j = 0; j < S::FQ; ++j) {
+    const int r = wq * S::QW + j * 32 + lrow;  // position in the tile
+    if constexpr (S::FP >= 2) {
 #pragma unroll
-      for (int p = 0; p < C::kFM / 2; ++p) {
+      for (int i = 0; i < S::FP / 2; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float h[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int j = 4 * q + jj;
-            h[jj] = act ? silu_mul(acc[p][ni][j], acc[p + C::kFM / 2][ni][j]) : 0.0f;
-          }
-          u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-          *(u32x2*)(hrow + p * 32 + 8 * q + 4 * lhalf) = v;
+          for (int e = 0; e < 4; ++e)
+            h[e] = silu_mul(f.acc[i][j][4 * q + e], f.acc[i + S::FP / 2][j][4 * q + e]);
+          const int cl = wp * C::HALF + i * 32 + 8 * q + 4 * lhalf;  // channel within tile
+          const int c = cl >> 3, hh = (cl >> 2) & 1;
+          const u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+          *(u32x2*)(stg + r * kRowB + ((c ^ (r % kCpr)) << 4) + hh * 8) = v;
         }
       }
     } else {
-      // CW == 16: one fragment holds gate rows 0..15 (j < 8) and up rows 16..31 (j >= 8).
+      // CW == 16: one fragment holds gate rows 0..15 (e < 8) and up rows 16..31 (e >= 8)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float h[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = 4 * q + jj;
-          h[jj] = act ? silu_mul(acc[0][ni][j], acc[0][ni][j + 8]) : 0.0f;
-        }
-        u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-        *(u32x2*)(hrow + 8 * q + 4 * lhalf) = v;
+        for (int e = 0; e < 4; ++e) h[e] = silu_mul(f.acc[0][j][4 * q + e], f.acc[0][j][4 * q + e + 8]);
+        const int cl = 8 * q + 4 * lhalf;
+        const int c = cl >> 3, hh = (cl >> 2) & 1;
+        const u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        *(u32x2*)(stg + r * kRowB + ((c ^ (r % kCpr)) << 4) + hh * 8) = v;
       }
     }
   }
+  __syncthreads();
+  // active positions: 16-byte segments to H[token, ch0 .. ch0 + CW)
+  for (int e = tid; e < nact * kCpr; e += 512) {
+    const int r = e / kCpr, c = e % kCpr;
+    const u32x4 v = *(const u32x4*)(stg + r * kRowB + ((c ^ (r % kCpr)) << 4));
+    *(u32x4*)(H + (size_t)s_tok[r] * d_ff + ch0 + c * 8) = v;
+  }
 }
+
+#define WIDE_GATE_UP_KERNEL(CW)                                                               \
+  __global__ __launch_bounds__(512, 1) void gate_up_bf16_kernel_##CW(                             \
+      const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,                            \
+      const uint16_t* __restrict__ Wu, const int32_t* __restrict__ perm,                          \
+      const int32_t* __restrict__ counts, int T, int d, int d_ff, int G,                          \
+      uint16_t* __restrict__ H, int ntok_tiles, int nct, int total) {                             \
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[MnShape<CW>::S::STAGE];                  \
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[MnShape<CW>::S::STAGE];                  \
+    __shared__ int s_tok[kTokTile];                                                               \
+    gate_up_body<CW>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, ntok_tiles, nct, total, sA, sB,   \
+                     s_tok);                                                                      \
+  }
+WIDE_GATE_UP_KERNEL(128)
+WIDE_GATE_UP_KERNEL(64)
+WIDE_GATE_UP_KERNEL(32)
+WIDE_GATE_UP_KERNEL(16)
+#undef WIDE_GATE_UP_KERNEL
 
 template <int CW>
 hipError_t launch_cw(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu, const int32_t* perm,
                      const int32_t* counts, int T, int d, int d_ff, int G, uint16_t* H,
-                     bool zero_inactive, hipStream_t stream) {
+                     hipStream_t stream) {
   const int ng = d_ff / G;
   const int nct = G / CW;
   const int ntok_tiles = (T + kTokTile - 1) / kTokTile;
   const long long total = (long long)ng * nct * ntok_tiles;
   const int per_xcd = (int)((total + 7) / 8);
-  hipLaunchKernelGGL(gate_up_bf16_kernel<CW>, dim3(per_xcd * 8), dim3(256), 0, stream, X, Wg, Wu,
-                     perm, counts, T, d, d_ff, G, H, zero_inactive ? 1 : 0, ntok_tiles, nct,
-                     (int)total);
+  auto kernel = CW == 128 ? gate_up_bf16_kernel_128
+                : CW == 64  ? gate_up_bf16_kernel_64
+                : CW == 32  ? gate_up_bf16_kernel_32
+                            : gate_up_bf16_kernel_16;
+  hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(512), 0, stream, X, Wg, Wu, perm, counts, T, d,
+                     d_ff, G, H, ntok_tiles, nct, (int)total);
   return hipGetLastError();
 }
 
@@ -242,15 +222,12 @@ hipError_t launch_cw(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu, 
 
 hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
-                               int G, uint16_t* H, bool zero_inactive, hipStream_t stream) {
+                               int G, uint16_t* H, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (G % 128 == 0)
-    return launch_cw<128>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
-  if (G % 64 == 0)
-    return launch_cw<64>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
-  if (G % 32 == 0)
-    return launch_cw<32>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
-  return launch_cw<16>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
+  if (G % 128 == 0) return launch_cw<128>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
+  if (G % 64 == 0) return launch_cw<64>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
+  if (G % 32 == 0) return launch_cw<32>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
+  return launch_cw<16>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
 }
 
 }  // namespace wide

@@ -117,9 +117,11 @@ wide_status_t validate(const Args& a, bool* decode) {
     return fail(WIDE_ERR_UNSUPPORTED, "kernels need d %% 64 == 0, d_ff %% 64 == 0, G %% 16 == 0 (d=%d d_ff=%d G=%d)",
                 a.d, a.d_ff, a.G);
   if (a.d_ff > 65536) return fail(WIDE_ERR_UNSUPPORTED, "kernels need d_ff <= 65536 (d_ff=%d)", a.d_ff);
-  if ((int64_t)a.T * a.d_ff > INT32_MAX || (int64_t)a.T * a.d > INT32_MAX ||
-      (int64_t)a.d * a.d_ff > INT32_MAX)
-    return fail(WIDE_ERR_UNSUPPORTED, "T*d_ff, T*d and d*d_ff must stay below 2^31");
+  // The bf16 kernels address each operand with 32-bit byte offsets into a
+  // buffer of at most 2^31 - 1 bytes.
+  if ((int64_t)a.T * a.d_ff >= (1ll << 30) || (int64_t)a.T * a.d >= (1ll << 30) ||
+      (int64_t)a.d * a.d_ff >= (1ll << 30))
+    return fail(WIDE_ERR_UNSUPPORTED, "T*d_ff, T*d and d*d_ff must stay below 2^30");
   if (!aligned16(a.X) || !aligned16(a.Wg) || !aligned16(a.Wu) || !aligned16(a.Wd) ||
       !aligned16(a.Y) || (a.H_out && !aligned16(a.H_out)))
     return fail(WIDE_ERR_ALIGN, "X, W*, Y and H_out must be 16-byte aligned");
@@ -164,7 +166,7 @@ wide_status_t run_stage(wide_stage_t stage, const Args& a) {
       if (a.dt == WIDE_BF16)
         e = wide::launch_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
                                       (const uint16_t*)a.Wu, perm, counts, a.T, a.d, a.d_ff, a.G,
-                                      (uint16_t*)H, zero_h, a.stream);
+                                      (uint16_t*)H, a.stream);
       else
         e = wide::launch_gate_up_f32((const float*)a.X, (const float*)a.Wg, (const float*)a.Wu,
                                      perm, counts, a.T, a.d, a.d_ff, a.G, (float*)H, zero_h,
