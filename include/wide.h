@@ -117,19 +117,20 @@ size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G, wi
  *
  * Prefill path (T > wide_decode_max_t(), or WIDE_FLAG_FORCE_PREFILL): mask
  * reorder, then the gate/up kernel over each group's active prefix (tiles past
- * the prefix exit, rows past it are not loaded, fragments past it are not
- * multiplied; SiLU(gate)*up fused in the epilogue and scattered to H), then the
- * down kernel, which owns each [token tile x output tile] of Y, accumulates
- * over the groups in registers, skips every K-block whose groups are inactive
- * for the whole token tile and loads H only for active (token, group) pairs.
+ * the prefix do no MFMA work, rows past it are not fetched, fragments past it
+ * are not multiplied; SiLU(gate)*up fused in the epilogue and scattered to H,
+ * with +0.0 written for every skipped (token, group)), then the down kernel,
+ * which owns each [token tile x output tile] of Y, accumulates over the
+ * channels in registers and skips every 64-channel K-block whose groups are
+ * inactive for the whole token tile (WIDE paper App. B, GEMM-MN and GEMM-K).
  * Decode path (bf16, T <= wide_decode_max_t()): no reorder (WIDE paper App. B:
  * the T_q = 1 case checks routing directly); a gate/up GEMV and a down GEMV
  * that stream only the weight rows/segments of groups active for some token.
  *
  * Sizes: T >= 0 (T == 0 enqueues nothing; X, mask and Y may then be NULL);
- * d, d_ff, G >= 1 with d_ff % G == 0. The kernels also need
- * d % 64 == 0, d_ff % 64 == 0 and G % 16 == 0 (else WIDE_ERR_UNSUPPORTED);
- * T, d, d_ff, G and T*d_ff must fit in int32 arithmetic per kernel index.
+ * d, d_ff, G >= 1 with d_ff % G == 0. The kernels also need d % 64 == 0,
+ * d_ff % 64 == 0, G % 16 == 0, d_ff <= 65536 and T*d, T*d_ff, d*d_ff < 2^30
+ * (each operand within 2^31 bytes), else WIDE_ERR_UNSUPPORTED.
  * bf16 results differ from exact arithmetic by fp32 accumulation and the two
  * roundings; the reduction order is fixed, so a call is deterministic.
  * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_DTYPE, WIDE_ERR_ALIGN,
