@@ -1,31 +1,42 @@
 """Benchmark of the group-sparse FFN on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-dense] [--no-decode]
+    python bench.py --profile [--steps K]     # short run for rocprofv3 (prefill, decode, a copy)
+    python bench.py --summarize DIR [--command CMD]   # rocprofv3 CSVs in DIR -> profiles/*.md
 
 One step = one wide_ffn_forward call (mask reorder, gate/up kernel, down
 kernel) over the Llama3.1-8B-shaped prefill workload: T=16384 tokens, d=4096,
 d_ff=14336, G=128 (112 groups), bf16, top-50% Gaussian-score mask per token,
 inputs resident in HBM. `value` is the effective throughput on active work:
-6*d*G*A flops per step (A = active (token, group) pairs) over the step time.
+6*d*G*A flops per step (A = active (token, group) pairs) over the step time,
+launched eagerly; `graph_ms_per_step` is the same step replayed from a
+captured HIP graph (the pages time kernels under graph replay).
 
 Also reported, on the same line:
-  roofline      the dominant kernel's algorithmic TFLOP/s (its share of the
-                active flops, timed live with HIP events on its launch stream)
-                against the bf16 dense MFMA peak; `traffic` comes from the
-                rocprofv3 counter summary under profiles/ when that summary
-                was taken on the current kernel source, else null;
-  cpu_baseline  the fp64 oracle on a bounded token sample (host cores);
+  roofline      the dominant kernel (the longest): its algorithmic TFLOP/s
+                (its share of the active flops) over its average duration,
+                timed live with HIP events on the stream it is launched on,
+                against the bf16 dense MFMA peak. `traffic` is the HBM bytes
+                per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by
+                the same counters read on a copy of known size), kept in
+                profiles/traffic_<kernel>_<workload>.md, or null when that
+                summary was taken on other kernel sources;
+  per_kernel_ms reorder, gate/up and down, events between the stages;
   dense         torch bf16 GEMMs (hipBLASLt) for the unpruned FFN;
-  decode        T=1 and T=16 decode steps, active-weight GB/s with the
-                weights rotated over 8 copies so each call reads HBM.
+  decode        T=1 and T=16 decode steps: active-weight GB/s against HBM
+                peak, weights rotated over 8 copies so each call reads HBM;
+  cpu_baseline  the fp64 oracle on a bounded token sample (host cores).
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,11 +45,24 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CSRC = "group_sparse_ffn_amd/csrc"
+# sources that define each kernel (a change to any of them invalidates its counters)
 KERNEL_SOURCES = {
-    "gate_up": "group_sparse_ffn_amd/csrc/gemm_mn.hip",
-    "down": "group_sparse_ffn_amd/csrc/gemm_k.hip",
-    "reorder": "group_sparse_ffn_amd/csrc/reorder.hip",
+    "gate_up": ["gemm_mn.hip", "mfma_core.h", "common.h"],
+    "down": ["gemm_k.hip", "mfma_core.h", "common.h"],
+    "reorder": ["reorder.hip", "common.h"],
+    "decode_gate_up": ["decode.hip", "common.h"],
+    "decode_down": ["decode.hip", "common.h"],
 }
+# substrings of the device symbol names of each kernel
+KERNEL_SYMBOLS = {
+    "gate_up": "gate_up_bf16_kernel",
+    "down": "down_bf16_kernel",
+    "reorder": "reorder_kernel",
+    "decode_gate_up": "decode_gate_up_kernel",
+    "decode_down": "decode_down_kernel",
+}
+COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read + 1 GiB written
 
 
 def log(msg: str) -> None:
@@ -46,20 +70,34 @@ def log(msg: str) -> None:
 
 
 def source_sha(kernel: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.json, if current."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch from the counter summary, if taken on the current sources."""
+    path = traffic_path(kernel, workload)
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_sha") != source_sha(kernel):
-        return None  # counters were taken on an older version of the kernel
-    return rec.get("bytes_per_launch")
+        for line in f:
+            m = re.match(r"^- (\w+): (\S+)", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("source_sha") != source_sha(kernel):
+        return None  # counters were taken on another version of the kernel
+    try:
+        return int(float(fields["bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def time_events(torch, fn, steps: int) -> float:
@@ -75,7 +113,23 @@ def time_events(torch, fn, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def bench_prefill(torch, wide, dg, steps: int, warmup: int):
+def graph_step_ms(torch, fn, steps: int) -> float:
+    """Average ms of fn() replayed from a captured graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    ms = time_events(torch, g.replay, steps)
+    del g
+    return ms
+
+
+def bench_prefill(torch, wide, dg, steps: int, warmup: int, graph: bool = True):
     w = dg.LLAMA8B_PREFILL
     log(f"generating {w.name}")
     inp = dg.make_inputs(w)
@@ -91,7 +145,6 @@ def bench_prefill(torch, wide, dg, steps: int, warmup: int):
         call.run()
     torch.cuda.synchronize()
     log(f"timing {steps} forward steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ms = time_events(torch, call.run, steps)
     wall = (time.perf_counter() - t0) * 1e3 / steps
@@ -111,9 +164,12 @@ def bench_prefill(torch, wide, dg, steps: int, warmup: int):
     torch.cuda.synchronize()
     per = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
            for i, (name, _) in enumerate(stages)}
-    out = {"workload": w, "A": A, "ng": ng, "ms": ms, "wall_ms": wall, "flops": flops,
-           "per_kernel_ms": per, "inputs": inp, "dev_inputs": d, "call": call}
-    return out
+    gms = None
+    if graph:
+        log("graph replay")
+        gms = graph_step_ms(torch, call.run, steps)
+    return {"workload": w, "A": A, "ng": ng, "ms": ms, "wall_ms": wall, "graph_ms": gms,
+            "flops": flops, "per_kernel_ms": per, "inputs": inp, "dev_inputs": d, "call": call}
 
 
 def dense_baseline(torch, d, steps: int, warmup: int):
@@ -158,20 +214,24 @@ def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
                       f"sampled tokens' active groups"}
 
 
+def decode_setup(torch, wide, dg, w, copies: int):
+    inp = dg.make_inputs(w)
+    dev = "cuda:0"
+    X = inp["X"].to(dev)
+    mask = inp["mask"].to(dev)
+    ws = [{k: inp[k].to(dev) for k in ("Wg", "Wu", "Wd")}]
+    for _ in range(copies - 1):
+        ws.append({k: v.clone() for k, v in ws[0].items()})
+    calls = [wide.FfnCall(X, c["Wg"], c["Wu"], c["Wd"], mask, w.G) for c in ws]
+    union = int(inp["mask"].numpy().any(axis=0).sum())
+    return calls, ws, union
+
+
 def bench_decode(torch, wide, dg, steps: int, copies: int = 8):
     res = {}
     for w in (dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16):
         log(f"decode {w.name}")
-        inp = dg.make_inputs(w)
-        dev = "cuda:0"
-        X = inp["X"].to(dev)
-        mask = inp["mask"].to(dev)
-        ws = [{k: inp[k].to(dev) for k in ("Wg", "Wu", "Wd")}]
-        for _ in range(copies - 1):
-            ws.append({k: v.clone() for k, v in ws[0].items()})
-        calls = [wide.FfnCall(X, c["Wg"], c["Wu"], c["Wd"], mask, w.G) for c in ws]
-        m = inp["mask"].numpy()
-        union = int(m.any(axis=0).sum())
+        calls, ws, union = decode_setup(torch, wide, dg, w, copies)
         act_bytes = 3 * w.d * w.G * union * 2
         for c in calls:
             c.run()
@@ -183,13 +243,128 @@ def bench_decode(torch, wide, dg, steps: int, copies: int = 8):
             idx[0] += 1
 
         ms = time_events(torch, step, n)
+
+        def stage_fn(st):
+            def f():
+                calls[idx[0] % copies].stage(st)
+                idx[0] += 1
+            return f
+        # the down GEMV reads the H its copy's gate/up wrote on an earlier step
+        ms_gu = time_events(torch, stage_fn(wide.WIDE_STAGE_DECODE_GATE_UP), n)
+        ms_dn = time_events(torch, stage_fn(wide.WIDE_STAGE_DECODE_DOWN), n)
+
+        # graph replay: one graph holding `copies` steps over the rotated weights
+        def all_copies():
+            for c in calls:
+                c.run()
+        gms = graph_step_ms(torch, all_copies, max(steps, 4)) / copies
+        gu_bytes = 2 * w.d * w.G * union * 2
+        dn_bytes = w.d * w.G * union * 2
         res[f"T{w.T}"] = {"us_per_step": ms * 1e3, "active_weight_GBps": act_bytes / ms / 1e6,
                           "hbm_frac": act_bytes / ms / 1e6 / PEAK_HBM_GBS,
+                          "graph_us_per_step": gms * 1e3,
+                          "graph_hbm_frac": act_bytes / gms / 1e6 / PEAK_HBM_GBS,
                           "active_groups": union, "active_weight_MB": act_bytes / 1e6,
-                          "weight_copies": copies}
+                          "weight_copies": copies,
+                          "gate_up_us": ms_gu * 1e3, "gate_up_GBps": gu_bytes / ms_gu / 1e6,
+                          "down_us": ms_dn * 1e3, "down_GBps": dn_bytes / ms_dn / 1e6}
         del calls, ws
         torch.cuda.empty_cache()
     return res
+
+
+def run_profile(steps: int):
+    """Short run for rocprofv3: prefill steps, decode steps, and one copy of known size."""
+    import torch
+    import group_sparse_ffn_amd as wide
+    from group_sparse_ffn_amd import datagen as dg
+    r = bench_prefill(torch, wide, dg, steps, 1, graph=False)
+    del r["call"], r["dev_inputs"]
+    torch.cuda.empty_cache()
+    for w in (dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16):
+        calls, ws, _ = decode_setup(torch, wide, dg, w, 8)
+        for _ in range(2):
+            for c in calls:
+                c.run()
+        torch.cuda.synchronize()
+        del calls, ws
+        torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"profile run done: {steps} prefill steps, 16 decode steps per T, one {COPY_BYTES} B copy")
+
+
+def summarize(directory: str, command: str):
+    """Turn rocprofv3 CSVs (kernel stats, FETCH_SIZE and WRITE_SIZE counter runs) into profiles/*.md."""
+    from group_sparse_ffn_amd import datagen as dg
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        rows = list(csv.DictReader(open(stats[0])))
+        lines = ["# Kernel trace: Llama3.1-8B-shaped FFN (prefill T=16384 and decode T=1, T=16)",
+                 "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+                 "| kernel | calls | avg (us) | min (us) | max (us) | share |",
+                 "|---|---|---|---|---|---|"]
+        for r in rows:
+            name = r["Name"]
+            short = next((k for k, v in KERNEL_SYMBOLS.items() if v in name), name[:60])
+            lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        out = os.path.join(ROOT, "profiles", "kernel_trace_llama8b.md")
+        open(out, "w").write("\n".join(lines) + "\n")
+        print(f"wrote {out}")
+    per = {}  # counter -> kernel -> list of values (KiB per dispatch)
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            per.setdefault(r["Counter_Name"], {}).setdefault(r["Kernel_Name"], []).append(
+                float(r["Counter_Value"]))
+    if not per:
+        return
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        if counter not in per:
+            raise SystemExit(f"no {counter} rows under {directory}")
+
+    def copy_kib(counter):
+        vals = [v for name, vs in per[counter].items() if "copy" in name.lower()
+                for v in vs if v > COPY_BYTES / 1024 * 0.5]
+        if not vals:
+            raise SystemExit("the calibration copy is missing from the counter runs")
+        return sum(vals) / len(vals)
+
+    scale = {c: (COPY_BYTES / 1024) / copy_kib(c) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    workloads = {"gate_up": dg.LLAMA8B_PREFILL.name, "down": dg.LLAMA8B_PREFILL.name,
+                 "reorder": dg.LLAMA8B_PREFILL.name}
+    for kernel, sym in KERNEL_SYMBOLS.items():
+        vals = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            vs = [v for name, lst in per[counter].items() if sym in name for v in lst]
+            if vs:
+                vals[counter] = sum(vs) / len(vs)
+        if len(vals) < 2:
+            continue
+        fetch = vals["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+        write = vals["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+        workload = workloads.get(kernel, "llama3.1-8b-ffn-decode")
+        text = [f"# HBM traffic per launch: {kernel} ({workload})", "",
+                "Two rocprofv3 counter runs of the command below (one with FETCH_SIZE, one with",
+                "WRITE_SIZE), averaged over the kernel's dispatches, in KiB, scaled by what the same",
+                f"counter reads for a device copy of {COPY_BYTES} bytes in the same run.", "",
+                "```", command.replace("PMC", "FETCH_SIZE"), command.replace("PMC", "WRITE_SIZE"),
+                "```", "",
+                f"- FETCH_SIZE_KiB: {vals['FETCH_SIZE']:.1f}",
+                f"- WRITE_SIZE_KiB: {vals['WRITE_SIZE']:.1f}",
+                f"- fetch_scale: {scale['FETCH_SIZE']:.4f}",
+                f"- write_scale: {scale['WRITE_SIZE']:.4f}",
+                f"- fetch_bytes: {fetch:.0f}",
+                f"- write_bytes: {write:.0f}",
+                f"- bytes_per_launch: {fetch + write:.0f}",
+                f"- source_sha: {source_sha(kernel)}", ""]
+        out = traffic_path(kernel, workload)
+        open(out, "w").write("\n".join(text))
+        print(f"wrote {out}")
 
 
 def main():
@@ -200,11 +375,20 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the group-sparse FFN "
               "here has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.profile:
+        run_profile(args.steps)
+        return
 
     import torch
     import group_sparse_ffn_amd as wide
@@ -228,6 +412,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 4),
+        "graph_ms_per_step": round(r["graph_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

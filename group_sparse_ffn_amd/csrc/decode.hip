@@ -3,147 +3,264 @@
 // the routing can be checked without reordering; App. B GEMM-MN/GEMM-K:
 // GEMV variants for small M; Sec. 1: dedicated fast paths for decoding).
 //
-// Both kernels are bound by streaming weights from HBM. The 16 tokens sit on
-// the N side of v_mfma_f32_16x16x32_bf16 (tokens past T read as zeros), so
-// the matrix core does the dot products and every weight byte is loaded once
-// per call with 16-byte lane loads (four lanes cover 64 contiguous bytes of a
-// row per instruction).
-//
-// gate/up: a workgroup owns 16 channels of one group; its four waves split
-//   K = d and meet in LDS. A group no token executes costs one mask read.
-//   Output: H[t, c] = silu(gate)*up, or +0.0 where the token skips the group.
-// down:    a workgroup owns 16 output rows; it lists the 32-channel chunks
-//   whose group some token executes and its four waves split that list. Only
-//   those segments of each Wdown row are read; one writer per output.
+// Both kernels are bound by streaming weights from HBM, so they are built for
+// balance and memory-level parallelism:
+//   * weights are read with non-temporal 16-byte loads (no reuse) in batches
+//     of eight per lane; the next batch is issued before the MFMAs of the
+//     current one, so loads stay in flight while the wave computes;
+//   * the tokens sit on the N side of v_mfma_f32_16x16x32_bf16 (tokens past T
+//     read as zeros), so the matrix core does the dot products and every
+//     weight byte is loaded exactly once per call;
+//   * gate/up: the work is cut into units of 8 channels of one group (their
+//     8 gate rows and 8 up rows form one 16-row MFMA operand; for T > 4,
+//     16 channels with separate gate and up operands that share each
+//     activation fragment). Every
+//     workgroup lists the groups that some token executes (U) and takes the
+//     blockIdx-th unit of U, so the active units are packed onto the first
+//     workgroups and spread evenly over the CUs; workgroups past the last
+//     unit exit. Four waves split K and meet in LDS.
+//     Output: H[t, c] = silu(gate)*up, or +0.0 where token t skips the group.
+//   * down: a workgroup owns 16 output rows; it lists the 32-channel chunks
+//     whose group is in U and its eight waves split that list. Only those
+//     segments of each Wdown row are read; one writer per output.
 #include "common.h"
 
 namespace wide {
 
 namespace {
 
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 8;      // gate/up loads in flight per lane
+constexpr int kDownUnroll = 8;  // down loads in flight per lane
+constexpr int kMaxGroups = 4096;  // d_ff / 16
+constexpr int kDecodeSmallT = 4;  // largest T that uses 8-channel gate/up units
 
+__device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
 
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
-    const uint16_t* __restrict__ Wu, const uint8_t* __restrict__ mask, int T, int d, int d_ff,
-    int G, uint16_t* __restrict__ H, int zero_inactive) {
-  __shared__ float s_red[4][64][8];
+// Lists the groups (or 32-channel chunks) executed by some token into s_list
+// (ascending) and returns their number. Every thread of the block must call
+// it. `nitems` items; item i covers groups [glo(i), ghi(i)].
+template <int kThreads, class Range>
+__device__ __forceinline__ int list_active(const uint8_t* __restrict__ mask, int T, int ng,
+                                           int nitems, Range range, uint16_t* s_list,
+                                           int* s_wave_cnt) {
+  constexpr int kWaves = kThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n = 0;
+  for (int b0 = 0; b0 < nitems; b0 += kThreads) {
+    const int it = b0 + tid;
+    bool any = false;
+    if (it < nitems) {
+      int glo, ghi;
+      range(it, glo, ghi);
+      // all T mask bytes are requested before any is tested (T <= 16)
+      for (int g = glo; g <= ghi; ++g) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          if (t < T) m |= mask[(size_t)t * ng + g];
+        any |= m != 0;
+      }
+    }
+    const uint64_t bal = __ballot(any);
+    if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int base = n;
+    for (int w = 0; w < wave; ++w) base += s_wave_cnt[w];
+    if (any) {
+      const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      s_list[base + rank] = (uint16_t)it;
+    }
+    for (int w = 0; w < kWaves; ++w) n += s_wave_cnt[w];
+    __syncthreads();
+  }
+  return n;
+}
+
+constexpr int kGuThreads = 256;
+constexpr int kGuWaves = kGuThreads / 64;
+
+// One work unit: UC channels of one group, all T tokens, full K split over
+// the four waves. UC = 8: the 8 gate rows and 8 up rows form one 16-row MFMA
+// operand (finest balance; for few tokens the activation fragment costs
+// almost nothing). UC = 16: separate gate and up operands of 16 rows share
+// each activation fragment (half the activation traffic for many tokens).
+template <int UC>
+__device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
+                                             const uint16_t* __restrict__ Wg,
+                                             const uint16_t* __restrict__ Wu,
+                                             const uint8_t* __restrict__ mask, int T, int d,
+                                             int d_ff, int G, uint16_t* __restrict__ H,
+                                             int zero_inactive, uint16_t* s_groups,
+                                             int* s_wave_cnt, float (*s_red)[64][8]) {
+  constexpr int NF = UC / 8;  // 16-row A operands per unit
   const int ng = d_ff / G;
-  const int c0 = blockIdx.x * 16;
-  const int g = c0 / G;
+  const int upg = G / UC;  // units per group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const bool mine = lane < T && mask[(size_t)lane * ng + g] != 0;
-  if (__ballot(mine) == 0) {
-    // no token executes this group: its weights are never read
-    if (zero_inactive && tid < T * 2) {
+  const int nact = list_active<kGuThreads>(
+      mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
+  const int u = blockIdx.x;
+  if (u >= nact * upg) {
+    // Past the active units: when H must hold exact zeros, the units of the
+    // groups no token executes (in unit order after the active ones) are
+    // cleared here.
+    if (!zero_inactive) return;
+    const int k = u - nact * upg;  // k-th unit of an inactive group
+    if (k >= (ng - nact) * upg) return;
+    const int want = k / upg;  // the want-th group (ascending) that no token executes
+    int g = -1;
+    for (int gg = 0, seen = 0, ai = 0; gg < ng; ++gg) {
+      if (ai < nact && s_groups[ai] == gg) {
+        ++ai;
+        continue;
+      }
+      if (seen++ == want) {
+        g = gg;
+        break;
+      }
+    }
+    if (g >= 0 && tid < T * NF) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      *(u32x4*)(H + (size_t)(tid >> 1) * d_ff + c0 + (tid & 1) * 8) = z;
+      *(u32x4*)(H + (size_t)(tid / NF) * d_ff + g * G + (k % upg) * UC + (tid % NF) * 8) = z;
     }
     return;
   }
+  const int g = s_groups[u / upg];
+  const int c0 = g * G + (u % upg) * UC;
 
   // wave w takes the 32-wide K slices [s_lo, s_hi) of d / 32
   const int nsub_all = d / 32;
-  const int s_lo = (wave * nsub_all) / 4;
-  const int s_hi = ((wave + 1) * nsub_all) / 4;
+  const int s_lo = (wave * nsub_all) / kGuWaves;
+  const int s_hi = ((wave + 1) * nsub_all) / kGuWaves;
   const int kbase = s_lo * 32 + 8 * (lane >> 4);
-  const int row = c0 + (lane & 15);
+  const int r = lane & 15;
+  // operand rows: UC == 8: rows 0..7 gate, 8..15 up of channels c0..c0+7;
+  //               UC == 16: operand 0 = gate rows, operand 1 = up rows of c0..c0+15
+  const uint16_t* pw[NF];
+  if (NF == 1) {
+    pw[0] = (r < 8 ? Wg : Wu) + (size_t)(c0 + (r & 7)) * d + kbase;
+  } else {
+    pw[0] = Wg + (size_t)(c0 + r) * d + kbase;
+    pw[NF - 1] = Wu + (size_t)(c0 + r) * d + kbase;
+  }
   const int tok = lane & 15;
-  const uint16_t* pg = Wg + (size_t)row * d + kbase;
-  const uint16_t* pu = Wu + (size_t)row * d + kbase;
   const uint16_t* px = (tok < T) ? X + (size_t)tok * d + kbase : nullptr;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nsub = s_hi - s_lo;
-  int s = 0;
-  for (; s + kUnroll <= nsub; s += kUnroll) {
-    u32x4 ag[kUnroll], au[kUnroll], bx[kUnroll];
+  // Software pipeline: the loads of batch b+1 are issued before the MFMAs of
+  // batch b, so every wave keeps a batch of loads in flight while it computes.
+  const int nb = nsub / kUnroll;
+  u32x4 aw[2][NF][kUnroll], bx[2][kUnroll];
+  auto load_batch = [&](int b, int set) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      ag[u] = ld16(pg + 32 * (s + u));
-      au[u] = ld16(pu + 32 * (s + u));
-      bx[u] = px ? ld16(px + 32 * (s + u)) : zero;
-    }
+    for (int q = 0; q < kUnroll; ++q) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, bx[u]);
-      acc_g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ag[u]), b, acc_g, 0, 0, 0);
-      acc_u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, au[u]), b, acc_u, 0, 0, 0);
+      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16_nt(pw[f] + 32 * (b * kUnroll + q));
+      bx[set][q] = px ? ld16(px + 32 * (b * kUnroll + q)) : zero;
     }
+  };
+  auto mma_batch = [&](int set) {
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw[set][f][q]),
+                                                         __builtin_bit_cast(bf16x8, bx[set][q]),
+                                                         acc[f], 0, 0, 0);
+  };
+  if (nb > 0) load_batch(0, 0);
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) load_batch(b + 1, 1);
+    mma_batch(0);
+    if (b + 1 >= nb) break;
+    if (b + 2 < nb) load_batch(b + 2, 0);
+    mma_batch(1);
   }
-  for (; s < nsub; ++s) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, px ? ld16(px + 32 * s) : zero);
-    acc_g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pg + 32 * s)), b, acc_g, 0, 0, 0);
-    acc_u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pu + 32 * s)), b, acc_u, 0, 0, 0);
+  for (int s = nb * kUnroll; s < nsub; ++s) {
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, px ? ld16(px + 32 * s) : zero);
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw[f] + 32 * s)),
+                                                       bv, acc[f], 0, 0, 0);
   }
 
+  // lane holds token (lane % 16) and operand rows 4*(lane/16) + e.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s_red[wave][lane][j] = acc_g[j];
-    s_red[wave][lane][4 + j] = acc_u[j];
-  }
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_red[wave][lane][4 * f + e] = acc[f][e];
   __syncthreads();
   if (wave != 0 || tok >= T) return;
-  // lane holds rows (channels) 4*(lane/16) + j and column (token) lane % 16
+  // UC == 8: gate channels 0..7 sit in lanes 0..31, the matching up rows in
+  // lanes 32..63; UC == 16: gate (operand 0) and up (operand 1) share a lane.
+  if (NF == 1 && lane >= 32) return;
   // A token that skips this group still gets +0.0 here: the down GEMV reads
   // every channel of a group that some token executes.
   const bool act = mask[(size_t)tok * ng + g] != 0;
   float h[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float gs = s_red[0][lane][j] + s_red[1][lane][j] + s_red[2][lane][j] + s_red[3][lane][j];
-    const float us = s_red[0][lane][4 + j] + s_red[1][lane][4 + j] + s_red[2][lane][4 + j] +
-                     s_red[3][lane][4 + j];
-    h[j] = act ? silu_mul(gs, us) : 0.0f;
+  for (int e = 0; e < 4; ++e) {
+    float gs = 0.0f, us = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGuWaves; ++w) {
+      gs += s_red[w][lane][e];
+      us += (NF == 1) ? s_red[w][lane + 32][e] : s_red[w][lane][4 + e];
+    }
+    h[e] = act ? silu_mul(gs, us) : 0.0f;
   }
-  u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+  const u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
   *(u32x2*)(H + (size_t)tok * d_ff + c0 + 4 * (lane >> 4)) = v;
 }
 
-__global__ __launch_bounds__(256) void decode_down_kernel(
+#define WIDE_DECODE_GATE_UP_KERNEL(UC)                                                          \
+  __global__ __launch_bounds__(kGuThreads) void decode_gate_up_kernel_##UC(                      \
+      const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,                          \
+      const uint16_t* __restrict__ Wu, const uint8_t* __restrict__ mask, int T, int d,          \
+      int d_ff, int G, uint16_t* __restrict__ H, int zero_inactive) {                           \
+    __shared__ uint16_t s_groups[kMaxGroups];                                                   \
+    __shared__ int s_wave_cnt[kGuWaves];                                                        \
+    __shared__ float s_red[kGuWaves][64][8];                                                    \
+    gate_up_unit<UC>(X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive, s_groups, s_wave_cnt,    \
+                     s_red);                                                                    \
+  }
+WIDE_DECODE_GATE_UP_KERNEL(8)
+WIDE_DECODE_GATE_UP_KERNEL(16)
+#undef WIDE_DECODE_GATE_UP_KERNEL
+
+constexpr int kDownThreads = 512;
+constexpr int kDownWaves = kDownThreads / 64;
+
+__global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G, uint16_t* __restrict__ Y) {
   constexpr int kMaxChunks = 2048;  // d_ff / 32 limit
   __shared__ uint16_t s_chunks[kMaxChunks];
-  __shared__ int s_wave_cnt[4];
-  __shared__ float s_red[4][64][4];
+  __shared__ int s_wave_cnt[kDownWaves];
+  __shared__ float s_red[kDownWaves][64][4];
   const int ng = d_ff / G;
   const int n0 = blockIdx.x * 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // chunks (32 channels) whose group some token executes
-  const int nchunks = d_ff / 32;
-  int nch = 0;
-  for (int b0 = 0; b0 < nchunks; b0 += 256) {
-    const int ch = b0 + tid;
-    bool any = false;
-    if (ch < nchunks) {
-      const int glo = (ch * 32) / G;
-      const int ghi = (ch * 32 + 31) / G;
-      for (int t = 0; t < T && !any; ++t)
-        for (int g = glo; g <= ghi; ++g) any |= mask[(size_t)t * ng + g] != 0;
-    }
-    const uint64_t bal = __ballot(any);
-    if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int base = nch;
-    for (int w = 0; w < wave; ++w) base += s_wave_cnt[w];
-    if (any) {
-      const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      s_chunks[base + rank] = (uint16_t)ch;
-    }
-    for (int w = 0; w < 4; ++w) nch += s_wave_cnt[w];
-    __syncthreads();
-  }
+  // 32-channel chunks whose group some token executes
+  const int nch = list_active<kDownThreads>(
+      mask, T, ng, d_ff / 32,
+      [G](int c, int& lo, int& hi) {
+        lo = (c * 32) / G;
+        hi = (c * 32 + 31) / G;
+      },
+      s_chunks, s_wave_cnt);
 
   const int koff = 8 * (lane >> 4);
   const int tok = lane & 15;
@@ -151,35 +268,52 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
   const uint16_t* ph = (tok < T) ? H + (size_t)tok * d_ff + koff : nullptr;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int i = wave;
-  for (; i + 4 * (kUnroll - 1) < nch; i += 4 * kUnroll) {
-    u32x4 a[kUnroll], b[kUnroll];
+  // this wave takes chunks wave, wave + kDownWaves, ...; batches of kDownUnroll
+  // chunks, the loads of batch b+1 issued before the MFMAs of batch b
+  const int mine = nch > wave ? (nch - wave + kDownWaves - 1) / kDownWaves : 0;
+  const int nb = mine / kDownUnroll;
+  u32x4 a[2][kDownUnroll], bb[2][kDownUnroll];
+  auto load_batch = [&](int b, int set) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int k = (int)s_chunks[i + 4 * u] * 32;
-      a[u] = ld16(pw + k);
-      b[u] = ph ? ld16(ph + k) : zero;
+    for (int q = 0; q < kDownUnroll; ++q) {
+      const int k = (int)s_chunks[wave + kDownWaves * (b * kDownUnroll + q)] * 32;
+      a[set][q] = ld16_nt(pw + k);
+      bb[set][q] = ph ? ld16(ph + k) : zero;
     }
+  };
+  auto mma_batch = [&](int set) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                    __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+    for (int q = 0; q < kDownUnroll; ++q)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[set][q]),
+                                                    __builtin_bit_cast(bf16x8, bb[set][q]), acc, 0, 0, 0);
+  };
+  if (nb > 0) load_batch(0, 0);
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) load_batch(b + 1, 1);
+    mma_batch(0);
+    if (b + 1 >= nb) break;
+    if (b + 2 < nb) load_batch(b + 2, 0);
+    mma_batch(1);
   }
-  for (; i < nch; i += 4) {
-    const int k = (int)s_chunks[i] * 32;
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw + k)),
+  for (int j = nb * kDownUnroll; j < mine; ++j) {
+    const int k = (int)s_chunks[wave + kDownWaves * j] * 32;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw + k)),
                                                   __builtin_bit_cast(bf16x8, ph ? ld16(ph + k) : zero),
                                                   acc, 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s_red[wave][lane][j] = acc[j];
+  for (int e = 0; e < 4; ++e) s_red[wave][lane][e] = acc[e];
   __syncthreads();
   if (wave != 0 || tok >= T) return;
   float y[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    y[j] = s_red[0][lane][j] + s_red[1][lane][j] + s_red[2][lane][j] + s_red[3][lane][j];
-  u32x2 v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  for (int e = 0; e < 4; ++e) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDownWaves; ++w) sum += s_red[w][lane][e];
+    y[e] = sum;
+  }
+  const u32x2 v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
   *(u32x2*)(Y + (size_t)tok * d + n0 + 4 * (lane >> 4)) = v;
 }
 
@@ -189,16 +323,22 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
                                       const uint8_t* mask, int T, int d, int d_ff, int G,
                                       uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_gate_up_kernel, dim3(d_ff / 16), dim3(256), 0, stream, X, Wg, Wu, mask,
-                     T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+  // few tokens: 8-channel units (finest balance); more tokens: 16-channel
+  // units whose gate and up operands share each activation fragment
+  if (T <= kDecodeSmallT)
+    hipLaunchKernelGGL(decode_gate_up_kernel_8, dim3(d_ff / 8), dim3(kGuThreads), 0, stream, X, Wg,
+                       Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+  else
+    hipLaunchKernelGGL(decode_gate_up_kernel_16, dim3(d_ff / 16), dim3(kGuThreads), 0, stream, X,
+                       Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
                                    int T, int d, int d_ff, int G, uint16_t* Y, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_down_kernel, dim3(d / 16), dim3(256), 0, stream, H, Wd, mask, T, d,
-                     d_ff, G, Y);
+  hipLaunchKernelGGL(decode_down_kernel, dim3(d / 16), dim3(kDownThreads), 0, stream, H, Wd, mask,
+                     T, d, d_ff, G, Y);
   return hipGetLastError();
 }
 
