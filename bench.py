@@ -317,10 +317,13 @@ def summarize(directory: str, command: str):
         open(out, "w").write("\n".join(lines) + "\n")
         print(f"wrote {out}")
     per = {}  # counter -> kernel -> list of values (KiB per dispatch)
+    per_id = {}  # counter -> kernel -> list of (dispatch id, value)
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
             per.setdefault(r["Counter_Name"], {}).setdefault(r["Kernel_Name"], []).append(
                 float(r["Counter_Value"]))
+            per_id.setdefault(r["Counter_Name"], {}).setdefault(r["Kernel_Name"], []).append(
+                (int(r["Dispatch_Id"]), float(r["Counter_Value"])))
     if not per:
         return
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -335,19 +338,29 @@ def summarize(directory: str, command: str):
         return sum(vals) / len(vals)
 
     scale = {c: (COPY_BYTES / 1024) / copy_kib(c) for c in ("FETCH_SIZE", "WRITE_SIZE")}
-    workloads = {"gate_up": dg.LLAMA8B_PREFILL.name, "down": dg.LLAMA8B_PREFILL.name,
-                 "reorder": dg.LLAMA8B_PREFILL.name}
-    for kernel, sym in KERNEL_SYMBOLS.items():
+    # (kernel, workload, dispatch selector): the profile run launches the decode
+    # kernels for T=1 first (16 calls), then for T=16
+    jobs = [("gate_up", dg.LLAMA8B_PREFILL.name, None), ("down", dg.LLAMA8B_PREFILL.name, None),
+            ("reorder", dg.LLAMA8B_PREFILL.name, None),
+            ("decode_gate_up", dg.LLAMA8B_DECODE_T1.name, 0),
+            ("decode_gate_up", dg.LLAMA8B_DECODE_T16.name, 1),
+            ("decode_down", dg.LLAMA8B_DECODE_T1.name, 0),
+            ("decode_down", dg.LLAMA8B_DECODE_T16.name, 1)]
+    for kernel, workload, half in jobs:
+        sym = KERNEL_SYMBOLS[kernel]
         vals = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            vs = [v for name, lst in per[counter].items() if sym in name for v in lst]
+            vs = [(d_id, v) for name, lst in per_id[counter].items() if sym in name for d_id, v in lst]
+            vs.sort()
+            if half is not None:
+                h = len(vs) // 2
+                vs = vs[:h] if half == 0 else vs[h:]
             if vs:
-                vals[counter] = sum(vs) / len(vs)
+                vals[counter] = sum(v for _, v in vs) / len(vs)
         if len(vals) < 2:
             continue
         fetch = vals["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
         write = vals["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
-        workload = workloads.get(kernel, "llama3.1-8b-ffn-decode")
         text = [f"# HBM traffic per launch: {kernel} ({workload})", "",
                 "Two rocprofv3 counter runs of the command below (one with FETCH_SIZE, one with",
                 "WRITE_SIZE), averaged over the kernel's dispatches, in KiB, scaled by what the same",
@@ -429,9 +442,18 @@ def main():
     if not args.no_dense:
         log("dense baseline")
         dms = dense_baseline(torch, r["dev_inputs"], max(5, args.steps // 2), 2)
+        # the same library path on an all-ones mask: the dense limit of these kernels
+        dv = r["dev_inputs"]
+        ones = torch.ones_like(dv["mask"])
+        call1 = wide.FfnCall(dv["X"], dv["Wg"], dv["Wu"], dv["Wd"], ones, w.G)
+        call1.run()
+        oms = time_events(torch, call1.run, max(5, args.steps // 2))
+        del call1
         line["dense"] = {"ms": round(dms, 4), "impl": "torch bf16 matmul (hipBLASLt)",
                          "speedup": round(dms / r["ms"], 3),
-                         "ideal_speedup": round(w.T * r["ng"] / r["A"], 3)}
+                         "ideal_speedup": round(w.T * r["ng"] / r["A"], 3),
+                         "all_ones_mask_ms": round(oms, 4),
+                         "speedup_vs_all_ones_mask": round(oms / r["ms"], 3)}
     del r["call"], r["dev_inputs"]
     torch.cuda.empty_cache()
     if not args.no_decode:

@@ -119,7 +119,10 @@ def test_ffn_small_all_outputs(T, d, d_ff, G, dtype, density, flags):
     assert rel_err(H, Href) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("T,G", [(1, 128), (3, 128), (16, 128), (5, 16), (16, 32)])
+# T <= 4 runs 8-channel gate/up units, T > 4 16-channel units; G = 16 and 32 put
+# several units in one group.
+@pytest.mark.parametrize("T,G", [(1, 128), (3, 128), (16, 128), (5, 16), (16, 32), (2, 16),
+                                 (4, 32), (1, 64), (8, 256)])
 def test_decode_path_vs_oracle(T, G):
     d, d_ff = 512, 2048
     assert T <= wide.decode_max_t() or T <= wide.WIDE_DECODE_T_LIMIT
@@ -128,6 +131,55 @@ def test_decode_path_vs_oracle(T, G):
     _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
     assert rel_err(Y, Yref) <= TOL["bf16"]
     check_h_zeros(H, inp["mask"], G)
+
+
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_decode_edge_masks(T):
+    """Decode path: empty groups, tokens with no group, one active group, all-zero mask."""
+    d, d_ff, G = 256, 1024, 32
+    ng = d_ff // G
+    inp = dg.random_small(300 + T, T, d, d_ff, G, "bf16", 0.4, wscale=0.05)
+    masks = []
+    m = inp["mask"].clone()
+    m[:, 2] = 0
+    m[0, :] = 0          # token 0 executes nothing
+    masks.append(m)
+    one = torch.zeros((T, ng), dtype=torch.uint8)
+    one[T - 1, ng - 1] = 1   # a single (token, group) pair in the last group
+    masks.append(one)
+    masks.append(torch.zeros((T, ng), dtype=torch.uint8))
+    for m in masks:
+        inp["mask"] = m
+        Y, H = run_ffn(inp, G, flags=wide.WIDE_FLAG_FORCE_DECODE)
+        _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], m, G)
+        check_h_zeros(H, m, G)
+        idle = (m.sum(dim=1) == 0).nonzero().flatten().tolist()
+        for t in idle:
+            assert bool((Y[t] == 0).all()) and not bool(torch.signbit(Y[t].float()).any())
+        if m.any():
+            assert rel_err(Y, Yref) <= TOL["bf16"]
+        else:
+            assert bool((Y == 0).all())
+
+
+@pytest.mark.parametrize("T,G,flags", [(700, 128, 0), (300, 16, 0), (3, 128, 0), (12, 64, 0),
+                                       (12, 64, wide.WIDE_FLAG_FORCE_PREFILL)])
+def test_result_does_not_depend_on_h_out(T, G, flags):
+    """Y with H kept in the workspace equals Y with H returned, bit for bit."""
+    d, d_ff = 256, 1024
+    inp = to_dev(dg.random_small(400 + T, T, d, d_ff, G, "bf16", 0.5, wscale=0.05))
+    a = wide.FfnCall(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G, flags=flags)
+    b = wide.FfnCall(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G, return_h=True,
+                     flags=flags)
+    # workspace and outputs start as garbage
+    a.workspace.fill_(0xAB)
+    a.Y.fill_(3.0)
+    b.H.fill_(-5.0)
+    Ya = a.run().clone()
+    Yb = b.run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(Ya, Yb)
+    check_h_zeros(b.H, inp["mask"], G)
 
 
 def test_decode_equals_prefill_within_tolerance_t16():
