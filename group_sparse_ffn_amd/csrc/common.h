@@ -58,14 +58,20 @@ hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t*
                           int32_t* counts, int32_t* padded, uint32_t* maskbits,
                           hipStream_t stream);
 
+// Largest group count for which the bf16 down kernel keeps the token tile's
+// mask bits in LDS and skips the H copies of inactive (token, group) pairs.
+constexpr int kDownMaxGroups = 768;
+
 // bf16 prefill gate/up over the reordered tokens (tile = 256 tokens). Writes
-// every element of H: the masked intermediate, +0.0 where the token skips.
+// H[t, c] for every active (token, group); with zero_inactive it also writes
+// +0.0 at every (token, channel) whose group the token skips.
 hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
-                               int G, uint16_t* H, hipStream_t stream);
+                               int G, uint16_t* H, bool zero_inactive, hipStream_t stream);
 
-// bf16 prefill down projection (output-stationary; H must be +0.0 at masked
-// channels; K-blocks inactive for a whole token tile are skipped).
+// bf16 prefill down projection (output-stationary; K-blocks inactive for a
+// whole token tile are skipped; with d_ff / G <= kDownMaxGroups the H copies of
+// inactive (token, group) pairs are skipped too, else H must hold +0.0 there).
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
                             int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
 

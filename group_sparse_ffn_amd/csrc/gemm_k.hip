@@ -14,8 +14,14 @@
 //   * 64-channel K-blocks whose groups are inactive for every token of the
 //     tile are skipped whole (copies, barriers and MFMAs); the list of live
 //     K-blocks is built once per workgroup from the packed mask bits;
-//   * H holds +0.0 at every (token, channel) whose group the token skips
-//     (written by the gate/up kernel), so inactive pairs contribute exactly 0.
+//   * the copy of an H row segment whose (token, group) is inactive uses an
+//     out-of-range buffer offset, which zero-fills LDS without touching
+//     memory (level-1 skipping of A packets): inactive pairs contribute
+//     exactly 0 whatever H holds there, and cost no HBM traffic. The tile's
+//     mask bits (256 tokens x ngroups) sit in an LDS table built once per
+//     workgroup; with more than kDownMaxGroups groups the table does not fit,
+//     the copies are not predicated, and the gate/up kernel writes +0.0 at
+//     every skipped (token, channel) instead.
 // Operands: MFMA A side = Wdown rows (output columns), B side = H rows
 // (tokens); the shared 8-wave mainloop streams both through LDS with
 // register-bypassing copies. Rows past d or T are zero-filled by
@@ -38,6 +44,7 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t sA[DS::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[DS::STAGE];
   __shared__ uint16_t s_steps[kMaxSteps];
+  __shared__ __attribute__((aligned(16))) uint32_t s_mw[kDownMaxGroups * 8];  // [group][8 words]: the tile's mask bits
   __shared__ int s_wave_cnt[8];
 
   const int total = ntt * nnt;
@@ -50,6 +57,17 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w0 = t0 / 32;  // first mask word of this token tile
+  const int ng = d_ff / G;
+  const bool table = ng <= kDownMaxGroups;
+
+  // the tile's mask words, group-major (zero past the last word)
+  if (table) {
+    for (int e = tid; e < ng * 8; e += 512) {
+      const int g = e >> 3, wi = e & 7;
+      s_mw[e] = (w0 + wi < words) ? maskbits[(size_t)g * words + w0 + wi] : 0u;
+    }
+    __syncthreads();
+  }
 
   // K-block admission: keep the 64-channel blocks with any active token.
   const int ksteps = d_ff / 64;
@@ -62,10 +80,15 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
       const int ghi = (s * 64 + 63) / G;
       uint32_t acc = 0;
       for (int g = glo; g <= ghi; ++g) {
-        const uint32_t* mw = maskbits + (size_t)g * words;
+        if (table) {
 #pragma unroll
-        for (int wi = 0; wi < 8; ++wi)
-          if (w0 + wi < words) acc |= mw[w0 + wi];
+          for (int wi = 0; wi < 8; ++wi) acc |= s_mw[g * 8 + wi];
+        } else {
+          const uint32_t* mw = maskbits + (size_t)g * words;
+#pragma unroll
+          for (int wi = 0; wi < 8; ++wi)
+            if (w0 + wi < words) acc |= mw[w0 + wi];
+        }
       }
       any = acc != 0;
     }
@@ -85,18 +108,34 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
 
   // Copies: wave w fills 1 KB blocks w, w+8, w+16, w+24 of the Wdown rows
   // and the same blocks of the H rows; rows past d or T get an out-of-range
-  // offset (zeros).
+  // offset (zeros). The lane's 16-byte chunk is the same in all its blocks.
+  const int chunk = core::copy_chunk(wave, lane);
   uint32_t voff_p[4], voff_q[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = wave + 8 * i;
-    const int chunk = core::copy_chunk(b, lane);
     const int r = 8 * b + (lane >> 3);
     voff_p[i] = (n0 + r < d) ? (uint32_t)((n0 + r) * d_ff + chunk * 8) * 2u : 0x80000000u;
     voff_q[i] = (t0 + r < T) ? (uint32_t)((t0 + r) * d_ff + chunk * 8) * 2u : 0x80000000u;
   }
+  // row r = 8*(wave + 8i) + lane/8 of the tile: mask word 2i + rw/32, bit rw%32
+  const int rw = 8 * wave + (lane >> 3);
   const uint32_t w_bytes = (uint32_t)d * (uint32_t)d_ff * 2u;
   const uint32_t h_bytes = (uint32_t)T * (uint32_t)d_ff * 2u;
+  // H copy offsets of the next stage to issue, with inactive (token, group)
+  // pairs turned into out-of-range offsets; computed by prepare() while the
+  // MFMAs of an earlier stage run.
+  uint32_t vq_next[4];
+  auto prepare = [&](int s) {
+    const int k0 = (int)s_steps[s] * 64;
+    const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * 8;  // this lane's group
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t vq = voff_q[i];
+      if (table && !((mw[2 * i + (rw >> 5)] >> (rw & 31)) & 1u)) vq = 0x80000000u;
+      vq_next[i] = vq;
+    }
+  };
   auto issue = [&](int s, uint8_t* stage) {
     const int k0 = (int)s_steps[s] * 64;
     const __amdgpu_buffer_rsrc_t wr =
@@ -108,14 +147,14 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
       const int b = wave + 8 * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void*)(stage + b * 1024), 16, voff_p[i], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (void*)(stage + DS::PBYTES + b * 1024), 16,
-                                               voff_q[i], 0, 0, 0);
+                                               vq_next[i], 0, 0, 0);
     }
   };
 
   const int wp = wave / DS::WQ;
   const int wq = wave % DS::WQ;
   core::Frags<DS> f;
-  core::mainloop<DS>(f, sA, sB, nst, wp, wq, lane, DS::FQ, issue);
+  core::mainloop<DS>(f, sA, sB, nst, wp, wq, lane, DS::FQ, issue, prepare);
   __syncthreads();  // every wave is done with the stages: reuse them for the epilogue
 
   // Epilogue: staged as [256 tokens][256 columns] bf16 (512-byte rows, chunk

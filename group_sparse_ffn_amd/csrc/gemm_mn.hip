@@ -18,9 +18,9 @@
 //            multiplied.
 // Epilogue: silu(gate) * up in fp32, rounded once to bf16 (RNE), staged
 // through LDS and scattered as 16-byte row segments to H[token, channels].
-// Every (token, channel) of the group that the token skips is written as +0.0,
-// so H holds the full masked intermediate and the down projection can read it
-// densely.
+// With zero_inactive, every (token, channel) of the group that the token skips
+// is also written as +0.0 (an H returned to the caller, or a down projection
+// that cannot skip those copies); otherwise only active pairs are written.
 #include "mfma_core.h"
 
 namespace wide {
@@ -49,7 +49,8 @@ __device__ __forceinline__ void gate_up_body(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ Wu, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, int T, int d, int d_ff, int G, uint16_t* __restrict__ H,
-    int ntok_tiles, int nct, int total, uint8_t* sA, uint8_t* sB, int* s_tok) {
+    int zero_inactive, int ntok_tiles, int nct, int total, uint8_t* sA, uint8_t* sB,
+    int* s_tok) {
   using C = MnShape<CW>;
   using S = typename C::S;
 
@@ -76,7 +77,7 @@ __device__ __forceinline__ void gate_up_body(
   __syncthreads();
 
   // Zeros for the positions of this tile whose token skips the group.
-  {
+  if (zero_inactive) {
     constexpr int kChunks = CW / 8;  // 16-byte chunks per row segment
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int e = nact * kChunks + tid; e < nrows * kChunks; e += 512) {
@@ -187,12 +188,12 @@ __device__ __forceinline__ void gate_up_body(
       const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,                            \
       const uint16_t* __restrict__ Wu, const int32_t* __restrict__ perm,                          \
       const int32_t* __restrict__ counts, int T, int d, int d_ff, int G,                          \
-      uint16_t* __restrict__ H, int ntok_tiles, int nct, int total) {                             \
+      uint16_t* __restrict__ H, int zero_inactive, int ntok_tiles, int nct, int total) {          \
     __shared__ __attribute__((aligned(1024))) uint8_t sA[MnShape<CW>::S::STAGE];                  \
     __shared__ __attribute__((aligned(1024))) uint8_t sB[MnShape<CW>::S::STAGE];                  \
     __shared__ int s_tok[kTokTile];                                                               \
-    gate_up_body<CW>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, ntok_tiles, nct, total, sA, sB,   \
-                     s_tok);                                                                      \
+    gate_up_body<CW>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, ntok_tiles, nct,   \
+                     total, sA, sB, s_tok);                                                       \
   }
 WIDE_GATE_UP_KERNEL(128)
 WIDE_GATE_UP_KERNEL(64)
@@ -203,7 +204,7 @@ WIDE_GATE_UP_KERNEL(16)
 template <int CW>
 hipError_t launch_cw(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu, const int32_t* perm,
                      const int32_t* counts, int T, int d, int d_ff, int G, uint16_t* H,
-                     hipStream_t stream) {
+                     bool zero_inactive, hipStream_t stream) {
   const int ng = d_ff / G;
   const int nct = G / CW;
   const int ntok_tiles = (T + kTokTile - 1) / kTokTile;
@@ -214,7 +215,7 @@ hipError_t launch_cw(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu, 
                 : CW == 32  ? gate_up_bf16_kernel_32
                             : gate_up_bf16_kernel_16;
   hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(512), 0, stream, X, Wg, Wu, perm, counts, T, d,
-                     d_ff, G, H, ntok_tiles, nct, (int)total);
+                     d_ff, G, H, zero_inactive ? 1 : 0, ntok_tiles, nct, (int)total);
   return hipGetLastError();
 }
 
@@ -222,12 +223,15 @@ hipError_t launch_cw(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu, 
 
 hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
-                               int G, uint16_t* H, hipStream_t stream) {
+                               int G, uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (G % 128 == 0) return launch_cw<128>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
-  if (G % 64 == 0) return launch_cw<64>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
-  if (G % 32 == 0) return launch_cw<32>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
-  return launch_cw<16>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, stream);
+  if (G % 128 == 0)
+    return launch_cw<128>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
+  if (G % 64 == 0)
+    return launch_cw<64>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
+  if (G % 32 == 0)
+    return launch_cw<32>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
+  return launch_cw<16>(X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
 }
 
 }  // namespace wide

@@ -102,17 +102,25 @@ struct Frags {
 // different numbers of copies; every wait drains this wave's copies). sA/sB are the two LDS stages. nq is the
 // number of this wave's Q fragments that hold at least one active row (level-2
 // skipping); a wave with nq == 0 still joins every barrier.
-template <class S, class Issue>
+// prepare(s) is called for stage s at least one k-step before issue(s) (for
+// stages >= 2 during the first k-step of stage s-2, while MFMAs run), so
+// per-stage copy offsets can be computed off the critical path.
+template <class S, class Issue, class Prepare>
 __device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, int nst, int wp,
-                                         int wq, int lane, int nq, Issue&& issue) {
+                                         int wq, int lane, int nq, Issue&& issue,
+                                         Prepare&& prepare) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int sw = swz(lrow);  // fragment bases are multiples of 32 rows
   const int pbase = (wp * S::PW + lrow) * kRowBytes;
   const int qbase = (wq * S::QW + lrow) * kRowBytes;
   f.zero();
   if (nst <= 0) return;
+  prepare(0);
   issue(0, sA);
-  if (nst > 1) issue(1, sB);
+  if (nst > 1) {
+    prepare(1);
+    issue(1, sB);
+  }
   __builtin_amdgcn_s_waitcnt(WIDE_VMCNT(0));
   __syncthreads();
   f.load(sA, 0, 0, pbase, qbase, sw, lhalf);
@@ -124,6 +132,7 @@ __device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, 
       const int set = kk & 1;
       if (kk < 3) {
         f.load(cur, kk + 1, set ^ 1, pbase, qbase, sw, lhalf);
+        if (kk == 0 && s + 2 < nst) prepare(s + 2);
         f.mma(set, nq);
       } else {
         // stage s+1 must have landed (each wave waits for its own copies)
@@ -139,6 +148,12 @@ __device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, 
       }
     }
   }
+}
+
+template <class S, class Issue>
+__device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, int nst, int wp,
+                                         int wq, int lane, int nq, Issue&& issue) {
+  mainloop(f, sA, sB, nst, wp, wq, lane, nq, issue, [](int) {});
 }
 
 }  // namespace core

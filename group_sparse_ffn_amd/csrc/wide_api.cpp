@@ -164,9 +164,11 @@ wide_status_t run_stage(wide_stage_t stage, const Args& a) {
       return hip_status(e, "mask reorder launch");
     case WIDE_STAGE_GATE_UP:
       if (a.dt == WIDE_BF16)
+        // zeros at skipped pairs when H is returned, or when the down kernel
+        // cannot skip their copies (too many groups for its LDS mask table)
         e = wide::launch_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
                                       (const uint16_t*)a.Wu, perm, counts, a.T, a.d, a.d_ff, a.G,
-                                      (uint16_t*)H, a.stream);
+                                      (uint16_t*)H, zero_h || ng > wide::kDownMaxGroups, a.stream);
       else
         e = wide::launch_gate_up_f32((const float*)a.X, (const float*)a.Wg, (const float*)a.Wu,
                                      perm, counts, a.T, a.d, a.d_ff, a.G, (float*)H, zero_h,
