@@ -40,6 +40,10 @@ def _load():
         lib.oracle_reorder.restype = ctypes.c_int
         lib.oracle_ffn.argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, i64, p, p]
         lib.oracle_ffn.restype = ctypes.c_int
+        lib.oracle_gemm_mn.argtypes = [p, p, p, i64, i64, i64, i64, p, i64, p]
+        lib.oracle_gemm_mn.restype = ctypes.c_int
+        lib.oracle_gemm_k.argtypes = [p, p, p, i64, i64, i64, i64, p, i64, p]
+        lib.oracle_gemm_k.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -111,3 +115,35 @@ def ffn(X, Wg, Wu, Wd, mask, G: int, rows=None):
     if rc != 0:
         raise ValueError(f"oracle_ffn rejected its arguments (rc={rc})")
     return H, Y
+
+
+def _gemm(fn_name, A, B, mask, G, rows, axis_len):
+    a, b = _as_f32(A), _as_f32(B)
+    m = _as_u8(mask)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape != (N, K):
+        raise ValueError("A must be [M, K] and B [N, K]")
+    if m.shape != (M, axis_len // G):
+        raise ValueError("mask has the wrong shape")
+    if rows is None:
+        r, n = None, M
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = r.shape[0]
+    C = np.empty((n, N), dtype=np.float64)
+    rc = getattr(_load(), fn_name)(_ptr(a), _ptr(b), _ptr(m), M, N, K, G,
+                                   None if r is None else _ptr(r), n, _ptr(C))
+    if rc != 0:
+        raise ValueError(f"{fn_name} rejected its arguments (rc={rc})")
+    return C
+
+
+def gemm_mn(A, B, mask, G: int, rows=None):
+    """N-axis group-masked C = A B^T in fp64: C[m,n] = mask[m, n/G] ? A[m].B[n] : 0."""
+    return _gemm("oracle_gemm_mn", A, B, mask, G, rows, _as_f32(B).shape[0])
+
+
+def gemm_k(A, B, mask, G: int, rows=None):
+    """K-axis group-masked C in fp64: C[m,n] = sum_k mask[m, k/G] A[m,k] B[n,k]."""
+    return _gemm("oracle_gemm_k", A, B, mask, G, rows, _as_f32(A).shape[1])

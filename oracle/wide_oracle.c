@@ -106,6 +106,67 @@ int oracle_ffn(const float* X, const float* Wg, const float* Wu, const float* Wd
   return ORACLE_OK;
 }
 
+/*
+ * Group-masked GEMMs, the two kernel families of the method beyond the FFN
+ * (WIDE paper App. B, "Implementation of GEMM-MN" and "Implementation of
+ * GEMM-K"). C = A B^T with A [M, K], B [N, K] (WIDE paper Sec. 3.2).
+ *
+ *   N axis (GEMM-MN: W_q, W_up, W_gate; M-axis dynamic depth is the case of a
+ *   single group, G == N): the columns of C are cut into groups of G and row m
+ *   keeps or skips each group:
+ *     C[m,n] = A[m,:].B[n,:]   if mask[m, n/G] != 0,   else 0 (select).
+ *   mask is [M, N/G].
+ *
+ *   K axis (GEMM-K: W_o, W_down): the reduction axis is cut into groups of G
+ *   and row m keeps or skips each group of its own input:
+ *     C[m,n] = sum over k with mask[m, k/G] != 0 of A[m,k] * B[n,k].
+ *   mask is [M, K/G].
+ * Products and sums in double; rows m listed in rows[0..nrows) (NULL: 0..nrows-1).
+ */
+int oracle_gemm_mn(const float* A, const float* B, const uint8_t* mask, int64_t M, int64_t N,
+                   int64_t K, int64_t G, const int64_t* rows, int64_t nrows, double* C) {
+  if (!A || !B || !mask || !C || M < 0 || N <= 0 || K <= 0 || G <= 0 || N % G != 0 || nrows < 0)
+    return ORACLE_BAD_ARG;
+  const int64_t ng = N / G;
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t m = rows ? rows[r] : r;
+    if (m < 0 || m >= M) return ORACLE_BAD_ARG;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t m = rows ? rows[r] : r;
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      if (mask[m * ng + n / G] != 0)
+        for (int64_t k = 0; k < K; ++k) acc += (double)A[m * K + k] * (double)B[n * K + k];
+      C[r * N + n] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_gemm_k(const float* A, const float* B, const uint8_t* mask, int64_t M, int64_t N,
+                  int64_t K, int64_t G, const int64_t* rows, int64_t nrows, double* C) {
+  if (!A || !B || !mask || !C || M < 0 || N <= 0 || K <= 0 || G <= 0 || K % G != 0 || nrows < 0)
+    return ORACLE_BAD_ARG;
+  const int64_t ng = K / G;
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t m = rows ? rows[r] : r;
+    if (m < 0 || m >= M) return ORACLE_BAD_ARG;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t m = rows ? rows[r] : r;
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        if (mask[m * ng + k / G] != 0) acc += (double)A[m * K + k] * (double)B[n * K + k];
+      C[r * N + n] = acc;
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -296,3 +296,177 @@ def test_oracle_rejects_bad_arguments():
     p = rand_problem(5, T=2, d=4, d_ff=8, G=4)
     with pytest.raises(ValueError):
         oracle.ffn(p["X"], p["Wg"], p["Wu"], p["Wd"], p["mask"], 4, rows=[0, 2])
+
+
+# ----------------------------------------------------------------------------- masked GEMM pins
+# The N-axis and K-axis group-masked GEMMs (the GEMM-MN and GEMM-K families):
+# C[m,n] = mask[m, n/G] ? A[m].B[n] : 0  and  C[m,n] = sum_k mask[m, k/G] A[m,k] B[n,k].
+
+def gemm_problem(seed, M, N, K, G, axis, density=0.5):
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((N, K)).astype(np.float32)
+    ng = (N if axis == "n" else K) // G
+    mask = (rng.random((M, ng)) < density).astype(np.uint8)
+    return A, B, mask
+
+
+def gemm_fn(axis):
+    return oracle.gemm_mn if axis == "n" else oracle.gemm_k
+
+
+def dense64(A, B):
+    return A.astype(np.float64) @ B.astype(np.float64).T
+
+
+def gpin_dense_limit(fn, axis):
+    A, B, m = gemm_problem(31, 7, 24, 20, 4, axis)
+    return rel(fn(A, B, np.ones_like(m), 4), dense64(A, B)) <= 1e-12
+
+
+def gpin_zero_limit(fn, axis):
+    A, B, m = gemm_problem(32, 5, 16, 12, 4, axis)
+    return bool(np.all(fn(A, B, np.zeros_like(m), 4) == 0.0))
+
+
+def gpin_uniform_mask(fn, axis):
+    """A mask shared by every row equals a dense GEMM on the kept columns (N) or K slices."""
+    G, M, N, K = 4, 6, 20, 24
+    A, B, m = gemm_problem(33, M, N, K, G, axis)
+    S = np.array([0, 2, 3])
+    m = np.zeros_like(m)
+    m[:, S] = 1
+    idx = np.concatenate([np.arange(g * G, (g + 1) * G) for g in S])
+    C = fn(A, B, m, G)
+    if axis == "n":
+        ref = np.zeros((M, N))
+        ref[:, idx] = dense64(A, B[idx])
+    else:
+        ref = dense64(A[:, idx], B[:, idx])
+    return rel(C, ref) <= 1e-12
+
+
+def gpin_additivity(fn, axis):
+    """K axis: the result is the sum of single-group results; N axis: the groups are disjoint."""
+    G, M, N, K = 4, 5, 16, 24
+    A, B, m = gemm_problem(34, M, N, K, G, axis)
+    C = fn(A, B, m, G)
+    acc = np.zeros_like(C)
+    for g in range(m.shape[1]):
+        mg = np.zeros_like(m)
+        mg[:, g] = m[:, g]
+        acc += fn(A, B, mg, G)
+    return rel(C, acc) <= 1e-12
+
+
+def gpin_row_equivariance(fn, axis):
+    A, B, m = gemm_problem(35, 9, 16, 16, 8, axis)
+    C = fn(A, B, m, 8)
+    pi = np.random.default_rng(5).permutation(9)
+    return bool(np.array_equal(fn(A[pi], B, m[pi], 8), C[pi]))
+
+
+def gpin_mpmath(fn, axis):
+    mpmath.mp.dps = 50
+    worst = 0.0
+    for seed, (M, N, K, G) in enumerate([(3, 8, 6, 2), (2, 4, 8, 4), (4, 6, 6, 1)]):
+        A, B, m = gemm_problem(200 + seed, M, N, K, G, axis, density=0.6)
+        C = fn(A, B, m, G)
+        ref = np.zeros((M, N), dtype=object)
+        for i in range(M):
+            for n in range(N):
+                if axis == "n":
+                    keep = m[i, n // G] != 0
+                    ref[i, n] = mpmath.fsum(mpmath.mpf(float(A[i, k])) * mpmath.mpf(float(B[n, k]))
+                                            for k in range(K)) if keep else mpmath.mpf(0)
+                else:
+                    ref[i, n] = mpmath.fsum(mpmath.mpf(float(A[i, k])) * mpmath.mpf(float(B[n, k]))
+                                            for k in range(K) if m[i, k // G])
+        scale = max(float(abs(v)) for v in ref.flat) or 1.0
+        for c, r in zip(C.flat, ref.flat):
+            worst = max(worst, float(abs(mpmath.mpf(float(c)) - r)) / scale)
+    return worst <= 1e-14
+
+
+GEMM_PINS = [gpin_dense_limit, gpin_zero_limit, gpin_uniform_mask, gpin_additivity,
+             gpin_row_equivariance, gpin_mpmath]
+
+
+@pytest.mark.parametrize("axis", ["n", "k"])
+@pytest.mark.parametrize("pin", GEMM_PINS, ids=lambda f: f.__name__)
+def test_oracle_gemm_pins(pin, axis):
+    assert pin(gemm_fn(axis), axis)
+
+
+def test_oracle_gemm_single_group_is_row_skipping():
+    """M-axis (dynamic depth) is the N-axis case with one group: rows are dense or zero."""
+    A, B, _ = gemm_problem(36, 6, 12, 10, 12, "n")
+    m = np.array([[1], [0], [1], [1], [0], [0]], dtype=np.uint8)
+    C = oracle.gemm_mn(A, B, m, 12)
+    D = dense64(A, B)
+    assert np.array_equal(C[m[:, 0] == 0], np.zeros((3, 12)))
+    assert rel(C[m[:, 0] != 0], D[m[:, 0] != 0]) <= 1e-12
+
+
+def test_oracle_ffn_is_the_composition_of_the_masked_gemms():
+    """The FFN oracle equals GEMM-K(silu(GEMM-MN(X, Wg)) * GEMM-MN(X, Wu), Wd) with one mask."""
+    G = 4
+    p = rand_problem(41, T=6, d=12, d_ff=16, G=G)
+    a = oracle.gemm_mn(p["X"], p["Wg"], p["mask"], G)
+    b = oracle.gemm_mn(p["X"], p["Wu"], p["mask"], G)
+    H = silu64(a) * b  # zero wherever the group is masked
+    Hf = H.astype(np.float32)  # the GEMM oracle takes float32 operands
+    Y = oracle.gemm_k(Hf, p["Wd"], p["mask"], G)
+    Href, Yref = oracle.ffn(p["X"], p["Wg"], p["Wu"], p["Wd"], p["mask"], G)
+    assert rel(H, Href) <= 1e-12
+    assert rel(Y, Yref) <= 1e-6  # float32 rounding of H
+
+
+def _np_gemm(A, B, mask, G, axis, bug=None):
+    A, B = A.astype(np.float64), B.astype(np.float64)
+    M, K = A.shape
+    N = B.shape[0]
+    L = N if axis == "n" else K
+    gidx = (np.arange(L) % (L // G)) if bug == "interleaved_groups" else (np.arange(L) // G)
+    m = mask
+    if bug == "mask_ignored":
+        m = np.ones_like(mask)
+    if bug == "row_shift":
+        m = np.roll(mask, 1, axis=0)
+    keep = m[:, gidx] != 0
+    if axis == "n":
+        C = np.where(keep, A @ B.T, 0.0)
+        if bug == "mask_on_k":
+            C = A @ B.T
+    else:
+        C = np.where(keep, A, 0.0) @ B.T
+        if bug == "mask_on_n":
+            C = np.where(keep[:, :N] if keep.shape[1] >= N else 1.0, A @ B.T, 0.0)
+    if bug == "transposed_b":
+        C = C.T[:M, :N] if C.shape[0] >= N else C[:, ::-1]
+    return C
+
+
+GEMM_MUTANTS = [(axis, bug) for axis in ("n", "k")
+                for bug in ("interleaved_groups", "mask_ignored", "row_shift", "transposed_b")]
+GEMM_MUTANTS += [("n", "mask_on_k"), ("k", "mask_on_n")]
+
+
+@pytest.mark.parametrize("axis", ["n", "k"])
+def test_gemm_pins_pass_on_correct_numpy_variant(axis):
+    fn = lambda A, B, m, G: _np_gemm(A, B, m, G, axis)  # noqa: E731
+    assert all(pin(fn, axis) for pin in GEMM_PINS if pin is not gpin_mpmath)
+
+
+@pytest.mark.parametrize("axis,bug", GEMM_MUTANTS)
+def test_gemm_pins_catch_planted_mistake(axis, bug):
+    fn = lambda A, B, m, G: _np_gemm(A, B, m, G, axis, bug=bug)  # noqa: E731
+    results = {}
+    for pin in GEMM_PINS:
+        if pin is gpin_mpmath:
+            continue
+        try:
+            results[pin.__name__] = pin(fn, axis)
+        except (ValueError, IndexError):
+            results[pin.__name__] = False
+    assert not all(results.values()), f"no pin caught '{bug}' on axis {axis}: {results}"
