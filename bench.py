@@ -189,6 +189,44 @@ def dense_baseline(torch, d, steps: int, warmup: int):
     return ms
 
 
+def bench_masked_gemms(torch, wide, dg, steps: int):
+    """The N-axis and K-axis masked GEMMs at Llama3.1-8B attention shapes.
+
+    Times one library call (mask reorder or bit packing + the GEMM kernel) and
+    torch's dense bf16 A @ B^T on the same operands.
+    """
+    out = {}
+    dev = "cuda:0"
+    for w in (dg.LLAMA8B_ATTN_Q, dg.LLAMA8B_ATTN_O, dg.LLAMA8B_DEPTH):
+        log(f"masked GEMM {w.name}")
+        inp = dg.make_gemm_inputs(w)
+        act = int(inp["mask"].sum())
+        d = {k: v.to(dev) for k, v in inp.items()}
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(wide.gemm_workspace_size(w.M, w.ngroups), dtype=torch.uint8, device=dev)
+        fn = wide.gemm_mn if w.axis == "mn" else wide.gemm_k
+        call = lambda: fn(d["A"], d["B"], d["mask"], w.G, C=C, workspace=ws)
+        for _ in range(3):
+            call()
+        ms = time_events(torch, call, steps)
+        Bt = d["B"]
+        dense = lambda: d["A"] @ Bt.t()
+        for _ in range(3):
+            dense()
+        dms = time_events(torch, dense, steps)
+        # active flops: 2 * (the unpruned extent) * G per active (row, group)
+        other = w.K if w.axis == "mn" else w.N
+        flops = 2.0 * other * w.G * act
+        out[w.name] = {"M": w.M, "N": w.N, "K": w.K, "G": w.G, "axis": w.axis,
+                       "density": round(act / (w.M * w.ngroups), 4), "ms": round(ms, 4),
+                       "active_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                       "dense_ms": round(dms, 4), "speedup_vs_dense": round(dms / ms, 3),
+                       "ideal_speedup": round(w.M * w.ngroups / max(act, 1), 3)}
+        del d, C, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
     """fp64 oracle on a seeded token sample, scaled to effective TFLOP/s."""
     import numpy as np
@@ -388,6 +426,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--command", default="")
@@ -458,6 +497,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = bench_decode(torch, wide, dg, args.steps)
+    if not args.no_gemm:
+        line["masked_gemms"] = bench_masked_gemms(torch, wide, dg, args.steps)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         import oracle

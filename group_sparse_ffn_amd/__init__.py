@@ -18,6 +18,7 @@ from ._lib import (WIDE_BF16, WIDE_DECODE_T_LIMIT, WIDE_F32, WIDE_FLAG_FORCE_DEC
                    WideError)
 
 __all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decode_max_t",
+           "gemm_mn", "gemm_k", "gemm_workspace_size",
            "FfnCall", "WideError", "WIDE_TOKEN_TILE", "WIDE_DECODE_T_LIMIT",
            "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
            "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
@@ -122,3 +123,49 @@ def ffn_forward(X, Wg, Wu, Wd, mask, G: int, return_h: bool = False, flags: int 
 
 def ffn_stage(stage: int, call: FfnCall) -> None:
     call.stage(stage)
+
+
+# ---------------------------------------------------------------- masked GEMMs
+
+
+def gemm_workspace_size(M: int, ngroups: int) -> int:
+    return int(_lib.load().wide_gemm_workspace_size(M, ngroups))
+
+
+def _gemm(fn_name: str, A, B, mask, G: int, routed_axis: str, C=None, workspace=None):
+    for name, t in (("A", A), ("B", B), ("mask", mask)):
+        _need_cuda(name, t)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    if mask.dtype != torch.uint8:
+        raise ValueError("mask must be uint8")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape != (N, K):
+        raise ValueError("expected A [M, K] and B [N, K]")
+    routed = N if routed_axis == "n" else K
+    if routed % G != 0 or mask.shape != (M, routed // G):
+        raise ValueError(f"mask must be [M, {routed_axis.upper()} // G] with G dividing "
+                         f"{routed_axis.upper()}")
+    dev = A.device
+    if C is None:
+        C = torch.empty((M, N), dtype=A.dtype, device=dev)
+    _need_cuda("C", C)
+    nbytes = gemm_workspace_size(M, routed // G)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    fn = getattr(_lib.load(), fn_name)
+    _lib.check(fn(A.data_ptr(), B.data_ptr(), mask.data_ptr(), M, N, K, G, WIDE_BF16, C.data_ptr(),
+                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                  _stream_ptr(dev)))
+    return C
+
+
+def gemm_mn(A, B, mask, G: int, C=None, workspace=None):
+    """N-axis masked GEMM: C[m, n] = A[m] . B[n] if mask[m, n // G] else 0 (bf16)."""
+    return _gemm("wide_gemm_mn", A, B, mask, G, "n", C, workspace)
+
+
+def gemm_k(A, B, mask, G: int, C=None, workspace=None):
+    """K-axis masked GEMM: C[m, n] = sum over active groups g of A[m, g] . B[n, g] (bf16)."""
+    return _gemm("wide_gemm_k", A, B, mask, G, "k", C, workspace)

@@ -41,11 +41,15 @@ _i32 = ctypes.c_int32
 _u32 = ctypes.c_uint32
 _sz = ctypes.c_size_t
 _FFN_ARGS = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p, _p, _sz, _u32, _p]
+_GEMM_ARGS = [_p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p, _sz, _p]
 SIGNATURES = {
     "wide_reorder_masks": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "wide_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int]),
     "wide_ffn_forward": (ctypes.c_int, _FFN_ARGS),
     "wide_ffn_stage": (ctypes.c_int, [ctypes.c_int] + _FFN_ARGS),
+    "wide_gemm_workspace_size": (_sz, [_i32, _i32]),
+    "wide_gemm_mn": (ctypes.c_int, _GEMM_ARGS),
+    "wide_gemm_k": (ctypes.c_int, _GEMM_ARGS),
     "wide_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "wide_last_error": (ctypes.c_char_p, []),
     "wide_decode_max_t": (_i32, []),

@@ -58,8 +58,12 @@ hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t*
                           int32_t* counts, int32_t* padded, uint32_t* maskbits,
                           hipStream_t stream);
 
+// Packed mask bits alone: maskbits[g, w] bit b = mask[32w + b, g] != 0.
+hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* maskbits,
+                                 hipStream_t stream);
+
 // Largest group count for which the bf16 down kernel keeps the token tile's
-// mask bits in LDS and skips the H copies of inactive (token, group) pairs.
+// mask bits in an LDS table (beyond it, it reads them from global memory).
 constexpr int kDownMaxGroups = 768;
 
 // bf16 prefill gate/up over the reordered tokens (tile = 256 tokens). Writes
@@ -69,9 +73,15 @@ hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint
                                const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
                                int G, uint16_t* H, bool zero_inactive, hipStream_t stream);
 
-// bf16 prefill down projection (output-stationary; K-blocks inactive for a
-// whole token tile are skipped; with d_ff / G <= kDownMaxGroups the H copies of
-// inactive (token, group) pairs are skipped too, else H must hold +0.0 there).
+// bf16 N-axis masked GEMM over reordered rows: C[m, n] = A[m] . B[n] where
+// row m takes group n / G, else +0.0 (every element of C is written).
+hipError_t launch_gemm_mn_bf16(const uint16_t* A, const uint16_t* B, const int32_t* perm,
+                               const int32_t* counts, int M, int K, int N, int G, uint16_t* C,
+                               hipStream_t stream);
+
+// bf16 prefill down projection, also the K-axis masked GEMM (output-stationary;
+// K-blocks inactive for a whole token tile are skipped and the H copies of
+// inactive (token, group) pairs read zeros, so H's values there never matter).
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
                             int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
 

@@ -19,9 +19,10 @@
 //     memory (level-1 skipping of A packets): inactive pairs contribute
 //     exactly 0 whatever H holds there, and cost no HBM traffic. The tile's
 //     mask bits (256 tokens x ngroups) sit in an LDS table built once per
-//     workgroup; with more than kDownMaxGroups groups the table does not fit,
-//     the copies are not predicated, and the gate/up kernel writes +0.0 at
-//     every skipped (token, channel) instead.
+//     workgroup; with more than kDownMaxGroups groups the table does not fit
+//     and each lane reads its mask words from global memory instead, one
+//     stage ahead, so the stage's own wait covers those loads too.
+// The same kernel is the K-axis masked GEMM C = (mask-expanded A) . B^T.
 // Operands: MFMA A side = Wdown rows (output columns), B side = H rows
 // (tokens); the shared 8-wave mainloop streams both through LDS with
 // register-bypassing copies. Rows past d or T are zero-filled by
@@ -126,16 +127,36 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
   // pairs turned into out-of-range offsets; computed by prepare() while the
   // MFMAs of an earlier stage run.
   uint32_t vq_next[4];
-  auto prepare = [&](int s) {
+  // Without the LDS table: this lane's 4 mask words (tile rows rw, rw + 64,
+  // rw + 128, rw + 192) for the next stage to prepare, loaded by
+  // the prepare() of the stage before (or before the mainloop for stage 0).
+  uint32_t mw0 = 0u, mw1 = 0u, mw2 = 0u, mw3 = 0u;
+  auto fetch = [&](int s) {
     const int k0 = (int)s_steps[s] * 64;
-    const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * 8;  // this lane's group
+    const uint32_t* mw = maskbits + (size_t)((k0 + chunk * 8) / G) * words;
+    const int wi = w0 + (rw >> 5);
+    mw0 = wi < words ? mw[wi] : 0u;
+    mw1 = wi + 2 < words ? mw[wi + 2] : 0u;
+    mw2 = wi + 4 < words ? mw[wi + 4] : 0u;
+    mw3 = wi + 6 < words ? mw[wi + 6] : 0u;
+  };
+  auto prepare = [&](int s) {
+    if (table) {
+      const int k0 = (int)s_steps[s] * 64;
+      const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * 8;  // this lane's group
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t vq = voff_q[i];
-      if (table && !((mw[2 * i + (rw >> 5)] >> (rw & 31)) & 1u)) vq = 0x80000000u;
-      vq_next[i] = vq;
+      for (int i = 0; i < 4; ++i)
+        vq_next[i] = ((mw[2 * i + (rw >> 5)] >> (rw & 31)) & 1u) ? voff_q[i] : 0x80000000u;
+    } else {
+      const uint32_t sh = rw & 31;
+      vq_next[0] = ((mw0 >> sh) & 1u) ? voff_q[0] : 0x80000000u;
+      vq_next[1] = ((mw1 >> sh) & 1u) ? voff_q[1] : 0x80000000u;
+      vq_next[2] = ((mw2 >> sh) & 1u) ? voff_q[2] : 0x80000000u;
+      vq_next[3] = ((mw3 >> sh) & 1u) ? voff_q[3] : 0x80000000u;
+      if (s + 1 < nst) fetch(s + 1);
     }
   };
+  if (!table && nst > 0) fetch(0);
   auto issue = [&](int s, uint8_t* stage) {
     const int k0 = (int)s_steps[s] * 64;
     const __amdgpu_buffer_rsrc_t wr =

@@ -105,7 +105,34 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const uint8_t* __rest
   }
 }
 
+// Packed mask bits alone (the K-axis GEMM needs no row lists): thread (w, g)
+// gathers bit b of word w of group g from mask[32w + b, g]; consecutive lanes
+// take consecutive groups, so each of the 32 byte reads is coalesced.
+__global__ __launch_bounds__(256) void pack_mask_bits_kernel(const uint8_t* __restrict__ mask,
+                                                             int T, int ng, int words,
+                                                             uint32_t* __restrict__ maskbits) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)ng * words) return;
+  const int g = (int)(idx % ng);
+  const int w = (int)(idx / ng);
+  const int t0 = 32 * w;
+  const int n = min(32, T - t0);
+  uint32_t bits = 0;
+  for (int b = 0; b < n; ++b) bits |= (mask[(size_t)(t0 + b) * ng + g] != 0 ? 1u : 0u) << b;
+  maskbits[(size_t)g * words + w] = bits;
+}
+
 }  // namespace
+
+hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* maskbits,
+                                 hipStream_t stream) {
+  const int words = (T + 31) / 32;
+  const long long n = (long long)ng * words;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_mask_bits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     mask, T, ng, words, maskbits);
+  return hipGetLastError();
+}
 
 hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t* perm,
                           int32_t* counts, int32_t* padded, uint32_t* maskbits,

@@ -164,11 +164,11 @@ wide_status_t run_stage(wide_stage_t stage, const Args& a) {
       return hip_status(e, "mask reorder launch");
     case WIDE_STAGE_GATE_UP:
       if (a.dt == WIDE_BF16)
-        // zeros at skipped pairs when H is returned, or when the down kernel
-        // cannot skip their copies (too many groups for its LDS mask table)
+        // zeros at skipped pairs only when H is returned: the down kernel
+        // never reads H at an inactive (token, group)
         e = wide::launch_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
                                       (const uint16_t*)a.Wu, perm, counts, a.T, a.d, a.d_ff, a.G,
-                                      (uint16_t*)H, zero_h || ng > wide::kDownMaxGroups, a.stream);
+                                      (uint16_t*)H, zero_h, a.stream);
       else
         e = wide::launch_gate_up_f32((const float*)a.X, (const float*)a.Wg, (const float*)a.Wu,
                                      perm, counts, a.T, a.d, a.d_ff, a.G, (float*)H, zero_h,
@@ -262,6 +262,112 @@ WIDE_API wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const v
   if (T == 0) return ok();
   st = run_stage(stage, a);
   if (st != WIDE_OK) return st;
+  return ok();
+}
+
+// ---------------------------------------------------------------- masked GEMMs
+
+namespace {
+
+// Workspace of the masked GEMMs (each region 256-byte aligned):
+//   perm     int32  [ngroups, M]   (N axis)
+//   counts   int32  [ngroups]      (N axis)
+//   padded   int32  [ngroups]      (N axis)
+//   maskbits uint32 [ngroups, ceil(M/32)]   (K axis)
+struct GemmLayout {
+  size_t perm, counts, padded, maskbits, total;
+};
+
+GemmLayout gemm_layout(int64_t M, int64_t ng) {
+  GemmLayout L{};
+  size_t off = 0;
+  L.perm = off;
+  off = round_up(off + (size_t)(ng * M) * 4, 256);
+  L.counts = off;
+  off = round_up(off + (size_t)ng * 4, 256);
+  L.padded = off;
+  off = round_up(off + (size_t)ng * 4, 256);
+  L.maskbits = off;
+  off = round_up(off + (size_t)(ng * ((M + 31) / 32)) * 4, 256);
+  L.total = off;
+  return L;
+}
+
+// routed = N (N axis) or K (K axis).
+wide_status_t validate_gemm(const void* A, const void* B, const uint8_t* mask, int32_t M, int32_t N,
+                            int32_t K, int32_t G, int32_t routed, wide_dtype_t dt, const void* C,
+                            const void* ws, size_t ws_bytes) {
+  if (!B) return fail(WIDE_ERR_NULL, "B must be non-NULL");
+  if (M != 0 && (!A || !mask || !C))
+    return fail(WIDE_ERR_NULL, "A, mask and C must be non-NULL when M > 0");
+  if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (M < 0 || N <= 0 || K <= 0 || G <= 0)
+    return fail(WIDE_ERR_SHAPE, "need M >= 0 and N, K, G >= 1 (M=%d N=%d K=%d G=%d)", M, N, K, G);
+  if (routed % G != 0)
+    return fail(WIDE_ERR_SHAPE, "the routed axis (%d) is not a multiple of G=%d", routed, G);
+  if (dt != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the masked GEMMs run bf16 only");
+  if (K % 64 != 0 || G % 16 != 0 || N % 8 != 0)
+    return fail(WIDE_ERR_UNSUPPORTED, "kernels need K %% 64 == 0, G %% 16 == 0, N %% 8 == 0 (N=%d K=%d G=%d)",
+                N, K, G);
+  if (K > 65536) return fail(WIDE_ERR_UNSUPPORTED, "kernels need K <= 65536 (K=%d)", K);
+  if ((int64_t)M * K >= (1ll << 30) || (int64_t)N * K >= (1ll << 30) || (int64_t)M * N >= (1ll << 30))
+    return fail(WIDE_ERR_UNSUPPORTED, "M*K, N*K and M*N must stay below 2^30");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C))
+    return fail(WIDE_ERR_ALIGN, "A, B and C must be 16-byte aligned");
+  const GemmLayout L = gemm_layout(M, routed / G);
+  if (!ws) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  return WIDE_OK;
+}
+
+}  // namespace
+
+WIDE_API size_t wide_gemm_workspace_size(int32_t M, int32_t ngroups) {
+  if (M < 0 || ngroups < 1) return 0;
+  return gemm_layout(M, ngroups).total;
+}
+
+WIDE_API wide_status_t wide_gemm_mn(const void* A, const void* B, const uint8_t* mask, int32_t M,
+                                    int32_t N, int32_t K, int32_t G, wide_dtype_t dtype, void* C,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  wide_status_t st =
+      validate_gemm(A, B, mask, M, N, K, G, N, dtype, C, workspace, workspace_bytes);
+  if (st != WIDE_OK) return st;
+  if (M == 0) return ok();
+  const int ng = N / G;
+  const GemmLayout L = gemm_layout(M, ng);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = wide::launch_reorder(mask, M, ng, WIDE_TOKEN_TILE, perm, counts, padded, nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "mask reorder launch");
+  e = wide::launch_gemm_mn_bf16((const uint16_t*)A, (const uint16_t*)B, perm, counts, M, K, N, G,
+                                (uint16_t*)C, s);
+  if (e != hipSuccess) return hip_status(e, "GEMM-MN launch");
+  return ok();
+}
+
+WIDE_API wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* mask, int32_t M,
+                                   int32_t N, int32_t K, int32_t G, wide_dtype_t dtype, void* C,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  wide_status_t st =
+      validate_gemm(A, B, mask, M, N, K, G, K, dtype, C, workspace, workspace_bytes);
+  if (st != WIDE_OK) return st;
+  if (M == 0) return ok();
+  const int ng = K / G;
+  const GemmLayout L = gemm_layout(M, ng);
+  uint32_t* maskbits = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.maskbits);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = wide::launch_pack_mask_bits(mask, M, ng, maskbits, s);
+  if (e != hipSuccess) return hip_status(e, "mask pack launch");
+  e = wide::launch_down_bf16((const uint16_t*)A, (const uint16_t*)B, maskbits, M, N, K, G,
+                             (uint16_t*)C, s);
+  if (e != hipSuccess) return hip_status(e, "GEMM-K launch");
   return ok();
 }
 

@@ -211,3 +211,73 @@ def random_small(seed: int, T: int, d: int, d_ff: int, G: int, dtype: str = "f32
         "Wd": to_dtype(normal_f32(seed + 3, (d, d_ff), wscale), dtype),
         "mask": torch.from_numpy(mask_bernoulli(T, ng, density, seed + 4)),
     }
+
+
+# ---------------------------------------------------------------- masked GEMMs
+
+@dataclasses.dataclass(frozen=True)
+class GemmWorkload:
+    """One group-masked GEMM C = A B^T (A [M, K], B [N, K]) routed on `axis`.
+
+    axis "mn": the mask [M, N/G] routes output columns (an attention W_q
+    projection; with G = N, one group, the M-axis / dynamic-depth case);
+    axis "k": the mask [M, K/G] routes the reduction (an attention W_o
+    projection). Recipe: A ~ N(0,1) with seed s, B ~ 0.02 N(0,1) with seed
+    s + 1, mask with seed s + 4, s = 1000 * wid; bf16 rounded once.
+    """
+    name: str
+    wid: int
+    M: int
+    N: int
+    K: int
+    G: int
+    axis: str                # "mn" or "k"
+    mask_kind: str           # as for Workload
+    density: float = 0.5
+
+    @property
+    def ngroups(self) -> int:
+        return (self.N if self.axis == "mn" else self.K) // self.G
+
+    @property
+    def seed(self) -> int:
+        return 1000 * self.wid
+
+
+# Llama3.1-8B attention projections at the prefill length: 32 query heads of
+# 128 channels in 8 GQA groups, so one routed group = 4 heads = 512 channels.
+LLAMA8B_ATTN_Q = GemmWorkload("llama3.1-8b-attn-wq-prefill", 6, M=16384, N=4096, K=4096, G=512,
+                              axis="mn", mask_kind="topk")
+LLAMA8B_ATTN_O = GemmWorkload("llama3.1-8b-attn-wo-prefill", 7, M=16384, N=4096, K=4096, G=512,
+                              axis="k", mask_kind="topk")
+# Dynamic depth: one group spanning all N outputs, a token keeps or skips the layer.
+LLAMA8B_DEPTH = GemmWorkload("llama3.1-8b-depth-wq-prefill", 8, M=16384, N=4096, K=4096, G=4096,
+                             axis="mn", mask_kind="bernoulli")
+
+
+def make_gemm_mask(w: GemmWorkload, kind: Optional[str] = None, M: Optional[int] = None):
+    kind = kind or w.mask_kind
+    M = w.M if M is None else M
+    ng = w.ngroups
+    seed = w.seed + 4
+    if kind == "bernoulli":
+        return mask_bernoulli(M, ng, w.density, seed)
+    if kind == "topk":
+        return mask_topk(M, ng, int(round(ng * w.density)), seed)
+    if kind == "beta":
+        return mask_beta(M, ng, w.density, seed)
+    if kind == "ones":
+        return np.ones((M, ng), dtype=np.uint8)
+    if kind == "zeros":
+        return np.zeros((M, ng), dtype=np.uint8)
+    raise ValueError(kind)
+
+
+def make_gemm_inputs(w: GemmWorkload, M: Optional[int] = None,
+                     mask_kind: Optional[str] = None) -> dict:
+    """A [M, K], B [N, K] bf16 and mask uint8 as CPU tensors."""
+    M = w.M if M is None else M
+    s = w.seed
+    return {"A": to_dtype(normal_f32(s, (M, w.K)), "bf16"),
+            "B": to_dtype(normal_f32(s + 1, (w.N, w.K), 0.02), "bf16"),
+            "mask": torch.from_numpy(make_gemm_mask(w, mask_kind, M))}

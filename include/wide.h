@@ -118,11 +118,13 @@ size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G, wi
  * Prefill path (T > wide_decode_max_t(), or WIDE_FLAG_FORCE_PREFILL): mask
  * reorder, then the gate/up kernel over each group's active prefix (tiles past
  * the prefix do no MFMA work, rows past it are not fetched, fragments past it
- * are not multiplied; SiLU(gate)*up fused in the epilogue and scattered to H,
- * with +0.0 written for every skipped (token, group)), then the down kernel,
- * which owns each [token tile x output tile] of Y, accumulates over the
- * channels in registers and skips every 64-channel K-block whose groups are
- * inactive for the whole token tile (WIDE paper App. B, GEMM-MN and GEMM-K).
+ * are not multiplied; SiLU(gate)*up fused in the epilogue and scattered to H
+ * for the active (token, group) pairs only, plus +0.0 at the others when
+ * H_out is given), then the down kernel, which owns each [token tile x output
+ * tile] of Y, accumulates over the channels in registers, skips every
+ * 64-channel K-block whose groups are inactive for the whole token tile and
+ * never reads H at an inactive (token, group) (WIDE paper App. B, GEMM-MN
+ * and GEMM-K).
  * Decode path (bf16, T <= wide_decode_max_t()): no reorder (WIDE paper App. B:
  * the T_q = 1 case checks routing directly); a gate/up GEMV and a down GEMV
  * that stream only the weight rows/segments of groups active for some token.
@@ -162,6 +164,56 @@ wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const void* Wgat
                              const void* Wdown, const uint8_t* mask, int32_t T, int32_t d,
                              int32_t d_ff, int32_t G, wide_dtype_t dtype, void* Y, void* H_out,
                              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * The two group-masked GEMM families the FFN kernels are built from, exposed
+ * on their own (WIDE paper App. B, "Implementation of GEMM-MN" and
+ * "Implementation of GEMM-K"). C = A B^T with A [M, K] and B [N, K]; a mask
+ * uint8 [M, ngroups] (nonzero = active) routes each row of A over groups of G
+ * consecutive indices of one axis:
+ *
+ *   wide_gemm_mn (N axis; ngroups = N / G):
+ *     C[m,n] = A[m,:] . B[n,:]   if mask[m, n / G] != 0,   else C[m,n] = +0.0
+ *     The N-axis path covers an attention W_q projection (groups of query
+ *     heads) and the FFN gate/up; with G = N (ngroups = 1) it is the M-axis
+ *     case, dynamic depth: a row with mask 0 gets an all-zero output row.
+ *   wide_gemm_k (K axis; ngroups = K / G):
+ *     C[m,n] = sum_k [mask[m, k / G] != 0] A[m,k] B[n,k]
+ *     The K-axis path covers an attention W_o projection (groups of heads in
+ *     its input) and the FFN down projection. A's values at inactive
+ *     (row, group) pairs are never read: they may hold anything, NaN included.
+ *
+ * Both run bf16 operands with fp32 accumulation over the full K range in a
+ * fixed order (one writer per output, no atomics) and round C once (RNE).
+ * wide_gemm_mn reorders the mask columns on the device (as
+ * wide_reorder_masks) and runs one workgroup per (G-aligned channel block,
+ * 256-row tile of the group's active prefix); wide_gemm_k packs the mask into
+ * bits on the device and runs one workgroup per 256 x 256 output tile,
+ * skipping every 64-wide K-block inactive for all its rows.
+ *
+ *   A        [M, K]  device, bf16, read only.
+ *   B        [N, K]  device, bf16, read only ([out, in], as nn.Linear).
+ *   mask     [M, ngroups] device, uint8, read only.
+ *   C        [M, N]  device, bf16, written in full (every element).
+ *   workspace        device, >= wide_gemm_workspace_size(M, ngroups) bytes,
+ *                    256-byte aligned; contents on entry are ignored.
+ *   dtype            WIDE_BF16 (WIDE_F32 returns WIDE_ERR_UNSUPPORTED).
+ * Sizes: M >= 0 (M == 0 enqueues nothing; A, mask and C may then be NULL),
+ * N, K, G >= 1, G divides the routed axis (N for wide_gemm_mn, K for
+ * wide_gemm_k). The kernels also need K % 64 == 0, G % 16 == 0, N % 8 == 0,
+ * K <= 65536 and M*K, N*K, M*N < 2^30, else WIDE_ERR_UNSUPPORTED.
+ * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_DTYPE, WIDE_ERR_ALIGN,
+ * WIDE_ERR_WORKSPACE, WIDE_ERR_UNSUPPORTED, WIDE_ERR_HIP.
+ */
+size_t wide_gemm_workspace_size(int32_t M, int32_t ngroups);
+
+wide_status_t wide_gemm_mn(const void* A, const void* B, const uint8_t* mask, int32_t M, int32_t N,
+                           int32_t K, int32_t G, wide_dtype_t dtype, void* C, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* mask, int32_t M, int32_t N,
+                          int32_t K, int32_t G, wide_dtype_t dtype, void* C, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* wide_status_string(wide_status_t status);

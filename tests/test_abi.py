@@ -130,3 +130,64 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.load()
+
+
+def gemm_call(lib, fn, **kw):
+    a = dict(A=FAKE, B=FAKE, mask=FAKE, M=300, N=512, K=256, G=64, dtype=_lib.WIDE_BF16, C=FAKE,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return getattr(lib, fn)(a["A"], a["B"], a["mask"], a["M"], a["N"], a["K"], a["G"], a["dtype"],
+                            a["C"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+GEMM_BAD = [
+    (dict(A=None), _lib.WIDE_ERR_NULL),
+    (dict(B=None, M=0), _lib.WIDE_ERR_NULL),
+    (dict(mask=None), _lib.WIDE_ERR_NULL),
+    (dict(C=None), _lib.WIDE_ERR_NULL),
+    (dict(dtype=9), _lib.WIDE_ERR_DTYPE),
+    (dict(dtype=_lib.WIDE_F32), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(M=-1), _lib.WIDE_ERR_SHAPE),
+    (dict(N=0), _lib.WIDE_ERR_SHAPE),
+    (dict(K=0), _lib.WIDE_ERR_SHAPE),
+    (dict(G=0), _lib.WIDE_ERR_SHAPE),
+    (dict(K=96, N=96, G=32), _lib.WIDE_ERR_UNSUPPORTED),        # K % 64
+    (dict(N=520, K=520, G=40), _lib.WIDE_ERR_UNSUPPORTED),      # K % 64 and G % 16
+    (dict(N=1 << 17, K=1 << 17, G=1 << 10), _lib.WIDE_ERR_UNSUPPORTED),  # K > 65536
+    (dict(M=1 << 20, N=2048, K=2048, G=128), _lib.WIDE_ERR_UNSUPPORTED),  # M*K >= 2^30
+    (dict(A=FAKE + 8), _lib.WIDE_ERR_ALIGN),
+    (dict(C=FAKE + 2), _lib.WIDE_ERR_ALIGN),
+    (dict(ws=FAKE + 64), _lib.WIDE_ERR_ALIGN),
+    (dict(ws=None), _lib.WIDE_ERR_WORKSPACE),
+    (dict(ws_bytes=256), _lib.WIDE_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,status", GEMM_BAD + [(dict(N=500, G=64), _lib.WIDE_ERR_SHAPE)])
+def test_gemm_mn_validation(lib, kw, status):
+    assert gemm_call(lib, "wide_gemm_mn", **kw) == status
+    assert lib.wide_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", GEMM_BAD + [
+    (dict(K=320, G=128), _lib.WIDE_ERR_SHAPE),                  # G does not divide K
+    (dict(N=500), _lib.WIDE_ERR_UNSUPPORTED),                   # N % 8
+])
+def test_gemm_k_validation(lib, kw, status):
+    assert gemm_call(lib, "wide_gemm_k", **kw) == status
+    assert lib.wide_last_error().decode() != ""
+
+
+def test_gemm_m0_is_a_no_op(lib):
+    for fn in ("wide_gemm_mn", "wide_gemm_k"):
+        assert gemm_call(lib, fn, M=0, A=None, mask=None, C=None) == _lib.WIDE_OK
+        assert lib.wide_last_error().decode() == ""
+
+
+def test_gemm_workspace_size(lib):
+    M, ng = 16384, 8
+    ws = lib.wide_gemm_workspace_size(M, ng)
+    need = ng * M * 4 + 2 * ng * 4 + ng * (M // 32) * 4
+    assert need <= ws <= need + 4 * 256
+    assert lib.wide_gemm_workspace_size(-1, 8) == 0
+    assert lib.wide_gemm_workspace_size(16, 0) == 0
