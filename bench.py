@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
     "reorder": ["reorder.hip", "common.h"],
     "decode_gate_up": ["decode.hip", "common.h"],
     "decode_down": ["decode.hip", "common.h"],
+    "gemm_mn": ["gemm_mn.hip", "mfma_core.h", "common.h"],
+    "pack_mask_bits": ["reorder.hip", "common.h"],
 }
 # substrings of the device symbol names of each kernel
 KERNEL_SYMBOLS = {
@@ -61,6 +63,8 @@ KERNEL_SYMBOLS = {
     "reorder": "reorder_kernel",
     "decode_gate_up": "decode_gate_up_kernel",
     "decode_down": "decode_down_kernel",
+    "gemm_mn": "gemm_mn_bf16_kernel",
+    "pack_mask_bits": "pack_mask_bits_kernel",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read + 1 GiB written
 
@@ -220,6 +224,7 @@ def bench_masked_gemms(torch, wide, dg, steps: int):
         out[w.name] = {"M": w.M, "N": w.N, "K": w.K, "G": w.G, "axis": w.axis,
                        "density": round(act / (w.M * w.ngroups), 4), "ms": round(ms, 4),
                        "active_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                       "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                        "dense_ms": round(dms, 4), "speedup_vs_dense": round(dms / ms, 3),
                        "ideal_speedup": round(w.M * w.ngroups / max(act, 1), 3)}
         del d, C, ws
@@ -327,41 +332,112 @@ def run_profile(steps: int):
         torch.cuda.synchronize()
         del calls, ws
         torch.cuda.empty_cache()
+    for w in PROFILE_GEMMS(dg):
+        inp = {k: v.to("cuda:0") for k, v in dg.make_gemm_inputs(w).items()}
+        fn = wide.gemm_mn if w.axis == "mn" else wide.gemm_k
+        for _ in range(PROFILE_GEMM_CALLS):
+            fn(inp["A"], inp["B"], inp["mask"], w.G)
+        torch.cuda.synchronize()
+        del inp
+        torch.cuda.empty_cache()
     src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"profile run done: {steps} prefill steps, 16 decode steps per T, one {COPY_BYTES} B copy")
+    log(f"profile run done: {steps} prefill steps, 16 decode steps per T, "
+        f"{PROFILE_GEMM_CALLS} calls per masked GEMM, one {COPY_BYTES} B copy")
 
 
-def summarize(directory: str, command: str):
-    """Turn rocprofv3 CSVs (kernel stats, FETCH_SIZE and WRITE_SIZE counter runs) into profiles/*.md."""
+PROFILE_GEMM_CALLS = 3
+PROFILE_DECODE_CALLS = 16
+
+
+def PROFILE_GEMMS(dg):
+    return (dg.LLAMA8B_ATTN_Q, dg.LLAMA8B_ATTN_O, dg.LLAMA8B_DEPTH)
+
+
+def profile_plan(dg, steps: int):
+    """(workload, kernel, dispatches) in the order `--profile --steps N` launches them."""
+    n = 1 + 2 * steps  # warmup, timed and staged prefill steps
+    pre = dg.LLAMA8B_PREFILL.name
+    plan = [(pre, "reorder", n), (pre, "gate_up", n), (pre, "down", n)]
+    for w in (dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16):
+        plan += [(w.name, "decode_gate_up", PROFILE_DECODE_CALLS),
+                 (w.name, "decode_down", PROFILE_DECODE_CALLS)]
+    for w in PROFILE_GEMMS(dg):
+        if w.axis == "mn":
+            plan += [(w.name, "reorder", PROFILE_GEMM_CALLS), (w.name, "gemm_mn", PROFILE_GEMM_CALLS)]
+        else:
+            plan += [(w.name, "pack_mask_bits", PROFILE_GEMM_CALLS),
+                     (w.name, "down", PROFILE_GEMM_CALLS)]
+    return plan
+
+
+def split_by_plan(plan, dispatches):
+    """dispatches: kernel -> [(dispatch id, value)] -> {(workload, kernel): [values]}.
+
+    Each kernel's dispatches, in dispatch order, are dealt to the plan entries of
+    that kernel in plan order."""
+    out = {}
+    for kernel in {k for _, k, _ in plan}:
+        seq = sorted(dispatches.get(kernel, []))
+        pos = 0
+        for workload, k, n in plan:
+            if k != kernel:
+                continue
+            out[(workload, kernel)] = [v for _, v in seq[pos:pos + n]]
+            pos += n
+    return out
+
+
+def summarize(directory: str, command: str, steps: int):
+    """Turn rocprofv3 CSVs (kernel trace, FETCH_SIZE and WRITE_SIZE counter runs) into profiles/*.md.
+
+    Dispatches are attributed to workloads by their order in the profile run."""
     from group_sparse_ffn_amd import datagen as dg
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
-    if stats:
-        rows = list(csv.DictReader(open(stats[0])))
-        lines = ["# Kernel trace: Llama3.1-8B-shaped FFN (prefill T=16384 and decode T=1, T=16)",
+    plan = profile_plan(dg, steps)
+
+    def kernel_of(name):
+        return next((k for k, v in KERNEL_SYMBOLS.items() if v in name), None)
+
+    traces = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        durs = {}
+        for r in csv.DictReader(open(traces[0])):
+            k = kernel_of(r["Kernel_Name"])
+            if k is not None:
+                durs.setdefault(k, []).append(
+                    (int(r["Dispatch_Id"]),
+                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        split = split_by_plan(plan, durs)
+        lines = ["# Kernel trace: Llama3.1-8B-shaped FFN (prefill T=16384, decode T=1 and T=16) "
+                 "and masked GEMMs at its attention shapes",
                  "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
-                 "| kernel | calls | avg (us) | min (us) | max (us) | share |",
-                 "|---|---|---|---|---|---|"]
-        for r in rows:
-            name = r["Name"]
-            short = next((k for k, v in KERNEL_SYMBOLS.items() if v in name), name[:60])
-            lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                         f"{float(r['Percentage']):.1f}% |")
+                 "Per-dispatch durations from the kernel trace, attributed to workloads by "
+                 "launch order.", "",
+                 "| kernel | workload | calls | median (us) | avg (us) | min (us) | max (us) |",
+                 "|---|---|---|---|---|---|---|"]
+        for workload, kernel, _ in plan:
+            v = split.get((workload, kernel), [])
+            if not v:
+                continue
+            med = sorted(v)[len(v) // 2]
+            lines.append(f"| {kernel} | {workload} | {len(v)} | {med:.1f} | {sum(v) / len(v):.1f} | "
+                         f"{min(v):.1f} | {max(v):.1f} |")
         out = os.path.join(ROOT, "profiles", "kernel_trace_llama8b.md")
         open(out, "w").write("\n".join(lines) + "\n")
         print(f"wrote {out}")
-    per = {}  # counter -> kernel -> list of values (KiB per dispatch)
-    per_id = {}  # counter -> kernel -> list of (dispatch id, value)
+    per = {}     # counter -> kernel name -> values (KiB per dispatch), for the copy calibration
+    per_id = {}  # counter -> kernel -> [(dispatch id, value)]
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
             per.setdefault(r["Counter_Name"], {}).setdefault(r["Kernel_Name"], []).append(
                 float(r["Counter_Value"]))
-            per_id.setdefault(r["Counter_Name"], {}).setdefault(r["Kernel_Name"], []).append(
-                (int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+            k = kernel_of(r["Kernel_Name"])
+            if k is not None:
+                per_id.setdefault(r["Counter_Name"], {}).setdefault(k, []).append(
+                    (int(r["Dispatch_Id"]), float(r["Counter_Value"])))
     if not per:
         return
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -376,33 +452,22 @@ def summarize(directory: str, command: str):
         return sum(vals) / len(vals)
 
     scale = {c: (COPY_BYTES / 1024) / copy_kib(c) for c in ("FETCH_SIZE", "WRITE_SIZE")}
-    # (kernel, workload, dispatch selector): the profile run launches the decode
-    # kernels for T=1 first (16 calls), then for T=16
-    jobs = [("gate_up", dg.LLAMA8B_PREFILL.name, None), ("down", dg.LLAMA8B_PREFILL.name, None),
-            ("reorder", dg.LLAMA8B_PREFILL.name, None),
-            ("decode_gate_up", dg.LLAMA8B_DECODE_T1.name, 0),
-            ("decode_gate_up", dg.LLAMA8B_DECODE_T16.name, 1),
-            ("decode_down", dg.LLAMA8B_DECODE_T1.name, 0),
-            ("decode_down", dg.LLAMA8B_DECODE_T16.name, 1)]
-    for kernel, workload, half in jobs:
-        sym = KERNEL_SYMBOLS[kernel]
+    split = {c: split_by_plan(plan, per_id.get(c, {})) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    for workload, kernel, _ in plan:
         vals = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            vs = [(d_id, v) for name, lst in per_id[counter].items() if sym in name for d_id, v in lst]
-            vs.sort()
-            if half is not None:
-                h = len(vs) // 2
-                vs = vs[:h] if half == 0 else vs[h:]
+            vs = split[counter].get((workload, kernel), [])
             if vs:
-                vals[counter] = sum(v for _, v in vs) / len(vs)
+                vals[counter] = sum(vs) / len(vs)
         if len(vals) < 2:
             continue
         fetch = vals["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
         write = vals["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
         text = [f"# HBM traffic per launch: {kernel} ({workload})", "",
                 "Two rocprofv3 counter runs of the command below (one with FETCH_SIZE, one with",
-                "WRITE_SIZE), averaged over the kernel's dispatches, in KiB, scaled by what the same",
-                f"counter reads for a device copy of {COPY_BYTES} bytes in the same run.", "",
+                "WRITE_SIZE), averaged over the kernel's dispatches for this workload, in KiB,",
+                f"scaled by what the same counter reads for a device copy of {COPY_BYTES} bytes",
+                "in the same run.", "",
                 "```", command.replace("PMC", "FETCH_SIZE"), command.replace("PMC", "WRITE_SIZE"),
                 "```", "",
                 f"- FETCH_SIZE_KiB: {vals['FETCH_SIZE']:.1f}",
@@ -432,7 +497,7 @@ def main():
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.command)
+        summarize(args.summarize, args.command, args.steps)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the group-sparse FFN "
