@@ -22,7 +22,20 @@
 //     Output: H[t, c] = silu(gate)*up, or +0.0 where token t skips the group.
 //   * down: a workgroup owns 16 output rows; it lists the 32-channel chunks
 //     whose group is in U and its eight waves split that list. Only those
-//     segments of each Wdown row are read; one writer per output.
+//     segments of each Wdown row are read; one writer per output. H is never
+//     read at a group no token executes (such a group may share a 32-channel
+//     chunk with an executed one when G = 16): those lanes use zeros.
+// For one or two tokens the matrix core gains nothing and its operand layout
+// (16 rows x 64 bytes per load) costs HBM efficiency, so a second pair of
+// kernels streams whole weight rows with contiguous 1 KB loads and VALU dot
+// products (v_dot2_f32_bf16) on a persistent grid (at T = 1 on the
+// Llama3.1-8B shape: gate/up 27 -> 21 us, down 17 -> 15 us):
+//   * gate/up: every wave takes channels of U in turn and reads its gate and
+//     up rows end to end; X sits in LDS;
+//   * down: every wave takes output rows in turn; one load covers 16 live
+//     32-channel chunks (64 bytes each) of the row; the live part of H is
+//     compacted into LDS once per workgroup, with zeros for groups no token
+//     executes.
 #include "common.h"
 
 namespace wide {
@@ -33,6 +46,33 @@ constexpr int kUnroll = 8;      // gate/up loads in flight per lane
 constexpr int kDownUnroll = 8;  // down loads in flight per lane
 constexpr int kMaxGroups = 4096;  // d_ff / 16
 constexpr int kDecodeSmallT = 4;  // largest T that uses 8-channel gate/up units
+constexpr int kValuMaxT = 2;      // largest T of the contiguous VALU kernels
+// Channels of compacted H the VALU down kernel holds per token in LDS: one
+// token fits four workgroups per CU, two tokens two.
+__host__ __device__ constexpr int valu_cap(int nt) { return nt == 1 ? 18432 : 14336; }
+constexpr int kValuMaxD = 8192;   // the VALU gate/up holds d / 512 loads per row per lane
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// dot of the eight bf16 held in each of two u32x4, accumulated in fp32 by
+// four v_dot2_f32_bf16. (The whole vector is reinterpreted and the pairs are
+// built from its elements: a bit cast of one 32-bit element of a u32x4 is
+// compiled by this toolchain into a reuse of element 0.)
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 p = {av[2 * e], av[2 * e + 1]}, q = {bv[2 * e], bv[2 * e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, q, acc, false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
 
 __device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
@@ -247,6 +287,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
   __shared__ uint16_t s_chunks[kMaxChunks];
   __shared__ int s_wave_cnt[kDownWaves];
   __shared__ float s_red[kDownWaves][64][4];
+  __shared__ uint8_t s_gact[kMaxGroups];  // G < 32: group executed by some token
   const int ng = d_ff / G;
   const int n0 = blockIdx.x * 16;
   const int tid = threadIdx.x;
@@ -261,6 +302,19 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
         hi = (c * 32 + 31) / G;
       },
       s_chunks, s_wave_cnt);
+  // With G < 32 a live chunk can hold a group that no token executes; its H
+  // was never written, so those lanes use zeros instead of reading it.
+  const bool split = G < 32;
+  if (split) {
+    for (int g = tid; g < ng; g += kDownThreads) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if (t < T) m |= mask[(size_t)t * ng + g];
+      s_gact[g] = m != 0;
+    }
+    __syncthreads();
+  }
 
   const int koff = 8 * (lane >> 4);
   const int tok = lane & 15;
@@ -278,7 +332,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
     for (int q = 0; q < kDownUnroll; ++q) {
       const int k = (int)s_chunks[wave + kDownWaves * (b * kDownUnroll + q)] * 32;
       a[set][q] = ld16_nt(pw + k);
-      bb[set][q] = ph ? ld16(ph + k) : zero;
+      bb[set][q] = (ph && (!split || s_gact[(k + koff) / G])) ? ld16(ph + k) : zero;
     }
   };
   auto mma_batch = [&](int set) {
@@ -297,8 +351,9 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
   }
   for (int j = nb * kDownUnroll; j < mine; ++j) {
     const int k = (int)s_chunks[wave + kDownWaves * j] * 32;
+    const bool live = ph && (!split || s_gact[(k + koff) / G]);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw + k)),
-                                                  __builtin_bit_cast(bf16x8, ph ? ld16(ph + k) : zero),
+                                                  __builtin_bit_cast(bf16x8, live ? ld16(ph + k) : zero),
                                                   acc, 0, 0, 0);
   }
 #pragma unroll
@@ -317,12 +372,223 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
   *(u32x2*)(Y + (size_t)tok * d + n0 + 4 * (lane >> 4)) = v;
 }
 
+// ---------------------------------------------------------------- T <= 2: VALU
+
+constexpr int kValuThreads = 256;
+constexpr int kValuWaves = kValuThreads / 64;
+
+// gate/up for T <= NT tokens. Wave items are the channels of the groups some
+// token executes; lane l reads 16 bytes at k = 8 l + 512 j of the item's gate
+// and up rows (whole 1 KB blocks per load), against X staged in LDS.
+template <int NT>
+__device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
+                                             const uint16_t* __restrict__ Wg,
+                                             const uint16_t* __restrict__ Wu,
+                                             const uint8_t* __restrict__ mask, int T, int d,
+                                             int d_ff, int G, uint16_t* __restrict__ H,
+                                             int zero_inactive, uint16_t* s_groups,
+                                             int* s_wave_cnt, uint16_t* s_x) {
+  constexpr int kJ = 8;  // 1 KB loads per row and k-block (4096 channels)
+  const int ng = d_ff / G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nact = list_active<kValuThreads>(
+      mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
+  // X rows of the NT tokens (rows past T are zeros)
+  const int cpr = d / 8;
+  for (int e = tid; e < NT * cpr; e += kValuThreads) {
+    const int t = e / cpr, c = e % cpr;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *(u32x4*)(s_x + t * d + 8 * c) = t < T ? ld16(X + (size_t)t * d + 8 * c) : z;
+  }
+  __syncthreads();
+  const int nj = d / 512;
+  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
+  const int nitems = nact * G;
+  for (int it = gw; it < nitems; it += nw) {
+    const int g = s_groups[it / G];
+    const int c = g * G + it % G;
+    const uint16_t* pg = Wg + (size_t)c * d + 8 * lane;
+    const uint16_t* pu = Wu + (size_t)c * d + 8 * lane;
+    float sg[NT], su[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sg[t] = su[t] = 0.0f;
+    for (int j0 = 0; j0 < nj; j0 += kJ) {
+      u32x4 vg[kJ], vu[kJ];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        if (j0 + j < nj) {
+          vg[j] = ld16_nt(pg + 512 * (j0 + j));
+          vu[j] = ld16_nt(pu + 512 * (j0 + j));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        if (j0 + j < nj) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const u32x4 xv = *(const u32x4*)(s_x + t * d + 512 * (j0 + j) + 8 * lane);
+            sg[t] = dot8(vg[j], xv, sg[t]);
+            su[t] = dot8(vu[j], xv, su[t]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      sg[t] = wave_sum(sg[t]);
+      su[t] = wave_sum(su[t]);
+    }
+    // lane t writes token t; a token that skips the group gets +0.0
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (lane == t && t < T) {
+        const bool act = mask[(size_t)t * ng + g] != 0;
+        H[(size_t)t * d_ff + c] = f32_to_bf16_bits(act ? silu_mul(sg[t], su[t]) : 0.0f);
+      }
+    }
+  }
+  if (!zero_inactive) return;
+  // groups no token executes: +0.0 over their channels (workgroup-strided)
+  for (int g = blockIdx.x; g < ng; g += gridDim.x) {
+    bool any = false;
+    for (int t = 0; t < T; ++t) any |= mask[(size_t)t * ng + g] != 0;
+    if (any) continue;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int e = tid; e < T * (G / 8); e += kValuThreads) {
+      const int t = e / (G / 8), c = e % (G / 8);
+      *(u32x4*)(H + (size_t)t * d_ff + g * G + 8 * c) = z;
+    }
+  }
+}
+
+// down for T <= NT tokens. Wave items are output rows; the live 32-channel
+// chunks are listed once, and H over them is compacted into LDS (zeros for
+// groups no token executes and for tokens past T). Lane l reads 16 bytes of
+// chunk 16 i + l / 4, piece l % 4, of the item's row.
+template <int NT>
+__device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
+                                          const uint16_t* __restrict__ Wd,
+                                          const uint8_t* __restrict__ mask, int T, int d, int d_ff,
+                                          int G, uint16_t* __restrict__ Y, uint16_t* s_chunks,
+                                          int* s_wave_cnt, uint16_t* s_h) {
+  constexpr int kBatch = 16;  // loads in flight per lane (a whole row of 256 live chunks)
+  const int ng = d_ff / G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = list_active<kValuThreads>(
+      mask, T, ng, d_ff / 32,
+      [G](int c, int& lo, int& hi) {
+        lo = (c * 32) / G;
+        hi = (c * 32 + 31) / G;
+      },
+      s_chunks, s_wave_cnt);
+  const int stride = nch * 32;  // compacted channels per token
+  for (int e = tid; e < NT * nch * 4; e += kValuThreads) {
+    const int t = e / (nch * 4), r = e % (nch * 4);
+    const int j = r >> 2, q = r & 3;
+    const int ch = (int)s_chunks[j] * 32 + 8 * q;
+    const int g = ch / G;
+    bool live = false;
+    for (int tt = 0; tt < T; ++tt) live |= mask[(size_t)tt * ng + g] != 0;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *(u32x4*)(s_h + t * stride + 32 * j + 8 * q) =
+        (t < T && live) ? ld16(H + (size_t)t * d_ff + ch) : z;
+  }
+  __syncthreads();
+  const int ninstr = (nch + 15) / 16;
+  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
+  const int piece = 8 * (lane & 3);
+  for (int n = gw; n < d; n += nw) {
+    const uint16_t* pw = Wd + (size_t)n * d_ff + piece;
+    float y[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = 0.0f;
+    for (int i0 = 0; i0 < ninstr; i0 += kBatch) {
+      u32x4 w[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int j = 16 * (i0 + q) + (lane >> 2);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        w[q] = j < nch ? ld16_nt(pw + (int)s_chunks[j] * 32) : z;
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int j = 16 * (i0 + q) + (lane >> 2);
+        if (j < nch) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            y[t] = dot8(w[q], *(const u32x4*)(s_h + t * stride + 32 * j + piece), y[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = wave_sum(y[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (lane == t && t < T) Y[(size_t)t * d + n] = f32_to_bf16_bits(y[t]);
+  }
+}
+
+#define WIDE_DECODE_VALU_KERNELS(NT)                                                            \
+  __global__ __launch_bounds__(kValuThreads) void decode_gate_up_valu_kernel_##NT(               \
+      const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,                          \
+      const uint16_t* __restrict__ Wu, const uint8_t* __restrict__ mask, int T, int d,          \
+      int d_ff, int G, uint16_t* __restrict__ H, int zero_inactive) {                           \
+    __shared__ uint16_t s_groups[kMaxGroups];                                                   \
+    __shared__ int s_wave_cnt[kValuWaves];                                                      \
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[NT * kValuMaxD];                       \
+    gate_up_valu<NT>(X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive, s_groups, s_wave_cnt,    \
+                     s_x);                                                                      \
+  }                                                                                             \
+  __global__ __launch_bounds__(kValuThreads) void decode_down_valu_kernel_##NT(                  \
+      const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,                          \
+      const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G,                          \
+      uint16_t* __restrict__ Y) {                                                               \
+    __shared__ uint16_t s_chunks[valu_cap(NT) / 32];                                            \
+    __shared__ int s_wave_cnt[kValuWaves];                                                      \
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[NT * valu_cap(NT)];                    \
+    down_valu<NT>(H, Wd, mask, T, d, d_ff, G, Y, s_chunks, s_wave_cnt, s_h);                   \
+  }
+WIDE_DECODE_VALU_KERNELS(1)
+WIDE_DECODE_VALU_KERNELS(2)
+#undef WIDE_DECODE_VALU_KERNELS
+
+// Shapes the VALU kernels take: whole 1 KB blocks per row, X in LDS, H over
+// every channel compactable into LDS.
+bool valu_shape(int T, int d, int d_ff) {
+  return T >= 1 && T <= kValuMaxT && d % 512 == 0 && d <= kValuMaxD && d_ff <= valu_cap(T) &&
+         d_ff % 32 == 0;
+}
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                       const uint8_t* mask, int T, int d, int d_ff, int G,
                                       uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  // one or two tokens: whole-row streaming on a persistent grid of three
+  // workgroups per CU (measured best of one to four at the Llama3.1-8B shape)
+  if (valu_shape(T, d, d_ff)) {
+    if (T == 1)
+      hipLaunchKernelGGL(decode_gate_up_valu_kernel_1, dim3(3 * num_cus()), dim3(kValuThreads), 0,
+                         stream, X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+    else
+      hipLaunchKernelGGL(decode_gate_up_valu_kernel_2, dim3(3 * num_cus()), dim3(kValuThreads), 0,
+                         stream, X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+    return hipGetLastError();
+  }
   // few tokens: 8-channel units (finest balance); more tokens: 16-channel
   // units whose gate and up operands share each activation fragment
   if (T <= kDecodeSmallT)
@@ -337,6 +603,17 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
 hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
                                    int T, int d, int d_ff, int G, uint16_t* Y, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (valu_shape(T, d, d_ff)) {
+    // two workgroups per CU (measured best of one, two and four), waves
+    // strided over the output rows
+    if (T == 1)
+      hipLaunchKernelGGL(decode_down_valu_kernel_1, dim3(2 * num_cus()), dim3(kValuThreads), 0,
+                         stream, H, Wd, mask, T, d, d_ff, G, Y);
+    else
+      hipLaunchKernelGGL(decode_down_valu_kernel_2, dim3(2 * num_cus()), dim3(kValuThreads), 0,
+                         stream, H, Wd, mask, T, d, d_ff, G, Y);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(decode_down_kernel, dim3(d / 16), dim3(kDownThreads), 0, stream, H, Wd, mask,
                      T, d, d_ff, G, Y);
   return hipGetLastError();

@@ -133,6 +133,35 @@ def test_decode_path_vs_oracle(T, G):
     check_h_zeros(H, inp["mask"], G)
 
 
+# No H_out: the workspace (H included) starts as NaN bits. Groups no token
+# executes are never written, and with G = 16 they share 32-channel chunks with
+# executed groups, so Y is finite and right only if the down GEMV never reads
+# them. T <= 2 with d % 512 == 0 takes the whole-row VALU kernels (also at the
+# edges of their LDS capacity: d_ff 18432 at T = 1, 14336 at T = 2, and just
+# past it), the rest the MFMA GEMVs.
+@pytest.mark.parametrize("T,d,d_ff,G", [
+    (1, 1024, 2048, 16), (2, 1024, 2048, 16), (1, 512, 2048, 32), (2, 2048, 2048, 512),
+    (3, 1024, 2048, 16), (5, 1024, 2048, 16), (16, 512, 2048, 16), (1, 256, 2048, 16),
+    (2, 8192, 1024, 64), (1, 512, 18432, 128), (2, 512, 14336, 128), (1, 512, 18496, 64),
+    (2, 512, 14400, 64),
+])
+def test_decode_never_reads_unwritten_h(T, d, d_ff, G):
+    inp = dg.random_small(500 + T + G, T, d, d_ff, G, "bf16", 0.3, wscale=0.05)
+    dv = to_dev(inp)
+    call = wide.FfnCall(dv["X"], dv["Wg"], dv["Wu"], dv["Wd"], dv["mask"], G,
+                        flags=wide.WIDE_FLAG_FORCE_DECODE)
+    call.workspace.fill_(0xFF)
+    Y = call.run()
+    torch.cuda.synchronize()
+    _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    assert bool(torch.isfinite(Y.float()).all())
+    assert rel_err(Y, Yref) <= TOL["bf16"]
+    # and with H returned, H holds exact zeros at every masked channel
+    Y2, H2 = run_ffn(inp, G, flags=wide.WIDE_FLAG_FORCE_DECODE)
+    check_h_zeros(H2, inp["mask"], G)
+    assert torch.equal(Y2.view(torch.int16), Y.view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [1, 4, 9])
 def test_decode_edge_masks(T):
     """Decode path: empty groups, tokens with no group, one active group, all-zero mask."""
