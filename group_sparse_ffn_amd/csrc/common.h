@@ -89,8 +89,13 @@ hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_
 hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                       const uint8_t* mask, int T, int d, int d_ff, int G,
                                       uint16_t* H, bool zero_inactive, hipStream_t stream);
+// For T > 2 (or shapes the whole-row kernels do not take) the down GEMV is
+// split over the live channel chunks: `part` holds kDecodeDownSplit * T * d
+// fp32 partial sums (workspace; contents on entry ignored).
+constexpr int kDecodeDownSplit = 8;
 hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
-                                   int T, int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
+                                   int T, int d, int d_ff, int G, uint16_t* Y, float* part,
+                                   hipStream_t stream);
 
 // fp32 prefill kernels (VALU, same structure as the bf16 ones).
 hipError_t launch_gate_up_f32(const float* X, const float* Wg, const float* Wu,

@@ -126,8 +126,9 @@ constexpr int kGuWaves = kGuThreads / 64;
 // One work unit: UC channels of one group, all T tokens, full K split over
 // the four waves. UC = 8: the 8 gate rows and 8 up rows form one 16-row MFMA
 // operand (finest balance; for few tokens the activation fragment costs
-// almost nothing). UC = 16: separate gate and up operands of 16 rows share
-// each activation fragment (half the activation traffic for many tokens).
+// almost nothing). UC = 16 / 32: UC/16 gate operands and UC/16 up operands of
+// 16 rows share each activation fragment (a half / a quarter of the
+// activation traffic per weight byte, for many tokens).
 template <int UC>
 __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
                                              const uint16_t* __restrict__ Wg,
@@ -135,8 +136,9 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
                                              const uint8_t* __restrict__ mask, int T, int d,
                                              int d_ff, int G, uint16_t* __restrict__ H,
                                              int zero_inactive, uint16_t* s_groups,
-                                             int* s_wave_cnt, float (*s_red)[64][8]) {
+                                             int* s_wave_cnt, float (*s_red)[64][16]) {
   constexpr int NF = UC / 8;  // 16-row A operands per unit
+  constexpr int kU = NF >= 4 ? 4 : kUnroll;  // loads per lane per batch and operand
   const int ng = d_ff / G;
   const int upg = G / UC;  // units per group
   const int tid = threadIdx.x;
@@ -181,13 +183,17 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   const int kbase = s_lo * 32 + 8 * (lane >> 4);
   const int r = lane & 15;
   // operand rows: UC == 8: rows 0..7 gate, 8..15 up of channels c0..c0+7;
-  //               UC == 16: operand 0 = gate rows, operand 1 = up rows of c0..c0+15
+  //   else operand f < NF/2: gate rows c0 + 16 f + r, operand f + NF/2: the up
+  //   rows of the same channels
   const uint16_t* pw[NF];
   if (NF == 1) {
     pw[0] = (r < 8 ? Wg : Wu) + (size_t)(c0 + (r & 7)) * d + kbase;
   } else {
-    pw[0] = Wg + (size_t)(c0 + r) * d + kbase;
-    pw[NF - 1] = Wu + (size_t)(c0 + r) * d + kbase;
+#pragma unroll
+    for (int f = 0; f < NF / 2; ++f) {
+      pw[f] = Wg + (size_t)(c0 + 16 * f + r) * d + kbase;
+      pw[f + NF / 2] = Wu + (size_t)(c0 + 16 * f + r) * d + kbase;
+    }
   }
   const int tok = lane & 15;
   const uint16_t* px = (tok < T) ? X + (size_t)tok * d + kbase : nullptr;
@@ -199,19 +205,19 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   const int nsub = s_hi - s_lo;
   // Software pipeline: the loads of batch b+1 are issued before the MFMAs of
   // batch b, so every wave keeps a batch of loads in flight while it computes.
-  const int nb = nsub / kUnroll;
-  u32x4 aw[2][NF][kUnroll], bx[2][kUnroll];
+  const int nb = nsub / kU;
+  u32x4 aw[2][NF][kU], bx[2][kU];
   auto load_batch = [&](int b, int set) {
 #pragma unroll
-    for (int q = 0; q < kUnroll; ++q) {
+    for (int q = 0; q < kU; ++q) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16_nt(pw[f] + 32 * (b * kUnroll + q));
-      bx[set][q] = px ? ld16(px + 32 * (b * kUnroll + q)) : zero;
+      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16_nt(pw[f] + 32 * (b * kU + q));
+      bx[set][q] = px ? ld16(px + 32 * (b * kU + q)) : zero;
     }
   };
   auto mma_batch = [&](int set) {
 #pragma unroll
-    for (int q = 0; q < kUnroll; ++q)
+    for (int q = 0; q < kU; ++q)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
         acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw[set][f][q]),
@@ -226,7 +232,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
     if (b + 2 < nb) load_batch(b + 2, 0);
     mma_batch(1);
   }
-  for (int s = nb * kUnroll; s < nsub; ++s) {
+  for (int s = nb * kU; s < nsub; ++s) {
     const bf16x8 bv = __builtin_bit_cast(bf16x8, px ? ld16(px + 32 * s) : zero);
 #pragma unroll
     for (int f = 0; f < NF; ++f)
@@ -242,24 +248,28 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   __syncthreads();
   if (wave != 0 || tok >= T) return;
   // UC == 8: gate channels 0..7 sit in lanes 0..31, the matching up rows in
-  // lanes 32..63; UC == 16: gate (operand 0) and up (operand 1) share a lane.
+  // lanes 32..63; else gate operand f and up operand f + NF/2 share a lane.
   if (NF == 1 && lane >= 32) return;
   // A token that skips this group still gets +0.0 here: the down GEMV reads
   // every channel of a group that some token executes.
   const bool act = mask[(size_t)tok * ng + g] != 0;
-  float h[4];
+  constexpr int NP = NF == 1 ? 1 : NF / 2;  // 16-channel (or 8-channel) blocks
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float gs = 0.0f, us = 0.0f;
+  for (int f = 0; f < NP; ++f) {
+    float h[4];
 #pragma unroll
-    for (int w = 0; w < kGuWaves; ++w) {
-      gs += s_red[w][lane][e];
-      us += (NF == 1) ? s_red[w][lane + 32][e] : s_red[w][lane][4 + e];
+    for (int e = 0; e < 4; ++e) {
+      float gs = 0.0f, us = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kGuWaves; ++w) {
+        gs += s_red[w][lane][4 * f + e];
+        us += (NF == 1) ? s_red[w][lane + 32][e] : s_red[w][lane][4 * (f + NP) + e];
+      }
+      h[e] = act ? silu_mul(gs, us) : 0.0f;
     }
-    h[e] = act ? silu_mul(gs, us) : 0.0f;
+    const u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+    *(u32x2*)(H + (size_t)tok * d_ff + c0 + 16 * f + 4 * (lane >> 4)) = v;
   }
-  const u32x2 v = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-  *(u32x2*)(H + (size_t)tok * d_ff + c0 + 4 * (lane >> 4)) = v;
 }
 
 #define WIDE_DECODE_GATE_UP_KERNEL(UC)                                                          \
@@ -269,33 +279,43 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
       int d_ff, int G, uint16_t* __restrict__ H, int zero_inactive) {                           \
     __shared__ uint16_t s_groups[kMaxGroups];                                                   \
     __shared__ int s_wave_cnt[kGuWaves];                                                        \
-    __shared__ float s_red[kGuWaves][64][8];                                                    \
+    __shared__ float s_red[kGuWaves][64][16];                                                   \
     gate_up_unit<UC>(X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive, s_groups, s_wave_cnt,    \
                      s_red);                                                                    \
   }
 WIDE_DECODE_GATE_UP_KERNEL(8)
 WIDE_DECODE_GATE_UP_KERNEL(16)
+WIDE_DECODE_GATE_UP_KERNEL(32)
 #undef WIDE_DECODE_GATE_UP_KERNEL
 
-constexpr int kDownThreads = 512;
-constexpr int kDownWaves = kDownThreads / 64;
+// Down GEMV for T > 2: split over the live chunks. A workgroup owns 64
+// output rows and one kDecodeDownSplit-th of the live 32-channel chunk list;
+// each wave multiplies every H fragment it loads by four 16-row blocks of
+// Wdown (a quarter of the H traffic of one block per fragment), and the four
+// waves meet in LDS. The fp32 partial sums go to `part` [split, T, d]; a
+// second kernel adds the splits in a fixed order and rounds once to bf16.
+constexpr int kSkRows = 64;
+constexpr int kSkThreads = 256;
+constexpr int kSkWaves = kSkThreads / 64;
+constexpr int kSkU = 4;  // chunks per batch per wave
+constexpr int kMaxChunks = 2048;  // d_ff / 32 limit
 
-__global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
+__global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
-    const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G, uint16_t* __restrict__ Y) {
-  constexpr int kMaxChunks = 2048;  // d_ff / 32 limit
+    const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G, float* __restrict__ part) {
   __shared__ uint16_t s_chunks[kMaxChunks];
-  __shared__ int s_wave_cnt[kDownWaves];
-  __shared__ float s_red[kDownWaves][64][4];
+  __shared__ int s_wave_cnt[kSkWaves];
+  __shared__ float s_red[kSkWaves][64][16];
   __shared__ uint8_t s_gact[kMaxGroups];  // G < 32: group executed by some token
   const int ng = d_ff / G;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = (int)(blockIdx.x / kDecodeDownSplit) * kSkRows;
+  const int split = (int)(blockIdx.x % kDecodeDownSplit);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
   // 32-channel chunks whose group some token executes
-  const int nch = list_active<kDownThreads>(
+  const int nch = list_active<kSkThreads>(
       mask, T, ng, d_ff / 32,
       [G](int c, int& lo, int& hi) {
         lo = (c * 32) / G;
@@ -304,9 +324,9 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
       s_chunks, s_wave_cnt);
   // With G < 32 a live chunk can hold a group that no token executes; its H
   // was never written, so those lanes use zeros instead of reading it.
-  const bool split = G < 32;
-  if (split) {
-    for (int g = tid; g < ng; g += kDownThreads) {
+  const bool halves = G < 32;
+  if (halves) {
+    for (int g = tid; g < ng; g += kSkThreads) {
       uint32_t m = 0;
 #pragma unroll
       for (int t = 0; t < 16; ++t)
@@ -315,31 +335,45 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
     }
     __syncthreads();
   }
+  const int lo = (split * nch) / kDecodeDownSplit;
+  const int hi = ((split + 1) * nch) / kDecodeDownSplit;
 
   const int koff = 8 * (lane >> 4);
   const int tok = lane & 15;
-  const uint16_t* pw = Wd + (size_t)(n0 + (lane & 15)) * d_ff + koff;
+  const uint16_t* pw[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) pw[rb] = Wd + (size_t)(n0 + 16 * rb + (lane & 15)) * d_ff + koff;
   const uint16_t* ph = (tok < T) ? H + (size_t)tok * d_ff + koff : nullptr;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // this wave takes chunks wave, wave + kDownWaves, ...; batches of kDownUnroll
+  f32x4 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this wave takes chunks lo + wave, lo + wave + 4, ...; batches of kSkU
   // chunks, the loads of batch b+1 issued before the MFMAs of batch b
-  const int mine = nch > wave ? (nch - wave + kDownWaves - 1) / kDownWaves : 0;
-  const int nb = mine / kDownUnroll;
-  u32x4 a[2][kDownUnroll], bb[2][kDownUnroll];
+  const int mine = hi - lo > wave ? (hi - lo - wave + kSkWaves - 1) / kSkWaves : 0;
+  const int nb = mine / kSkU;
+  u32x4 a[2][4][kSkU], bb[2][kSkU];
+  auto chunk_k = [&](int i) { return (int)s_chunks[lo + wave + kSkWaves * i] * 32; };
+  auto h_load = [&](int k) {
+    return (ph && (!halves || s_gact[(k + koff) / G])) ? ld16(ph + k) : zero;
+  };
   auto load_batch = [&](int b, int set) {
 #pragma unroll
-    for (int q = 0; q < kDownUnroll; ++q) {
-      const int k = (int)s_chunks[wave + kDownWaves * (b * kDownUnroll + q)] * 32;
-      a[set][q] = ld16_nt(pw + k);
-      bb[set][q] = (ph && (!split || s_gact[(k + koff) / G])) ? ld16(ph + k) : zero;
+    for (int q = 0; q < kSkU; ++q) {
+      const int k = chunk_k(b * kSkU + q);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) a[set][rb][q] = ld16_nt(pw[rb] + k);
+      bb[set][q] = h_load(k);
     }
   };
   auto mma_batch = [&](int set) {
 #pragma unroll
-    for (int q = 0; q < kDownUnroll; ++q)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[set][q]),
-                                                    __builtin_bit_cast(bf16x8, bb[set][q]), acc, 0, 0, 0);
+    for (int q = 0; q < kSkU; ++q)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[set][rb][q]),
+                                                          __builtin_bit_cast(bf16x8, bb[set][q]),
+                                                          acc[rb], 0, 0, 0);
   };
   if (nb > 0) load_batch(0, 0);
   for (int b = 0; b < nb; b += 2) {
@@ -349,27 +383,43 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_kernel(
     if (b + 2 < nb) load_batch(b + 2, 0);
     mma_batch(1);
   }
-  for (int j = nb * kDownUnroll; j < mine; ++j) {
-    const int k = (int)s_chunks[wave + kDownWaves * j] * 32;
-    const bool live = ph && (!split || s_gact[(k + koff) / G]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw + k)),
-                                                  __builtin_bit_cast(bf16x8, live ? ld16(ph + k) : zero),
-                                                  acc, 0, 0, 0);
-  }
+  for (int i = nb * kSkU; i < mine; ++i) {
+    const int k = chunk_k(i);
+    const bf16x8 hv = __builtin_bit_cast(bf16x8, h_load(k));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) s_red[wave][lane][e] = acc[e];
+    for (int rb = 0; rb < 4; ++rb)
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw[rb] + k)),
+                                                        hv, acc[rb], 0, 0, 0);
+  }
+  // lane holds token (lane % 16) and rows 16 rb + 4 (lane / 16) + e
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_red[wave][lane][4 * rb + e] = acc[rb][e];
   __syncthreads();
   if (wave != 0 || tok >= T) return;
-  float y[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float sum = 0.0f;
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kDownWaves; ++w) sum += s_red[w][lane][e];
-    y[e] = sum;
+    for (int w = 0; w < kSkWaves; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += s_red[w][lane][4 * rb + e];
+    *(f32x4*)(part + ((size_t)split * T + tok) * d + n0 + 16 * rb + 4 * (lane >> 4)) = y;
   }
+}
+
+// Y[t, n] = bf16(sum over the splits of part[s, t, n]), splits added in order.
+__global__ __launch_bounds__(256) void decode_down_reduce_kernel(const float* __restrict__ part,
+                                                                 int T, int d,
+                                                                 uint16_t* __restrict__ Y) {
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;  // 4 outputs per thread
+  if (i >= T * d / 4) return;
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < kDecodeDownSplit; ++sp) y += *(const f32x4*)(part + (size_t)sp * T * d + 4 * i);
   const u32x2 v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-  *(u32x2*)(Y + (size_t)tok * d + n0 + 4 * (lane >> 4)) = v;
+  *(u32x2*)(Y + 4 * (size_t)i) = v;
 }
 
 // ---------------------------------------------------------------- T <= 2: VALU
@@ -589,11 +639,15 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
                          stream, X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
     return hipGetLastError();
   }
-  // few tokens: 8-channel units (finest balance); more tokens: 16-channel
-  // units whose gate and up operands share each activation fragment
+  // few tokens: 8-channel units (finest balance); more tokens: 32-channel
+  // units (16 with G = 16) whose gate and up operands share each activation
+  // fragment
   if (T <= kDecodeSmallT)
     hipLaunchKernelGGL(decode_gate_up_kernel_8, dim3(d_ff / 8), dim3(kGuThreads), 0, stream, X, Wg,
                        Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+  else if (G % 32 == 0)
+    hipLaunchKernelGGL(decode_gate_up_kernel_32, dim3(d_ff / 32), dim3(kGuThreads), 0, stream, X,
+                       Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
   else
     hipLaunchKernelGGL(decode_gate_up_kernel_16, dim3(d_ff / 16), dim3(kGuThreads), 0, stream, X,
                        Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
@@ -601,7 +655,8 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
 }
 
 hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
-                                   int T, int d, int d_ff, int G, uint16_t* Y, hipStream_t stream) {
+                                   int T, int d, int d_ff, int G, uint16_t* Y, float* part,
+                                   hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (valu_shape(T, d, d_ff)) {
     // two workgroups per CU (measured best of one, two and four), waves
@@ -614,8 +669,12 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                          stream, H, Wd, mask, T, d, d_ff, G, Y);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(decode_down_kernel, dim3(d / 16), dim3(kDownThreads), 0, stream, H, Wd, mask,
-                     T, d, d_ff, G, Y);
+  hipLaunchKernelGGL(decode_down_splitk_kernel, dim3((d / kSkRows) * kDecodeDownSplit),
+                     dim3(kSkThreads), 0, stream, H, Wd, mask, T, d, d_ff, G, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_down_reduce_kernel, dim3((T * d / 4 + 255) / 256), dim3(256), 0, stream,
+                     part, T, d, Y);
   return hipGetLastError();
 }
 

@@ -50,11 +50,13 @@ size_t elt_size(wide_dtype_t dt) { return dt == WIDE_BF16 ? 2 : 4; }
 //   padded   int32  [ngroups]
 //   maskbits uint32 [ngroups, ceil(T/32)]
 //   H        dtype  [T, d_ff]   (used when the caller passes no H_out)
+//   part     fp32   [kDecodeDownSplit, T, d]   (T <= WIDE_DECODE_T_LIMIT only:
+//                   the decode down GEMV's partial sums)
 struct Layout {
-  size_t perm, counts, padded, maskbits, h, total;
+  size_t perm, counts, padded, maskbits, h, part, total;
 };
 
-Layout layout(int64_t T, int64_t d_ff, int64_t G, wide_dtype_t dt) {
+Layout layout(int64_t T, int64_t d, int64_t d_ff, int64_t G, wide_dtype_t dt) {
   const int64_t ng = d_ff / G;
   const int64_t words = (T + 31) / 32;
   Layout L{};
@@ -69,6 +71,8 @@ Layout layout(int64_t T, int64_t d_ff, int64_t G, wide_dtype_t dt) {
   off = round_up(off + (size_t)(ng * words) * 4, 256);
   L.h = off;
   off = round_up(off + (size_t)(T * d_ff) * elt_size(dt), 256);
+  L.part = off;
+  if (T <= WIDE_DECODE_T_LIMIT) off = round_up(off + (size_t)(wide::kDecodeDownSplit * T * d) * 4, 256);
   L.total = off;
   return L;
 }
@@ -136,7 +140,7 @@ wide_status_t validate(const Args& a, bool* decode) {
       return fail(WIDE_ERR_UNSUPPORTED, "the decode path needs bf16 and T <= %d", WIDE_DECODE_T_LIMIT);
     dec = true;
   }
-  const Layout L = layout(a.T, a.d_ff, a.G, a.dt);
+  const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt);
   if (!a.ws) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if ((reinterpret_cast<uintptr_t>(a.ws) & 255u) != 0)
     return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -147,12 +151,13 @@ wide_status_t validate(const Args& a, bool* decode) {
 }
 
 wide_status_t run_stage(wide_stage_t stage, const Args& a) {
-  const Layout L = layout(a.T, a.d_ff, a.G, a.dt);
+  const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt);
   char* ws = static_cast<char*>(a.ws);
   int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
   uint32_t* maskbits = reinterpret_cast<uint32_t*>(ws + L.maskbits);
+  float* part = reinterpret_cast<float*>(ws + L.part);
   void* H = a.H_out ? a.H_out : static_cast<void*>(ws + L.h);
   const bool zero_h = a.H_out != nullptr;
   const int ng = a.d_ff / a.G;
@@ -189,7 +194,7 @@ wide_status_t run_stage(wide_stage_t stage, const Args& a) {
       return hip_status(e, "decode gate/up launch");
     case WIDE_STAGE_DECODE_DOWN:
       e = wide::launch_decode_down_bf16((const uint16_t*)H, (const uint16_t*)a.Wd, a.mask, a.T, a.d,
-                                        a.d_ff, a.G, (uint16_t*)a.Y, a.stream);
+                                        a.d_ff, a.G, (uint16_t*)a.Y, part, a.stream);
       return hip_status(e, "decode down launch");
   }
   return fail(WIDE_ERR_SHAPE, "unknown stage %d", (int)stage);
@@ -218,7 +223,7 @@ WIDE_API size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int3
                                         wide_dtype_t dtype) {
   if (T < 0 || d <= 0 || d_ff <= 0 || G <= 0 || d_ff % G != 0) return 0;
   if (dtype != WIDE_F32 && dtype != WIDE_BF16) return 0;
-  return layout(T, d_ff, G, dtype).total;
+  return layout(T, d, d_ff, G, dtype).total;
 }
 
 WIDE_API wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup,
