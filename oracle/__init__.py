@@ -44,6 +44,8 @@ def _load():
         lib.oracle_gemm_mn.restype = ctypes.c_int
         lib.oracle_gemm_k.argtypes = [p, p, p, i64, i64, i64, i64, p, i64, p]
         lib.oracle_gemm_k.restype = ctypes.c_int
+        lib.oracle_router.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_int, p, i64, p, p]
+        lib.oracle_router.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -147,3 +149,32 @@ def gemm_mn(A, B, mask, G: int, rows=None):
 def gemm_k(A, B, mask, G: int, rows=None):
     """K-axis group-masked C in fp64: C[m,n] = sum_k mask[m, k/G] A[m,k] B[n,k]."""
     return _gemm("oracle_gemm_k", A, B, mask, G, rows, _as_f32(A).shape[1])
+
+
+ROUTER_ACTS = {"identity": 0, "relu": 1, "silu": 2}
+
+
+def router(X, W1, W2, act: str = "silu", rows=None):
+    """Bottleneck router in fp64 -> (logits [n, N_G, 2] float64, mask [n, N_G] uint8).
+
+    z = act(X W1^T), logits = z W2^T viewed as [N_G, 2]; a group executes
+    (mask 1) when its class-0 logit is >= its class-1 logit.
+    """
+    x, w1, w2 = _as_f32(X), _as_f32(W1), _as_f32(W2)
+    T, D = x.shape
+    r = w1.shape[0]
+    if w1.shape != (r, D) or w2.ndim != 2 or w2.shape[1] != r or w2.shape[0] % 2:
+        raise ValueError("W1 must be [r, D] and W2 [2*N_G, r]")
+    ng = w2.shape[0] // 2
+    if rows is None:
+        rr, n = None, T
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rr.shape[0]
+    logits = np.empty((n, ng, 2), dtype=np.float64)
+    mask = np.empty((n, ng), dtype=np.uint8)
+    rc = _load().oracle_router(_ptr(x), _ptr(w1), _ptr(w2), T, D, r, ng, ROUTER_ACTS[act],
+                               None if rr is None else _ptr(rr), n, _ptr(logits), _ptr(mask))
+    if rc != 0:
+        raise ValueError(f"oracle_router rejected its arguments (rc={rc})")
+    return logits, mask

@@ -167,6 +167,61 @@ int oracle_gemm_k(const float* A, const float* B, const uint8_t* mask, int64_t M
   return ORACLE_OK;
 }
 
+/*
+ * Bottleneck router (ai.info summary, "How decisions are made": input
+ * activations -> N_G two-way decisions per token through an inner dimension r
+ * of 16 or 32; argmax at inference; class 0 = execute, class 1 = skip. The
+ * paper's Sec. 3.1 "Routing Components" gives no formula.) Readings taken:
+ * no biases, an activation between the two maps chosen by the caller, logits
+ * laid out [T, N_G, 2] with the class fastest, and argmax taking the first
+ * maximum, so a tie executes:
+ *   z[t,j]       = act( sum_k X[t,k] * W1[j,k] )           j < r
+ *   logit[t,g,c] = sum_j W2[2g + c, j] * z[t,j]             c in {0, 1}
+ *   mask[t,g]    = 1 if logit[t,g,0] >= logit[t,g,1] else 0
+ * act: 0 identity, 1 relu(a) = max(a, 0), 2 silu(a) = a / (1 + exp(-a)).
+ * X [T, D], W1 [r, D], W2 [2*N_G, r]. Rows t listed in rows[0..nrows) (NULL:
+ * 0..nrows-1); logits [nrows, N_G, 2] and mask [nrows, N_G] per listed row.
+ */
+static double router_act(double a, int act) {
+  if (act == 1) return a > 0.0 ? a : 0.0;
+  if (act == 2) return a / (1.0 + exp(-a));
+  return a;
+}
+
+int oracle_router(const float* X, const float* W1, const float* W2, int64_t T, int64_t D,
+                  int64_t r, int64_t ngroups, int act, const int64_t* rows, int64_t nrows,
+                  double* logits, uint8_t* mask) {
+  if (!X || !W1 || !W2 || !logits || !mask || T < 0 || D <= 0 || r <= 0 || r > 256 ||
+      ngroups <= 0 || act < 0 || act > 2 || nrows < 0)
+    return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t t = rows ? rows[i] : i;
+    if (t < 0 || t >= T) return ORACLE_BAD_ARG;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t t = rows ? rows[i] : i;
+    double zp[256];
+    for (int64_t j = 0; j < r; ++j) {
+      double s = 0.0;
+      for (int64_t k = 0; k < D; ++k) s += (double)X[t * D + k] * (double)W1[j * D + k];
+      zp[j] = router_act(s, act);
+    }
+    for (int64_t g = 0; g < ngroups; ++g) {
+      double l[2];
+      for (int c = 0; c < 2; ++c) {
+        double s = 0.0;
+        for (int64_t j = 0; j < r; ++j) s += (double)W2[(2 * g + c) * r + j] * zp[j];
+        l[c] = s;
+      }
+      logits[(i * ngroups + g) * 2 + 0] = l[0];
+      logits[(i * ngroups + g) * 2 + 1] = l[1];
+      mask[i * ngroups + g] = l[0] >= l[1] ? 1 : 0;
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -470,3 +470,152 @@ def test_gemm_pins_catch_planted_mistake(axis, bug):
         except (ValueError, IndexError):
             results[pin.__name__] = False
     assert not all(results.values()), f"no pin caught '{bug}' on axis {axis}: {results}"
+
+
+# ----------------------------------------------------------------------------- router
+# The bottleneck router (ai.info summary, "How decisions are made"). Pins: a
+# hand-derived fixture, closed forms of the two nonlinearities, the argmax's
+# invariance to a positive scale of W2 and its flip when each group's two
+# class rows are swapped, token independence, and 50-digit brute force.
+
+def router_problem(seed, T, D, r, ng, scale=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((T, D)).astype(np.float32)
+    W1 = (rng.standard_normal((r, D)) / np.sqrt(D)).astype(np.float32)
+    W2 = (scale * rng.standard_normal((2 * ng, r)) / np.sqrt(r)).astype(np.float32)
+    return X, W1, W2
+
+
+def oracle_router_fn(X, W1, W2, act):
+    return oracle.router(X, W1, W2, act)
+
+
+def rpin_hand_fixture(fn):
+    f = json.load(open(os.path.join(GOLDEN, "router_hand.json")))
+    X, W1, W2 = (np.array(f[k], np.float32) for k in ("X", "W1", "W2"))
+    logits, mask = fn(X, W1, W2, f["act"])
+    return (np.array_equal(mask, np.array(f["mask"], np.uint8))
+            and np.allclose(logits, np.array(f["logits"]), rtol=0, atol=1e-12))
+
+
+def rpin_activation_closed_forms(fn):
+    # z = act(a) with a = x0, and one group whose class-0 logit is z, class-1 logit 0
+    X = np.array([[1.0, 0.0], [-2.0, 0.0], [0.5, 0.0]], np.float32)
+    W1 = np.array([[1.0, 0.0]], np.float32)
+    W2 = np.array([[1.0], [0.0]], np.float32)
+    ok = True
+    expect = {"identity": [1.0, -2.0, 0.5], "relu": [1.0, 0.0, 0.5],
+              "silu": [1 / (1 + np.exp(-1.0)), -2.0 / (1 + np.exp(2.0)), 0.5 / (1 + np.exp(-0.5))]}
+    for act, want in expect.items():
+        logits, mask = fn(X, W1, W2, act)
+        ok &= np.allclose(logits[:, 0, 0], want, rtol=0, atol=1e-14)
+        ok &= np.array_equal(mask[:, 0], (np.array(want) >= 0).astype(np.uint8))
+    return ok
+
+
+def rpin_scale_and_swap(fn):
+    X, W1, W2 = router_problem(11, 64, 48, 16, 12)
+    l0, m0 = fn(X, W1, W2, "silu")
+    _, m1 = fn(X, W1, (W2 * np.float32(4.0)).astype(np.float32), "silu")
+    swapped = W2.reshape(12, 2, 16)[:, ::-1, :].reshape(24, 16).copy()
+    _, m2 = fn(X, W1, swapped, "silu")
+    ties = l0[:, :, 0] == l0[:, :, 1]
+    return np.array_equal(m0, m1) and np.array_equal(m2[~ties], 1 - m0[~ties])
+
+
+def rpin_token_independence(fn):
+    X, W1, W2 = router_problem(12, 40, 32, 8, 6)
+    perm = np.random.Generator(np.random.PCG64(3)).permutation(40)
+    l, m = fn(X, W1, W2, "relu")
+    lp, mp_ = fn(X[perm], W1, W2, "relu")
+    return np.array_equal(lp, l[perm]) and np.array_equal(mp_, m[perm])
+
+
+def rpin_mpmath(fn):
+    mpmath.mp.dps = 50
+    X, W1, W2 = router_problem(13, 3, 8, 4, 3)
+    ok = True
+    for act in ("identity", "relu", "silu"):
+        logits, mask = fn(X, W1, W2, act)
+        for t in range(3):
+            z = []
+            for j in range(4):
+                a = mpmath.fsum(mpmath.mpf(float(X[t, k])) * mpmath.mpf(float(W1[j, k])) for k in range(8))
+                z.append(a if act == "identity" else (max(a, 0) if act == "relu" else a / (1 + mpmath.exp(-a))))
+            for g in range(3):
+                ref = [mpmath.fsum(mpmath.mpf(float(W2[2 * g + c, j])) * z[j] for j in range(4)) for c in (0, 1)]
+                ok &= abs(float(ref[0]) - logits[t, g, 0]) <= 1e-14 and abs(float(ref[1]) - logits[t, g, 1]) <= 1e-14
+                ok &= int(mask[t, g]) == int(ref[0] >= ref[1])
+    return ok
+
+
+ROUTER_PINS = [rpin_hand_fixture, rpin_activation_closed_forms, rpin_scale_and_swap,
+               rpin_token_independence, rpin_mpmath]
+
+
+@pytest.mark.parametrize("pin", ROUTER_PINS, ids=lambda p: p.__name__)
+def test_oracle_router_pins(pin):
+    assert pin(oracle_router_fn)
+
+
+def test_oracle_router_rows_subset_and_rejects_bad_arguments():
+    X, W1, W2 = router_problem(14, 30, 16, 8, 5)
+    l, m = oracle.router(X, W1, W2, "silu")
+    rows = [29, 0, 7]
+    lr, mr = oracle.router(X, W1, W2, "silu", rows=rows)
+    assert np.array_equal(lr, l[rows]) and np.array_equal(mr, m[rows])
+    with pytest.raises(ValueError):
+        oracle.router(X, W1, W2, "silu", rows=[30])
+    with pytest.raises(ValueError):
+        oracle.router(X, W1[:, :8], W2, "silu")
+
+
+def _np_router(X, W1, W2, act, bug=None):
+    x, w1, w2 = (np.asarray(a, np.float64) for a in (X, W1, W2))
+    if bug == "w1_transposed":
+        w1 = w1.T.reshape(w1.shape) if w1.shape[0] != w1.shape[1] else w1.T
+    a = x @ w1.T
+    if bug == "act_after_w2":
+        z = a
+    elif act == "relu":
+        z = np.maximum(a, 0)
+    elif act == "silu":
+        z = a / (1 + np.exp(-a))
+    else:
+        z = a
+    lg = z @ w2.T
+    if bug == "act_after_w2" and act != "identity":
+        lg = np.maximum(lg, 0) if act == "relu" else lg / (1 + np.exp(-lg))
+    ng = w2.shape[0] // 2
+    if bug == "class_major_layout":
+        logits = lg.reshape(-1, 2, ng).transpose(0, 2, 1)
+    else:
+        logits = lg.reshape(-1, ng, 2)
+    if bug == "polarity":
+        mask = (logits[:, :, 1] >= logits[:, :, 0]).astype(np.uint8)
+    elif bug == "tie_skips":
+        mask = (logits[:, :, 0] > logits[:, :, 1]).astype(np.uint8)
+    else:
+        mask = (logits[:, :, 0] >= logits[:, :, 1]).astype(np.uint8)
+    return logits, mask
+
+
+ROUTER_MUTANTS = ["polarity", "tie_skips", "class_major_layout", "act_after_w2", "w1_transposed"]
+
+
+def test_router_pins_pass_on_correct_numpy_variant():
+    assert all(pin(_np_router) for pin in ROUTER_PINS if pin is not rpin_mpmath)
+
+
+@pytest.mark.parametrize("bug", ROUTER_MUTANTS)
+def test_router_pins_catch_planted_mistake(bug):
+    fn = lambda X, W1, W2, act: _np_router(X, W1, W2, act, bug=bug)  # noqa: E731
+    results = {}
+    for pin in ROUTER_PINS:
+        if pin is rpin_mpmath:
+            continue
+        try:
+            results[pin.__name__] = bool(pin(fn))
+        except (ValueError, IndexError):
+            results[pin.__name__] = False
+    assert not all(results.values()), f"no pin caught '{bug}': {results}"
