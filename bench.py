@@ -232,6 +232,35 @@ def bench_masked_gemms(torch, wide, dg, steps: int):
     return out
 
 
+def bench_router(torch, wide, dg, steps: int):
+    """The bottleneck router (mask production) at the Llama3.1-8B FFN shape:
+    D = 4096, r = 32, 112 groups, SiLU, for the prefill length and T = 1."""
+    out = {}
+    dev = "cuda:0"
+    D, r, ng = 4096, 32, 112
+    rw = dg.make_router_weights(7, D, r, ng)
+    W1, W2 = rw["W1"].to(dev), rw["W2"].to(dev)
+    for T in (16384, 1):
+        X = dg.to_dtype(dg.normal_f32(8, (T, D)), "bf16").to(dev)
+        mask = torch.empty((T, ng), dtype=torch.uint8, device=dev)
+        call = lambda: wide.router_forward(X, W1, W2, "silu", mask=mask)
+        for _ in range(3):
+            call()
+        # replay of a graph holding 16 calls: the binding's host-side checks
+        # (and one graph launch per call) would dominate at T = 1
+        def calls16():
+            for _ in range(16):
+                call()
+        ms = graph_step_ms(torch, calls16, max(steps, 10)) / 16
+        nbytes = T * D * 2 + T * ng + r * D * 2 + 2 * ng * r * 2
+        out[f"T{T}"] = {"us": round(ms * 1e3, 2), "bytes": nbytes,
+                        "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "execute_fraction": round(float(mask.float().mean()), 4)}
+        del X, mask
+    return out
+
+
 def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
     """fp64 oracle on a seeded token sample, scaled to effective TFLOP/s."""
     import numpy as np
@@ -564,6 +593,7 @@ def main():
         line["decode"] = bench_decode(torch, wide, dg, args.steps)
     if not args.no_gemm:
         line["masked_gemms"] = bench_masked_gemms(torch, wide, dg, args.steps)
+        line["router"] = bench_router(torch, wide, dg, args.steps)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         import oracle

@@ -18,7 +18,7 @@ from ._lib import (WIDE_BF16, WIDE_DECODE_T_LIMIT, WIDE_F32, WIDE_FLAG_FORCE_DEC
                    WideError)
 
 __all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decode_max_t",
-           "gemm_mn", "gemm_k", "gemm_workspace_size",
+           "gemm_mn", "gemm_k", "gemm_workspace_size", "router_forward",
            "FfnCall", "WideError", "WIDE_TOKEN_TILE", "WIDE_DECODE_T_LIMIT",
            "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
            "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
@@ -169,3 +169,31 @@ def gemm_mn(A, B, mask, G: int, C=None, workspace=None):
 def gemm_k(A, B, mask, G: int, C=None, workspace=None):
     """K-axis masked GEMM: C[m, n] = sum over active groups g of A[m, g] . B[n, g] (bf16)."""
     return _gemm("wide_gemm_k", A, B, mask, G, "k", C, workspace)
+
+
+# ---------------------------------------------------------------- router
+
+_ACTS = {"identity": _lib.WIDE_ACT_IDENTITY, "relu": _lib.WIDE_ACT_RELU, "silu": _lib.WIDE_ACT_SILU}
+
+
+def router_forward(X, W1, W2, act: str = "silu", return_logits: bool = False, mask=None,
+                   logits=None):
+    """Bottleneck router -> mask [T, N_G] uint8 (1 = execute), and logits [T, N_G, 2] fp32."""
+    for name, t in (("X", X), ("W1", W1), ("W2", W2)):
+        _need_cuda(name, t)
+    if any(t.dtype != torch.bfloat16 for t in (X, W1, W2)):
+        raise ValueError("X, W1 and W2 must be bfloat16")
+    T, D = X.shape
+    r = W1.shape[0]
+    if W1.shape != (r, D) or W2.dim() != 2 or W2.shape[1] != r or W2.shape[0] % 2:
+        raise ValueError("expected W1 [r, D] and W2 [2 * ngroups, r]")
+    ng = W2.shape[0] // 2
+    dev = X.device
+    if mask is None:
+        mask = torch.empty((T, ng), dtype=torch.uint8, device=dev)
+    if return_logits and logits is None:
+        logits = torch.empty((T, ng, 2), dtype=torch.float32, device=dev)
+    _lib.check(_lib.load().wide_router_forward(
+        X.data_ptr(), W1.data_ptr(), W2.data_ptr(), T, D, r, ng, _ACTS[act], WIDE_BF16,
+        mask.data_ptr(), None if logits is None else logits.data_ptr(), _stream_ptr(dev)))
+    return (mask, logits) if return_logits else mask

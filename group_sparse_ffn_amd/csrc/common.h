@@ -97,6 +97,12 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                                    int T, int d, int d_ff, int G, uint16_t* Y, float* part,
                                    hipStream_t stream);
 
+// Bottleneck router: mask[t, g] = argmax over the two logits of group g is
+// class 0 (act 0 identity, 1 relu, 2 silu); logits [T, ng, 2] optional.
+hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
+                              int D, int r, int ng, int act, uint8_t* mask, float* logits,
+                              hipStream_t stream);
+
 // fp32 prefill kernels (VALU, same structure as the bf16 ones).
 hipError_t launch_gate_up_f32(const float* X, const float* Wg, const float* Wu,
                               const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,

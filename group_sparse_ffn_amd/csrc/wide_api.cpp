@@ -376,6 +376,35 @@ WIDE_API wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* 
   return ok();
 }
 
+WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
+                                           int32_t T, int32_t D, int32_t r, int32_t ngroups,
+                                           wide_act_t act, wide_dtype_t dtype, uint8_t* mask,
+                                           float* logits, void* stream) {
+  if (!W1 || !W2) return fail(WIDE_ERR_NULL, "W1 and W2 must be non-NULL");
+  if (T != 0 && (!X || !mask)) return fail(WIDE_ERR_NULL, "X and mask must be non-NULL when T > 0");
+  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (T < 0 || D <= 0 || r <= 0 || ngroups <= 0)
+    return fail(WIDE_ERR_SHAPE, "need T >= 0 and D, r, ngroups >= 1 (T=%d D=%d r=%d ngroups=%d)", T, D,
+                r, ngroups);
+  if (act != WIDE_ACT_IDENTITY && act != WIDE_ACT_RELU && act != WIDE_ACT_SILU)
+    return fail(WIDE_ERR_SHAPE, "unknown activation %d", (int)act);
+  if (dtype != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the router kernel runs bf16 only");
+  if (D % 32 != 0 || (r != 16 && r != 32 && r != 64))
+    return fail(WIDE_ERR_UNSUPPORTED, "the router kernel needs D %% 32 == 0 and r in {16, 32, 64} (D=%d r=%d)",
+                D, r);
+  if ((int64_t)T * D >= (1ll << 31) || (int64_t)T * ngroups >= (1ll << 31))
+    return fail(WIDE_ERR_UNSUPPORTED, "T*D and T*ngroups must stay below 2^31");
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) ||
+      (reinterpret_cast<uintptr_t>(logits) & 7u) != 0)
+    return fail(WIDE_ERR_ALIGN, "X, W1 and W2 must be 16-byte aligned, logits 8-byte aligned");
+  if (T == 0) return ok();
+  const hipError_t e = wide::launch_router_bf16((const uint16_t*)X, (const uint16_t*)W1,
+                                                (const uint16_t*)W2, T, D, r, ngroups, (int)act,
+                                                mask, logits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "router launch");
+  return ok();
+}
+
 WIDE_API const char* wide_status_string(wide_status_t s) {
   switch (s) {
     case WIDE_OK: return "ok";

@@ -281,3 +281,14 @@ def make_gemm_inputs(w: GemmWorkload, M: Optional[int] = None,
     return {"A": to_dtype(normal_f32(s, (M, w.K)), "bf16"),
             "B": to_dtype(normal_f32(s + 1, (w.N, w.K), 0.02), "bf16"),
             "mask": torch.from_numpy(make_gemm_mask(w, mask_kind, M))}
+
+
+# ---------------------------------------------------------------- router
+
+def make_router_weights(seed: int, D: int, r: int, ngroups: int) -> dict:
+    """Synthetic bottleneck-router weights (no trained ones exist here):
+    W1 [r, D] ~ N(0, 1/D) with seed `seed`, W2 [2*ngroups, r] ~ N(0, 1/r) with
+    seed `seed + 1`, both rounded once to bf16. With these scales the two
+    logits of a group are exchangeable, so about half the groups execute."""
+    return {"W1": to_dtype(normal_f32(seed, (r, D), 1.0 / np.sqrt(D)), "bf16"),
+            "W2": to_dtype(normal_f32(seed + 1, (2 * ngroups, r), 1.0 / np.sqrt(r)), "bf16")}

@@ -215,6 +215,43 @@ wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* mask, int
                           int32_t K, int32_t G, wide_dtype_t dtype, void* C, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * wide_router_forward - the bottleneck router that produces the group mask
+ * (ai.info summary, "How decisions are made": input activations -> N_G
+ * two-way decisions per token through an inner dimension r, typically 16 or
+ * 32; argmax at inference; class 0 = execute, class 1 = skip). The paper's
+ * Sec. 3.1 "Routing Components" prints no formula; the readings taken are no
+ * biases, an activation chosen by the caller, logits [T, N_G, 2] with the
+ * class fastest, and a tie going to class 0 (the first maximum):
+ *   z[t,j]       = act( X[t,:] . W1[j,:] )          j < r
+ *   logit[t,g,c] = W2[2g + c, :] . z[t,:]             c in {0, 1}
+ *   mask[t,g]    = 1 if logit[t,g,0] >= logit[t,g,1] else 0
+ * The mask is exactly what wide_ffn_forward, wide_gemm_mn and wide_gemm_k take.
+ *
+ *   X       [T, D]          device, bf16, read only (the FFN's input for an FFN router).
+ *   W1      [r, D]          device, bf16, read only.
+ *   W2      [2*ngroups, r]  device, bf16, read only (row 2g + c: class c of group g).
+ *   act     WIDE_ACT_*.
+ *   mask    [T, ngroups]    device, uint8, written.
+ *   logits  [T, ngroups, 2] device, fp32, written when non-NULL.
+ * z and the logits are computed in fp32 from bf16 operands (fp32 products and
+ * sums, fixed order), and the argmax is taken on those fp32 logits.
+ * Sizes: T >= 0 (T == 0 enqueues nothing; X, mask and logits may then be
+ * NULL), ngroups >= 1; the kernels need D % 32 == 0, r in {16, 32, 64} and
+ * T*D, T*ngroups < 2^31, else WIDE_ERR_UNSUPPORTED. bf16 only.
+ * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_DTYPE, WIDE_ERR_ALIGN,
+ * WIDE_ERR_UNSUPPORTED, WIDE_ERR_HIP.
+ */
+typedef enum {
+  WIDE_ACT_IDENTITY = 0,
+  WIDE_ACT_RELU = 1, /* max(a, 0) */
+  WIDE_ACT_SILU = 2  /* a / (1 + exp(-a)) */
+} wide_act_t;
+
+wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2, int32_t T,
+                                  int32_t D, int32_t r, int32_t ngroups, wide_act_t act,
+                                  wide_dtype_t dtype, uint8_t* mask, float* logits, void* stream);
+
 /* Static text for a status code. */
 const char* wide_status_string(wide_status_t status);
 

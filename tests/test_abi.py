@@ -191,3 +191,37 @@ def test_gemm_workspace_size(lib):
     assert need <= ws <= need + 4 * 256
     assert lib.wide_gemm_workspace_size(-1, 8) == 0
     assert lib.wide_gemm_workspace_size(16, 0) == 0
+
+
+def router_call(lib, **kw):
+    a = dict(X=FAKE, W1=FAKE, W2=FAKE, T=64, D=256, r=32, ng=8, act=_lib.WIDE_ACT_SILU,
+             dtype=_lib.WIDE_BF16, mask=FAKE, logits=None, stream=None)
+    a.update(kw)
+    return lib.wide_router_forward(a["X"], a["W1"], a["W2"], a["T"], a["D"], a["r"], a["ng"],
+                                   a["act"], a["dtype"], a["mask"], a["logits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W1=None), _lib.WIDE_ERR_NULL),
+    (dict(X=None), _lib.WIDE_ERR_NULL),
+    (dict(mask=None), _lib.WIDE_ERR_NULL),
+    (dict(dtype=4), _lib.WIDE_ERR_DTYPE),
+    (dict(dtype=_lib.WIDE_F32), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(T=-1), _lib.WIDE_ERR_SHAPE),
+    (dict(D=0), _lib.WIDE_ERR_SHAPE),
+    (dict(ng=0), _lib.WIDE_ERR_SHAPE),
+    (dict(act=7), _lib.WIDE_ERR_SHAPE),
+    (dict(D=48), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(r=24), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(T=1 << 24, D=256), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(X=FAKE + 8), _lib.WIDE_ERR_ALIGN),
+    (dict(W2=FAKE + 2), _lib.WIDE_ERR_ALIGN),
+    (dict(logits=FAKE + 4), _lib.WIDE_ERR_ALIGN),
+])
+def test_router_validation(lib, kw, status):
+    assert router_call(lib, **kw) == status
+    assert lib.wide_last_error().decode() != ""
+
+
+def test_router_t0_is_a_no_op(lib):
+    assert router_call(lib, T=0, X=None, mask=None) == _lib.WIDE_OK

@@ -1,0 +1,103 @@
+"""Bottleneck router on the GPU vs the fp64 oracle.
+
+Bars:
+  * logits: |gpu - oracle| <= 1e-3 * max|oracle logit| of the case (bf16
+    operands, fp32 products and sums over D terms, then over r terms);
+  * the GPU mask is its own fp32 argmax, bit for bit: mask == (l0 >= l1) on
+    the returned logits (the decision is taken in the kernel's precision);
+  * the GPU mask equals the oracle's wherever the oracle's two logits differ
+    by more than twice the logit tolerance (elsewhere either answer is right);
+  * identical class rows (an exact tie) execute; T == 0 is a no-op.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import group_sparse_ffn_amd as wide
+from group_sparse_ffn_amd import datagen as dg
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LOGIT_TOL = 1e-3
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+def inputs(seed, T, D, r, ng):
+    X = dg.to_dtype(dg.normal_f32(seed, (T, D)), "bf16")
+    w = dg.make_router_weights(seed + 10, D, r, ng)
+    return X, w["W1"], w["W2"]
+
+
+def check(X, W1, W2, act, rows=None):
+    mask, logits = wide.router_forward(X.to(DEV), W1.to(DEV), W2.to(DEV), act, return_logits=True)
+    torch.cuda.synchronize()
+    lref, mref = oracle.router(X, W1, W2, act, rows=rows)
+    if rows is not None:
+        idx = torch.from_numpy(np.asarray(rows)).to(DEV)
+        mask, logits = mask[idx], logits[idx]
+    lg = logits.double().cpu().numpy()
+    mk = mask.cpu().numpy()
+    tol = LOGIT_TOL * max(np.abs(lref).max(), 1e-30)
+    assert np.abs(lg - lref).max() <= tol
+    assert np.array_equal(mk, (lg[..., 0] >= lg[..., 1]).astype(np.uint8))
+    clear = np.abs(lref[..., 0] - lref[..., 1]) > 2 * tol
+    assert np.array_equal(mk[clear], mref[clear])
+    return mk
+
+
+@pytest.mark.parametrize("T,D,r,ng,act", [
+    (1, 64, 16, 1, "identity"), (15, 256, 32, 3, "relu"), (16, 512, 64, 112, "silu"),
+    (17, 4096, 32, 112, "silu"), (300, 1024, 16, 37, "relu"), (1000, 96, 32, 5, "silu"),
+    (257, 4096, 64, 8, "identity"), (40, 5120, 32, 136, "silu"),
+])
+def test_router_small_all_outputs(T, D, r, ng, act):
+    X, W1, W2 = inputs(T + D + r, T, D, r, ng)
+    mk = check(X, W1, W2, act)
+    # the synthetic router executes about half of the groups
+    if T * ng >= 1000:
+        assert 0.3 < mk.mean() < 0.7
+
+
+def test_router_llama8b_prefill_shape_sampled():
+    T, D, r, ng = 16384, 4096, 32, 112
+    X, W1, W2 = inputs(9, T, D, r, ng)
+    rng = np.random.Generator(np.random.PCG64(9))
+    rows = np.unique(np.concatenate([[0, 15, 16, T - 1], rng.integers(0, T, 60)]))
+    check(X, W1, W2, "silu", rows=rows)
+
+
+def test_router_exact_tie_executes():
+    T, D, r, ng = 50, 256, 16, 6
+    X, W1, W2 = inputs(5, T, D, r, ng)
+    W2 = W2.clone()
+    W2[1::2] = W2[0::2]  # class 1 row == class 0 row in every group
+    mask = wide.router_forward(X.to(DEV), W1.to(DEV), W2.to(DEV), "silu")
+    torch.cuda.synchronize()
+    assert bool((mask == 1).all())
+
+
+def test_router_t0_and_feeds_the_ffn():
+    w = dg.Workload("router-ffn", 31, T=300, d=512, d_ff=2048, G=128, dtype="bf16",
+                    mask_kind="bernoulli")
+    inp = dg.make_inputs(w)
+    rw = dg.make_router_weights(99, w.d, 32, w.ngroups)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    mask = wide.router_forward(d["X"], rw["W1"].to(DEV), rw["W2"].to(DEV), "silu")
+    Y = wide.ffn_forward(d["X"], d["Wg"], d["Wu"], d["Wd"], mask, w.G)
+    torch.cuda.synchronize()
+    _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], mask.cpu(), w.G)
+    y = Y.float().cpu().numpy().astype(np.float64)
+    assert np.abs(y - Yref).max() / np.abs(Yref).max() <= 2e-2
+    e = torch.empty((0, w.d), dtype=torch.bfloat16, device=DEV)
+    m0 = wide.router_forward(e, rw["W1"].to(DEV), rw["W2"].to(DEV), "silu")
+    torch.cuda.synchronize()
+    assert m0.shape == (0, w.ngroups)
