@@ -52,9 +52,14 @@ KERNEL_SOURCES = {
     "down": ["gemm_k.hip", "mfma_core.h", "common.h"],
     "reorder": ["reorder.hip", "common.h"],
     "decode_gate_up": ["decode.hip", "common.h"],
-    "decode_down": ["decode.hip", "common.h"],
     "gemm_mn": ["gemm_mn.hip", "mfma_core.h", "common.h"],
     "pack_mask_bits": ["reorder.hip", "common.h"],
+    "router": ["router.hip", "common.h"],
+    "router_small": ["router.hip", "common.h"],
+    "decode_down_splitk": ["decode.hip", "common.h"],
+    "decode_down_reduce": ["decode.hip", "common.h"],
+    "decode_gate_up_valu": ["decode.hip", "common.h"],
+    "decode_down_valu": ["decode.hip", "common.h"],
 }
 # substrings of the device symbol names of each kernel
 KERNEL_SYMBOLS = {
@@ -62,9 +67,14 @@ KERNEL_SYMBOLS = {
     "down": "down_bf16_kernel",
     "reorder": "reorder_kernel",
     "decode_gate_up": "decode_gate_up_kernel",
-    "decode_down": "decode_down_kernel",
     "gemm_mn": "gemm_mn_bf16_kernel",
     "pack_mask_bits": "pack_mask_bits_kernel",
+    "router": "router_kernel_",
+    "router_small": "router_small_kernel_",
+    "decode_down_splitk": "decode_down_splitk_kernel",
+    "decode_down_reduce": "decode_down_reduce_kernel",
+    "decode_gate_up_valu": "decode_gate_up_valu_kernel",
+    "decode_down_valu": "decode_down_valu_kernel",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read + 1 GiB written
 
@@ -363,12 +373,21 @@ def run_profile(steps: int):
         torch.cuda.empty_cache()
     for w in PROFILE_GEMMS(dg):
         inp = {k: v.to("cuda:0") for k, v in dg.make_gemm_inputs(w).items()}
+        # (router calls follow the masked GEMMs)
         fn = wide.gemm_mn if w.axis == "mn" else wide.gemm_k
         for _ in range(PROFILE_GEMM_CALLS):
             fn(inp["A"], inp["B"], inp["mask"], w.G)
         torch.cuda.synchronize()
         del inp
         torch.cuda.empty_cache()
+    rw = dg.make_router_weights(7, 4096, 32, 112)
+    W1, W2 = rw["W1"].to("cuda:0"), rw["W2"].to("cuda:0")
+    for T in PROFILE_ROUTER_T:
+        X = dg.to_dtype(dg.normal_f32(8, (T, 4096)), "bf16").to("cuda:0")
+        for _ in range(PROFILE_GEMM_CALLS):
+            wide.router_forward(X, W1, W2, "silu")
+        torch.cuda.synchronize()
+        del X
     src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -379,6 +398,8 @@ def run_profile(steps: int):
 
 PROFILE_GEMM_CALLS = 3
 PROFILE_DECODE_CALLS = 16
+PROFILE_ROUTER_T = (16384, 1)
+ROUTER_WORKLOADS = {16384: "llama3.1-8b-router-prefill", 1: "llama3.1-8b-router-decode-t1"}
 
 
 def PROFILE_GEMMS(dg):
@@ -390,15 +411,22 @@ def profile_plan(dg, steps: int):
     n = 1 + 2 * steps  # warmup, timed and staged prefill steps
     pre = dg.LLAMA8B_PREFILL.name
     plan = [(pre, "reorder", n), (pre, "gate_up", n), (pre, "down", n)]
-    for w in (dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16):
-        plan += [(w.name, "decode_gate_up", PROFILE_DECODE_CALLS),
-                 (w.name, "decode_down", PROFILE_DECODE_CALLS)]
+    # T = 1 takes the whole-row VALU GEMVs; T = 16 the MFMA gate/up and the
+    # split-K down with its reduce
+    t1, t16 = dg.LLAMA8B_DECODE_T1.name, dg.LLAMA8B_DECODE_T16.name
+    plan += [(t1, "decode_gate_up_valu", PROFILE_DECODE_CALLS),
+             (t1, "decode_down_valu", PROFILE_DECODE_CALLS),
+             (t16, "decode_gate_up", PROFILE_DECODE_CALLS),
+             (t16, "decode_down_splitk", PROFILE_DECODE_CALLS),
+             (t16, "decode_down_reduce", PROFILE_DECODE_CALLS)]
     for w in PROFILE_GEMMS(dg):
         if w.axis == "mn":
             plan += [(w.name, "reorder", PROFILE_GEMM_CALLS), (w.name, "gemm_mn", PROFILE_GEMM_CALLS)]
         else:
             plan += [(w.name, "pack_mask_bits", PROFILE_GEMM_CALLS),
                      (w.name, "down", PROFILE_GEMM_CALLS)]
+    plan += [(ROUTER_WORKLOADS[16384], "router", PROFILE_GEMM_CALLS),
+             (ROUTER_WORKLOADS[1], "router_small", PROFILE_GEMM_CALLS)]
     return plan
 
 
