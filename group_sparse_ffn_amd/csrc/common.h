@@ -58,6 +58,11 @@ hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t*
                           int32_t* counts, int32_t* padded, uint32_t* maskbits,
                           hipStream_t stream);
 
+// The same reorder from packed mask bits (made by launch_pack_mask_bits).
+hipError_t launch_reorder_from_bits(const uint32_t* maskbits, int T, int ng, int tile,
+                                    int32_t* perm, int32_t* counts, int32_t* padded,
+                                    hipStream_t stream);
+
 // Packed mask bits alone: maskbits[g, w] bit b = mask[32w + b, g] != 0.
 hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* maskbits,
                                  hipStream_t stream);

@@ -122,7 +122,105 @@ __global__ __launch_bounds__(256) void pack_mask_bits_kernel(const uint8_t* __re
   maskbits[(size_t)g * words + w] = bits;
 }
 
+// Reorder from packed mask bits (the path inside wide_ffn_forward and
+// wide_gemm_mn, where the bits are made by the packing kernel above from
+// coalesced reads of the mask rows; the column reads of reorder_kernel touch a
+// cache line per token). A workgroup of 256 threads owns one group and one
+// chunk of 64 64-token words (4096 tokens) of its contiguous bit row: it counts
+// the whole row and the words before its chunk, scans the chunk's word
+// popcounts in one wave, and each wave places a word's 64 tokens at once
+// (lane l: token 64 w + l; rank among the word's actives = popcount of the
+// bits below l).
+constexpr int kBitsThreads = 256;
+constexpr int kBitsWaves = kBitsThreads / 64;
+constexpr int kBitsChunk = 64;  // 64-token words per workgroup
+
+__global__ __launch_bounds__(kBitsThreads) void reorder_bits_kernel(
+    const uint32_t* __restrict__ maskbits, int T, int ng, int tile, int words,
+    int32_t* __restrict__ perm, int32_t* __restrict__ counts, int32_t* __restrict__ padded) {
+  __shared__ int s_sum[2][kBitsWaves];
+  __shared__ int s_base[kBitsChunk];
+  __shared__ uint64_t s_bits[kBitsChunk];
+  const int g = blockIdx.x;
+  const int c0 = (int)blockIdx.y * kBitsChunk;  // first word of this chunk
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t* __restrict__ mb = maskbits + (size_t)g * words;
+  const int nw64 = (words + 1) / 2;
+  auto word64 = [&](int w) -> uint64_t {
+    const uint64_t lo = mb[2 * w];
+    const uint64_t hi = 2 * w + 1 < words ? mb[2 * w + 1] : 0u;
+    return lo | (hi << 32);
+  };
+
+  // the row's count and the actives before this chunk
+  int all = 0, before = 0;
+  for (int w = tid; w < nw64; w += kBitsThreads) {
+    const int pc = __popcll(word64(w));
+    all += pc;
+    before += w < c0 ? pc : 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    all += __shfl_xor(all, off, 64);
+    before += __shfl_xor(before, off, 64);
+  }
+  if (lane == 0) {
+    s_sum[0][wave] = all;
+    s_sum[1][wave] = before;
+  }
+  // the chunk's words and their exclusive popcount scan (wave 0)
+  if (wave == 0) {
+    const int w = c0 + lane;
+    const uint64_t bits = w < nw64 ? word64(w) : 0ull;
+    const int pc = __popcll(bits);
+    int incl = pc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    s_base[lane] = incl - pc;
+    s_bits[lane] = bits;
+  }
+  __syncthreads();
+  int count = 0, base0 = 0;
+#pragma unroll
+  for (int w = 0; w < kBitsWaves; ++w) {
+    count += s_sum[0][w];
+    base0 += s_sum[1][w];
+  }
+  int32_t* __restrict__ prow = perm + (size_t)g * T;
+  const int nwc = min(kBitsChunk, nw64 - c0);
+  for (int j = wave; j < nwc; j += kBitsWaves) {
+    const uint64_t b = s_bits[j];
+    const int base = base0 + s_base[j];
+    const int t = 64 * (c0 + j) + lane;
+    const int below = __popcll(b & ((1ull << lane) - 1ull));
+    if (t < T) {
+      const int pos = ((b >> lane) & 1ull) ? base + below : count + (t - base - below);
+      prow[pos] = t;
+    }
+  }
+  if (blockIdx.y == 0 && tid == 0) {
+    counts[g] = count;
+    padded[g] = (int)(((long long)count + tile - 1) / tile) * tile;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_reorder_from_bits(const uint32_t* maskbits, int T, int ng, int tile,
+                                    int32_t* perm, int32_t* counts, int32_t* padded,
+                                    hipStream_t stream) {
+  const int words = (T + 31) / 32;
+  const int nw64 = (words + 1) / 2;
+  const int nchunks = nw64 > 0 ? (nw64 + kBitsChunk - 1) / kBitsChunk : 1;
+  hipLaunchKernelGGL(reorder_bits_kernel, dim3(ng, nchunks), dim3(kBitsThreads), 0, stream,
+                     maskbits, T, ng, tile, words, perm, counts, padded);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* maskbits,
                                  hipStream_t stream) {

@@ -164,8 +164,12 @@ wide_status_t run_stage(wide_stage_t stage, const Args& a) {
   hipError_t e = hipSuccess;
   switch (stage) {
     case WIDE_STAGE_REORDER:
-      e = wide::launch_reorder(a.mask, a.T, ng, WIDE_TOKEN_TILE, perm, counts, padded, maskbits,
-                               a.stream);
+      // packed bits from coalesced reads of the mask rows, then the per-group
+      // partition from each group's contiguous bit row
+      e = wide::launch_pack_mask_bits(a.mask, a.T, ng, maskbits, a.stream);
+      if (e != hipSuccess) return hip_status(e, "mask pack launch");
+      e = wide::launch_reorder_from_bits(maskbits, a.T, ng, WIDE_TOKEN_TILE, perm, counts, padded,
+                                         a.stream);
       return hip_status(e, "mask reorder launch");
     case WIDE_STAGE_GATE_UP:
       if (a.dt == WIDE_BF16)
@@ -348,8 +352,11 @@ WIDE_API wide_status_t wide_gemm_mn(const void* A, const void* B, const uint8_t*
   int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
+  uint32_t* maskbits = reinterpret_cast<uint32_t*>(ws + L.maskbits);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = wide::launch_reorder(mask, M, ng, WIDE_TOKEN_TILE, perm, counts, padded, nullptr, s);
+  hipError_t e = wide::launch_pack_mask_bits(mask, M, ng, maskbits, s);
+  if (e != hipSuccess) return hip_status(e, "mask pack launch");
+  e = wide::launch_reorder_from_bits(maskbits, M, ng, WIDE_TOKEN_TILE, perm, counts, padded, s);
   if (e != hipSuccess) return hip_status(e, "mask reorder launch");
   e = wide::launch_gemm_mn_bf16((const uint16_t*)A, (const uint16_t*)B, perm, counts, M, K, N, G,
                                 (uint16_t*)C, s);

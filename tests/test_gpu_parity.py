@@ -83,6 +83,50 @@ def test_reorder_bit_exact(T, ng, tile, kind):
     assert np.array_equal(padded.cpu().numpy(), rpad)
 
 
+def _round_up(x, a):
+    return (x + a - 1) // a * a
+
+
+# The FFN's own reorder stage (packed bits, then a per-group partition of each
+# bit row) leaves perm / counts / padded at the front of the workspace:
+# perm int32 [ng, T], then counts [ng] and padded [ng], each 256-byte aligned.
+@pytest.mark.parametrize("T,ng,kind", [
+    (64, 16, "bernoulli"), (1, 3, "bernoulli"), (1000, 37, "bernoulli"), (1025, 5, "bernoulli"),
+    (16384, 112, "topk"), (300, 8, "ones"), (300, 8, "zeros"), (16385, 7, "zipf"),
+    (65, 1, "bernoulli"), (40000, 2, "bernoulli"),
+])
+def test_ffn_reorder_stage_bit_exact(T, ng, kind):
+    G, d = 64, 64
+    d_ff = ng * G
+    if kind == "bernoulli":
+        m = dg.mask_bernoulli(T, ng, 0.4, seed=T + 7 * ng)
+    elif kind == "topk":
+        m = dg.mask_topk(T, ng, ng // 2, seed=2005)
+    elif kind == "zipf":
+        m = dg.mask_zipf(T, ng, 0.5, seed=5005)
+    elif kind == "ones":
+        m = np.ones((T, ng), np.uint8)
+    else:
+        m = np.zeros((T, ng), np.uint8)
+    X = torch.zeros((T, d), dtype=torch.bfloat16, device=DEV)
+    W = torch.zeros((d_ff, d), dtype=torch.bfloat16, device=DEV)
+    Wd = torch.zeros((d, d_ff), dtype=torch.bfloat16, device=DEV)
+    call = wide.FfnCall(X, W, W, Wd, torch.from_numpy(m).to(DEV), G,
+                        flags=wide.WIDE_FLAG_FORCE_PREFILL)
+    call.workspace.fill_(0xCD)
+    wide.ffn_stage(wide.WIDE_STAGE_REORDER, call)
+    torch.cuda.synchronize()
+    ws = call.workspace
+    o_counts = _round_up(ng * T * 4, 256)
+    o_padded = o_counts + _round_up(ng * 4, 256)
+    perm = ws[: ng * T * 4].view(torch.int32).reshape(ng, T).cpu().numpy()
+    counts = ws[o_counts: o_counts + ng * 4].view(torch.int32).cpu().numpy()
+    padded = ws[o_padded: o_padded + ng * 4].view(torch.int32).cpu().numpy()
+    rp, rc, rpad = oracle.reorder(m, wide.WIDE_TOKEN_TILE)
+    assert np.array_equal(perm, rp)
+    assert np.array_equal(counts, rc) and np.array_equal(padded, rpad)
+
+
 def test_reorder_nonzero_bytes_count_as_active():
     m = dg.mask_bernoulli(500, 6, 0.5, seed=1) * np.uint8(200)
     perm, counts, _ = wide.reorder_masks(torch.from_numpy(m).to(DEV), 256)
