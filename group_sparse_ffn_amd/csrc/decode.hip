@@ -5,9 +5,13 @@
 //
 // Both kernels are bound by streaming weights from HBM, so they are built for
 // balance and memory-level parallelism:
-//   * weights are read with non-temporal 16-byte loads (no reuse) in batches
-//     of eight per lane; the next batch is issued before the MFMAs of the
-//     current one, so loads stay in flight while the wave computes;
+//   * weights are read with 16-byte loads in batches per lane; the next batch
+//     is issued before the MFMAs of the current one, so loads stay in flight
+//     while the wave computes. The MFMA operand layout reads half of a 128-byte
+//     line per load and the other half with the next one, so these loads keep
+//     the default cache policy (with the non-temporal hint the second half
+//     missed again: the T = 16 gate/up took 63 instead of 58 us); the
+//     whole-row kernels below read whole lines and stream them non-temporally;
 //   * the tokens sit on the N side of v_mfma_f32_16x16x32_bf16 (tokens past T
 //     read as zeros), so the matrix core does the dot products and every
 //     weight byte is loaded exactly once per call;
@@ -211,7 +215,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
 #pragma unroll
     for (int q = 0; q < kU; ++q) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16_nt(pw[f] + 32 * (b * kU + q));
+      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16(pw[f] + 32 * (b * kU + q));
       bx[set][q] = px ? ld16(px + 32 * (b * kU + q)) : zero;
     }
   };
@@ -236,7 +240,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
     const bf16x8 bv = __builtin_bit_cast(bf16x8, px ? ld16(px + 32 * s) : zero);
 #pragma unroll
     for (int f = 0; f < NF; ++f)
-      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw[f] + 32 * s)),
+      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[f] + 32 * s)),
                                                        bv, acc[f], 0, 0, 0);
   }
 
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     for (int q = 0; q < kSkU; ++q) {
       const int k = chunk_k(b * kSkU + q);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[set][rb][q] = ld16_nt(pw[rb] + k);
+      for (int rb = 0; rb < 4; ++rb) a[set][rb][q] = ld16(pw[rb] + k);
       bb[set][q] = h_load(k);
     }
   };
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     const bf16x8 hv = __builtin_bit_cast(bf16x8, h_load(k));
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
-      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16_nt(pw[rb] + k)),
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[rb] + k)),
                                                         hv, acc[rb], 0, 0, 0);
   }
   // lane holds token (lane % 16) and rows 16 rb + 4 (lane / 16) + e

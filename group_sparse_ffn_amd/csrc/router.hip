@@ -11,7 +11,7 @@
 //
 // The first map reads every activation byte once and is bound by HBM, so the
 // kernel is built to stream X: a workgroup owns 64 tokens and its four waves
-// split D; each wave reads 16-byte non-temporal pieces of X in the layout of a
+// split D; each wave reads 16-byte pieces of X in the layout of a
 // v_mfma_f32_16x16x32_bf16 operand (16 tokens x 32 channels per load) against
 // the r / 16 matching fragments of W1 (shared by every workgroup, served from
 // L2, each fragment used for all four 16-token blocks), with the loads of the next
@@ -30,9 +30,9 @@ namespace {
 // one block, so that the chain of dependent loads along D is 16 times shorter.
 constexpr int kRtGC = 64;  // groups whose W2 rows are staged in LDS at a time
 
-__device__ __forceinline__ u32x4 rt_ld_nt(const uint16_t* p) {
-  return __builtin_nontemporal_load((const u32x4*)p);
-}
+// X pieces are read in the MFMA operand layout (half of a 128-byte line per
+// load, the other half with the next), so they keep the default cache policy.
+__device__ __forceinline__ u32x4 rt_ld(const uint16_t* p) { return *(const u32x4*)p; }
 
 __device__ __forceinline__ float router_act(float a, int act) {
   if (act == 1) return a > 0.0f ? a : 0.0f;
@@ -88,7 +88,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
     for (int q = 0; q < kU; ++q) {
       const int k = 32 * (bt * kU + q);
 #pragma unroll
-      for (int b = 0; b < kRtRB; ++b) ax[set][b][q] = px[b] ? rt_ld_nt(px[b] + k) : zero;
+      for (int b = 0; b < kRtRB; ++b) ax[set][b][q] = px[b] ? rt_ld(px[b] + k) : zero;
 #pragma unroll
       for (int f = 0; f < NF; ++f) bw[set][f][q] = *(const u32x4*)(pw[f] + k);
     }
@@ -115,7 +115,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   for (int s = nb * kU; s < nsub; ++s) {
 #pragma unroll
     for (int b = 0; b < kRtRB; ++b) {
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, px[b] ? rt_ld_nt(px[b] + 32 * s) : zero);
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, px[b] ? rt_ld(px[b] + 32 * s) : zero);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
         acc[b][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
