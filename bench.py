@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "decode_gate_up": ["decode.hip", "common.h"],
     "gemm_mn": ["gemm_mn.hip", "mfma_core.h", "common.h"],
     "pack_mask_bits": ["reorder.hip", "common.h"],
+    "reorder_bits": ["reorder.hip", "common.h"],
     "router": ["router.hip", "common.h"],
     "router_small": ["router.hip", "common.h"],
     "decode_down_splitk": ["decode.hip", "common.h"],
@@ -69,6 +70,7 @@ KERNEL_SYMBOLS = {
     "decode_gate_up": "decode_gate_up_kernel",
     "gemm_mn": "gemm_mn_bf16_kernel",
     "pack_mask_bits": "pack_mask_bits_kernel",
+    "reorder_bits": "reorder_bits_kernel",
     "router": "router_kernel_",
     "router_small": "router_small_kernel_",
     "decode_down_splitk": "decode_down_splitk_kernel",
@@ -271,6 +273,37 @@ def bench_router(torch, wide, dg, steps: int):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def achievable_peaks(torch, steps: int = 10):
+    """Context for the fixed peaks: hipBLASLt on a dense 8192^3 bf16 GEMM, and
+    a 1 GiB device copy (read + write bytes over time)."""
+    dev = "cuda:0"
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    ms = time_events(torch, lambda: a @ b, steps)
+    del a, b
+    src = torch.empty(COPY_BYTES // 2, device=dev, dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    cms = time_events(torch, lambda: dst.copy_(src), steps)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"hipblaslt_8192cube_bf16_tflops": round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1),
+            "device_copy_GBps": round(2 * COPY_BYTES / (cms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
     """fp64 oracle on a seeded token sample, scaled to effective TFLOP/s."""
     import numpy as np
@@ -291,7 +324,7 @@ def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
     active = int(m[rows].sum())
     flops = 6.0 * w.d * w.G * active
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} of {w.T} tokens (seeded), fp64, {t:.1f} s; effective flops of the "
                       f"sampled tokens' active groups"}
 
@@ -410,7 +443,9 @@ def profile_plan(dg, steps: int):
     """(workload, kernel, dispatches) in the order `--profile --steps N` launches them."""
     n = 1 + 2 * steps  # warmup, timed and staged prefill steps
     pre = dg.LLAMA8B_PREFILL.name
-    plan = [(pre, "reorder", n), (pre, "gate_up", n), (pre, "down", n)]
+    # the reorder stage is the mask-bit packing and the per-group partition
+    plan = [(pre, "pack_mask_bits", n), (pre, "reorder_bits", n), (pre, "gate_up", n),
+            (pre, "down", n)]
     # T = 1 takes the whole-row VALU GEMVs; T = 16 the MFMA gate/up and the
     # split-K down with its reduce
     t1, t16 = dg.LLAMA8B_DECODE_T1.name, dg.LLAMA8B_DECODE_T16.name
@@ -421,7 +456,9 @@ def profile_plan(dg, steps: int):
              (t16, "decode_down_reduce", PROFILE_DECODE_CALLS)]
     for w in PROFILE_GEMMS(dg):
         if w.axis == "mn":
-            plan += [(w.name, "reorder", PROFILE_GEMM_CALLS), (w.name, "gemm_mn", PROFILE_GEMM_CALLS)]
+            plan += [(w.name, "pack_mask_bits", PROFILE_GEMM_CALLS),
+                     (w.name, "reorder_bits", PROFILE_GEMM_CALLS),
+                     (w.name, "gemm_mn", PROFILE_GEMM_CALLS)]
         else:
             plan += [(w.name, "pack_mask_bits", PROFILE_GEMM_CALLS),
                      (w.name, "down", PROFILE_GEMM_CALLS)]
@@ -445,6 +482,71 @@ def split_by_plan(plan, dispatches):
             out[(workload, kernel)] = [v for _, v in seq[pos:pos + n]]
             pos += n
     return out
+
+
+# flops of one MFMA instruction of each kernel (its instruction shape)
+MFMA_FLOPS = {"gate_up": 2 * 32 * 32 * 16, "down": 2 * 32 * 32 * 16, "gemm_mn": 2 * 32 * 32 * 16,
+              "decode_gate_up": 2 * 16 * 16 * 32, "decode_down_splitk": 2 * 16 * 16 * 32,
+              "router": 2 * 16 * 16 * 32, "router_small": 2 * 16 * 16 * 32}
+
+
+def work_closed_forms(dg):
+    """(workload, kernel) -> (algorithmic flops, flops the kernel is designed to execute)."""
+    pre = dg.LLAMA8B_PREFILL
+    A = pre.T * (pre.ngroups // 2)  # top-50% masks: exactly ng/2 groups per token
+    out = {(pre.name, "gate_up"): (4.0 * pre.d * pre.G * A, 4.0 * pre.d * pre.G * A),
+           (pre.name, "down"): (2.0 * pre.d * pre.G * A, 2.0 * pre.T * pre.d * pre.d_ff)}
+    for w in (dg.LLAMA8B_ATTN_Q, dg.LLAMA8B_ATTN_O, dg.LLAMA8B_DEPTH):
+        a = int(dg.make_gemm_mask(w).sum())
+        if w.axis == "mn":
+            out[(w.name, "gemm_mn")] = (2.0 * w.K * w.G * a, 2.0 * w.K * w.G * a)
+        else:
+            out[(w.name, "down")] = (2.0 * w.N * w.G * a, 2.0 * w.M * w.N * w.K)
+    t16 = dg.LLAMA8B_DECODE_T16
+    # 16 token columns per MFMA; every group is live at T = 16
+    out[(t16.name, "decode_gate_up")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
+    out[(t16.name, "decode_down_splitk")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
+    out[("llama3.1-8b-router-prefill", "router")] = (2.0 * 16384 * 4096 * 32,) * 2
+    out[("llama3.1-8b-router-decode-t1", "router_small")] = (2.0 * 16 * 4096 * 32,) * 2
+    return out
+
+
+def mfma_summary(directory, command, plan, split_fn):
+    """profiles/mfma_work_llama8b.md: MFMA instructions counted by rocprofv3 x
+    flops per instruction, against the closed forms of the work."""
+    from group_sparse_ffn_amd import datagen as dg
+    per_id = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != "SQ_INSTS_MFMA":
+                continue
+            k = next((kk for kk, v in KERNEL_SYMBOLS.items() if v in r["Kernel_Name"]), None)
+            if k is not None:
+                per_id.setdefault(k, []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    if not per_id:
+        return
+    split = split_fn(plan, per_id)
+    forms = work_closed_forms(dg)
+    lines = ["# MFMA work per launch: counted vs closed form", "",
+             "`SQ_INSTS_MFMA` from a rocprofv3 counter run of the command below, averaged over",
+             "each kernel's dispatches for the workload, times the flops of the kernel's MFMA",
+             "instruction (32x32x16 bf16 = 32768, 16x16x32 bf16 = 16384). `algorithmic` is the",
+             "method's work (active pairs only); `designed` is what the kernel is built to",
+             "execute (the down kernel runs the dense product; decode pads tokens to 16).", "",
+             "```", command.replace("PMC", "SQ_INSTS_MFMA"), "```", "",
+             "| kernel | workload | counted TFLOP | algorithmic TFLOP | designed TFLOP | counted / designed |",
+             "|---|---|---|---|---|---|"]
+    for workload, kernel, _ in plan:
+        v = split.get((workload, kernel), [])
+        if not v or (workload, kernel) not in forms or kernel not in MFMA_FLOPS:
+            continue
+        counted = sum(v) / len(v) * MFMA_FLOPS[kernel]
+        alg, des = forms[(workload, kernel)]
+        lines.append(f"| {kernel} | {workload} | {counted / 1e12:.4f} | {alg / 1e12:.4f} | "
+                     f"{des / 1e12:.4f} | {counted / des:.4f} |")
+    out = os.path.join(ROOT, "profiles", "mfma_work_llama8b.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
 
 
 def summarize(directory: str, command: str, steps: int):
@@ -485,6 +587,7 @@ def summarize(directory: str, command: str, steps: int):
         out = os.path.join(ROOT, "profiles", "kernel_trace_llama8b.md")
         open(out, "w").write("\n".join(lines) + "\n")
         print(f"wrote {out}")
+    mfma_summary(directory, command, plan, split_by_plan)
     per = {}     # counter -> kernel name -> values (KiB per dispatch), for the copy calibration
     per_id = {}  # counter -> kernel -> [(dispatch id, value)]
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
@@ -610,6 +713,7 @@ def main():
         call1.run()
         oms = time_events(torch, call1.run, max(5, args.steps // 2))
         del call1
+        line["achievable_peaks"] = achievable_peaks(torch)
         line["dense"] = {"ms": round(dms, 4), "impl": "torch bf16 matmul (hipBLASLt)",
                          "speedup": round(dms / r["ms"], 3),
                          "ideal_speedup": round(w.T * r["ng"] / r["A"], 3),

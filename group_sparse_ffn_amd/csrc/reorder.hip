@@ -117,8 +117,13 @@ __global__ __launch_bounds__(256) void pack_mask_bits_kernel(const uint8_t* __re
   const int w = (int)(idx / ng);
   const int t0 = 32 * w;
   const int n = min(32, T - t0);
+  // all 32 byte loads are issued before the first is used
+  uint8_t v[32];
+#pragma unroll
+  for (int b = 0; b < 32; ++b) v[b] = b < n ? mask[(size_t)(t0 + b) * ng + g] : 0;
   uint32_t bits = 0;
-  for (int b = 0; b < n; ++b) bits |= (mask[(size_t)(t0 + b) * ng + g] != 0 ? 1u : 0u) << b;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) bits |= (v[b] != 0 ? 1u : 0u) << b;
   maskbits[(size_t)g * words + w] = bits;
 }
 
