@@ -208,3 +208,39 @@ def test_ffn_many_groups_never_reads_skipped_h():
     _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], w.G)
     assert bool(torch.isfinite(Y.float()).all())
     assert rel_err(Y, Yref) <= TOL
+
+
+def _graph_replays_match(run_fn, out, eager, n=4):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_fn()
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(n):
+        out.fill_(3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from eager"
+    return g
+
+
+@pytest.mark.parametrize("axis", ["mn", "k"])
+def test_gemm_graph_replay_matches_eager(axis):
+    w = _w(700, 512, 512, 128, axis, "bernoulli", 0.5, wid=28)
+    inp = {k: v.to(DEV) for k, v in dg.make_gemm_inputs(w).items()}
+    fn = wide.gemm_mn if axis == "mn" else wide.gemm_k
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(wide.gemm_workspace_size(w.M, w.ngroups), dtype=torch.uint8, device=DEV)
+    fn(inp["A"], inp["B"], inp["mask"], w.G, C=C, workspace=ws)
+    torch.cuda.synchronize()
+    eager = C.clone()
+    g = _graph_replays_match(lambda: fn(inp["A"], inp["B"], inp["mask"], w.G, C=C, workspace=ws),
+                             C, eager)
+    # the mask is read on the device at replay time
+    inp["mask"].zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert bool((C == 0).all())

@@ -101,3 +101,26 @@ def test_router_t0_and_feeds_the_ffn():
     m0 = wide.router_forward(e, rw["W1"].to(DEV), rw["W2"].to(DEV), "silu")
     torch.cuda.synchronize()
     assert m0.shape == (0, w.ngroups)
+
+
+def test_router_graph_replay_matches_eager():
+    T, D, r, ng = 300, 1024, 32, 37
+    X, W1, W2 = (t.to(DEV) for t in inputs(21, T, D, r, ng))
+    mask = torch.empty((T, ng), dtype=torch.uint8, device=DEV)
+    logits = torch.empty((T, ng, 2), dtype=torch.float32, device=DEV)
+    wide.router_forward(X, W1, W2, "silu", mask=mask, logits=logits, return_logits=True)
+    torch.cuda.synchronize()
+    eager = mask.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            wide.router_forward(X, W1, W2, "silu", mask=mask, logits=logits, return_logits=True)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        mask.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(mask, eager), f"replay {i} differs from eager"
