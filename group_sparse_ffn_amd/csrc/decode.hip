@@ -85,8 +85,8 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*
 
 // Lists the groups (or 32-channel chunks) executed by some token into s_list
 // (ascending) and returns their number. Every thread of the block must call
-// it. `nitems` items; item i covers groups [glo(i), ghi(i)].
-template <int kThreads, class Range>
+// it. `nitems` items; item i covers groups [glo(i), ghi(i)]; 1 <= T <= kMaxT.
+template <int kThreads, int kMaxT, class Range>
 __device__ __forceinline__ int list_active(const uint8_t* __restrict__ mask, int T, int ng,
                                            int nitems, Range range, uint16_t* s_list,
                                            int* s_wave_cnt) {
@@ -99,12 +99,13 @@ __device__ __forceinline__ int list_active(const uint8_t* __restrict__ mask, int
     if (it < nitems) {
       int glo, ghi;
       range(it, glo, ghi);
-      // all T mask bytes are requested before any is tested (T <= 16)
+      // all mask bytes are requested before any is tested: token rows past
+      // T - 1 are clamped to T - 1 (T >= 1), which leaves the OR unchanged and
+      // keeps the loads out of branches
       for (int g = glo; g <= ghi; ++g) {
         uint32_t m = 0;
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-          if (t < T) m |= mask[(size_t)t * ng + g];
+        for (int t = 0; t < kMaxT; ++t) m |= mask[(size_t)min(t, T - 1) * ng + g];
         any |= m != 0;
       }
     }
@@ -149,7 +150,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int nact = list_active<kGuThreads>(
+  const int nact = list_active<kGuThreads, 16>(
       mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
   const int u = blockIdx.x;
   if (u >= nact * upg) {
@@ -199,9 +200,12 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
       pw[f + NF / 2] = Wu + (size_t)(c0 + 16 * f + r) * d + kbase;
     }
   }
+  // B operand column = token; columns past T - 1 repeat token T - 1's row
+  // (each output column depends on its own B column only, and those columns
+  // are never stored), so no load sits in a branch and the wait counts stay
+  // exact across the double buffer
   const int tok = lane & 15;
-  const uint16_t* px = (tok < T) ? X + (size_t)tok * d + kbase : nullptr;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const uint16_t* px = X + (size_t)min(tok, T - 1) * d + kbase;
 
   f32x4 acc[NF];
 #pragma unroll
@@ -211,13 +215,17 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   // batch b, so every wave keeps a batch of loads in flight while it computes.
   const int nb = nsub / kU;
   u32x4 aw[2][NF][kU], bx[2][kU];
+  // the scheduling barrier keeps a batch's loads together, ahead of the
+  // MFMAs that follow (the scheduler would otherwise sink them between those
+  // MFMAs, behind waits for the previous batch)
   auto load_batch = [&](int b, int set) {
 #pragma unroll
     for (int q = 0; q < kU; ++q) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16(pw[f] + 32 * (b * kU + q));
-      bx[set][q] = px ? ld16(px + 32 * (b * kU + q)) : zero;
+      bx[set][q] = ld16(px + 32 * (b * kU + q));
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto mma_batch = [&](int set) {
 #pragma unroll
@@ -228,16 +236,27 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
                                                          __builtin_bit_cast(bf16x8, bx[set][q]),
                                                          acc[f], 0, 0, 0);
   };
-  if (nb > 0) load_batch(0, 0);
-  for (int b = 0; b < nb; b += 2) {
-    if (b + 1 < nb) load_batch(b + 1, 1);
-    mma_batch(0);
-    if (b + 1 >= nb) break;
-    if (b + 2 < nb) load_batch(b + 2, 0);
-    mma_batch(1);
+  // (No load is issued under a condition inside the loop: the wait counts
+  // then stay exact, and the MFMAs of one batch wait only for that batch.)
+  if (nb > 0) {
+    load_batch(0, 0);
+    int b = 0;
+    for (; b + 2 < nb; b += 2) {
+      load_batch(b + 1, 1);
+      mma_batch(0);
+      load_batch(b + 2, 0);
+      mma_batch(1);
+    }
+    if (b + 1 < nb) {
+      load_batch(b + 1, 1);
+      mma_batch(0);
+      mma_batch(1);
+    } else {
+      mma_batch(0);
+    }
   }
   for (int s = nb * kU; s < nsub; ++s) {
-    const bf16x8 bv = __builtin_bit_cast(bf16x8, px ? ld16(px + 32 * s) : zero);
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(px + 32 * s));
 #pragma unroll
     for (int f = 0; f < NF; ++f)
       acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[f] + 32 * s)),
@@ -304,6 +323,9 @@ constexpr int kSkWaves = kSkThreads / 64;
 constexpr int kSkU = 4;  // chunks per batch per wave
 constexpr int kMaxChunks = 2048;  // d_ff / 32 limit
 
+// HALVES (G == 16): a live 32-channel chunk can hold a group that no token
+// executes; its H was never written, so those lanes use zeros instead.
+template <bool HALVES>
 __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G, float* __restrict__ part) {
@@ -319,22 +341,18 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   const int wave = tid >> 6;
 
   // 32-channel chunks whose group some token executes
-  const int nch = list_active<kSkThreads>(
+  const int nch = list_active<kSkThreads, 16>(
       mask, T, ng, d_ff / 32,
       [G](int c, int& lo, int& hi) {
         lo = (c * 32) / G;
         hi = (c * 32 + 31) / G;
       },
       s_chunks, s_wave_cnt);
-  // With G < 32 a live chunk can hold a group that no token executes; its H
-  // was never written, so those lanes use zeros instead of reading it.
-  const bool halves = G < 32;
-  if (halves) {
+  if (HALVES) {
     for (int g = tid; g < ng; g += kSkThreads) {
       uint32_t m = 0;
 #pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if (t < T) m |= mask[(size_t)t * ng + g];
+      for (int t = 0; t < 16; ++t) m |= mask[(size_t)min(t, T - 1) * ng + g];
       s_gact[g] = m != 0;
     }
     __syncthreads();
@@ -347,7 +365,8 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   const uint16_t* pw[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) pw[rb] = Wd + (size_t)(n0 + 16 * rb + (lane & 15)) * d_ff + koff;
-  const uint16_t* ph = (tok < T) ? H + (size_t)tok * d_ff + koff : nullptr;
+  // token columns past T - 1 repeat token T - 1 (never stored, see gate/up)
+  const uint16_t* ph = H + (size_t)min(tok, T - 1) * d_ff + koff;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc[4];
 #pragma unroll
@@ -358,8 +377,17 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   const int nb = mine / kSkU;
   u32x4 a[2][4][kSkU], bb[2][kSkU];
   auto chunk_k = [&](int i) { return (int)s_chunks[lo + wave + kSkWaves * i] * 32; };
-  auto h_load = [&](int k) {
-    return (ph && (!halves || s_gact[(k + koff) / G])) ? ld16(ph + k) : zero;
+  // H loads are unconditional (inside H's bounds). With HALVES, the lanes of
+  // a group no token executes get an all-zero AND mask, applied when the
+  // fragment is used, so nothing unwritten reaches the sums and no load or
+  // move of a loaded value sits in a branch.
+  uint32_t hm[2][kSkU];
+  auto h_mask = [&](int k) -> uint32_t {
+    return HALVES ? (s_gact[(k + koff) >> 4] ? 0xFFFFFFFFu : 0u) : 0xFFFFFFFFu;
+  };
+  auto masked = [](const u32x4& v, uint32_t m) {
+    const u32x4 mv = {m, m, m, m};
+    return __builtin_bit_cast(bf16x8, v & mv);
   };
   auto load_batch = [&](int b, int set) {
 #pragma unroll
@@ -367,29 +395,42 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
       const int k = chunk_k(b * kSkU + q);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) a[set][rb][q] = ld16(pw[rb] + k);
-      bb[set][q] = h_load(k);
+      bb[set][q] = ld16(ph + k);
+      hm[set][q] = h_mask(k);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the batch's loads stay together (see gate/up)
   };
   auto mma_batch = [&](int set) {
 #pragma unroll
-    for (int q = 0; q < kSkU; ++q)
+    for (int q = 0; q < kSkU; ++q) {
+      const bf16x8 hv = HALVES ? masked(bb[set][q], hm[set][q]) : __builtin_bit_cast(bf16x8, bb[set][q]);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
         acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[set][rb][q]),
-                                                          __builtin_bit_cast(bf16x8, bb[set][q]),
-                                                          acc[rb], 0, 0, 0);
+                                                          hv, acc[rb], 0, 0, 0);
+    }
   };
-  if (nb > 0) load_batch(0, 0);
-  for (int b = 0; b < nb; b += 2) {
-    if (b + 1 < nb) load_batch(b + 1, 1);
-    mma_batch(0);
-    if (b + 1 >= nb) break;
-    if (b + 2 < nb) load_batch(b + 2, 0);
-    mma_batch(1);
+  // (no load is issued under a condition inside the loop; see gate/up)
+  if (nb > 0) {
+    load_batch(0, 0);
+    int b = 0;
+    for (; b + 2 < nb; b += 2) {
+      load_batch(b + 1, 1);
+      mma_batch(0);
+      load_batch(b + 2, 0);
+      mma_batch(1);
+    }
+    if (b + 1 < nb) {
+      load_batch(b + 1, 1);
+      mma_batch(0);
+      mma_batch(1);
+    } else {
+      mma_batch(0);
+    }
   }
   for (int i = nb * kSkU; i < mine; ++i) {
     const int k = chunk_k(i);
-    const bf16x8 hv = __builtin_bit_cast(bf16x8, h_load(k));
+    const bf16x8 hv = HALVES ? masked(ld16(ph + k), h_mask(k)) : __builtin_bit_cast(bf16x8, ld16(ph + k));
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[rb] + k)),
@@ -445,14 +486,15 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
   constexpr int kJ = 8;  // 1 KB loads per row and k-block (4096 channels)
   const int ng = d_ff / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nact = list_active<kValuThreads>(
+  const int nact = list_active<kValuThreads, NT>(
       mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
   // X rows of the NT tokens (rows past T are zeros)
   const int cpr = d / 8;
   for (int e = tid; e < NT * cpr; e += kValuThreads) {
     const int t = e / cpr, c = e % cpr;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(s_x + t * d + 8 * c) = t < T ? ld16(X + (size_t)t * d + 8 * c) : z;
+    const u32x4 v = ld16(X + (size_t)min(t, T - 1) * d + 8 * c);
+    *(u32x4*)(s_x + t * d + 8 * c) = t < T ? v : z;
   }
   __syncthreads();
   const int nj = d / 512;
@@ -467,13 +509,14 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
 #pragma unroll
     for (int t = 0; t < NT; ++t) sg[t] = su[t] = 0.0f;
     for (int j0 = 0; j0 < nj; j0 += kJ) {
+      // blocks past the row's end re-read its last block (never used), so
+      // no load sits in a branch
       u32x4 vg[kJ], vu[kJ];
 #pragma unroll
       for (int j = 0; j < kJ; ++j) {
-        if (j0 + j < nj) {
-          vg[j] = ld16_nt(pg + 512 * (j0 + j));
-          vu[j] = ld16_nt(pu + 512 * (j0 + j));
-        }
+        const int jj = min(j0 + j, nj - 1);
+        vg[j] = ld16_nt(pg + 512 * jj);
+        vu[j] = ld16_nt(pu + 512 * jj);
       }
 #pragma unroll
       for (int j = 0; j < kJ; ++j) {
@@ -505,7 +548,8 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
   // groups no token executes: +0.0 over their channels (workgroup-strided)
   for (int g = blockIdx.x; g < ng; g += gridDim.x) {
     bool any = false;
-    for (int t = 0; t < T; ++t) any |= mask[(size_t)t * ng + g] != 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) any |= mask[(size_t)min(t, T - 1) * ng + g] != 0;
     if (any) continue;
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int e = tid; e < T * (G / 8); e += kValuThreads) {
@@ -528,7 +572,7 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
   constexpr int kBatch = 16;  // loads in flight per lane (a whole row of 256 live chunks)
   const int ng = d_ff / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = list_active<kValuThreads>(
+  const int nch = list_active<kValuThreads, NT>(
       mask, T, ng, d_ff / 32,
       [G](int c, int& lo, int& hi) {
         lo = (c * 32) / G;
@@ -542,10 +586,13 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
     const int ch = (int)s_chunks[j] * 32 + 8 * q;
     const int g = ch / G;
     bool live = false;
-    for (int tt = 0; tt < T; ++tt) live |= mask[(size_t)tt * ng + g] != 0;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) live |= mask[(size_t)min(tt, T - 1) * ng + g] != 0;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(s_h + t * stride + 32 * j + 8 * q) =
-        (t < T && live) ? ld16(H + (size_t)t * d_ff + ch) : z;
+    // an H fragment of a group no token executes may be unwritten: it is
+    // loaded (in bounds) and replaced by zeros, never summed
+    const u32x4 v = ld16(H + (size_t)min(t, T - 1) * d_ff + ch);
+    *(u32x4*)(s_h + t * stride + 32 * j + 8 * q) = (t < T && live) ? v : z;
   }
   __syncthreads();
   const int ninstr = (nch + 15) / 16;
@@ -558,11 +605,12 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
     for (int t = 0; t < NT; ++t) y[t] = 0.0f;
     for (int i0 = 0; i0 < ninstr; i0 += kBatch) {
       u32x4 w[kBatch];
+      // chunk slots past the list's end re-read its last chunk (never used),
+      // so no load sits in a branch
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const int j = 16 * (i0 + q) + (lane >> 2);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        w[q] = j < nch ? ld16_nt(pw + (int)s_chunks[j] * 32) : z;
+        const int j = min(16 * (i0 + q) + (lane >> 2), nch - 1);
+        w[q] = ld16_nt(pw + (int)s_chunks[j] * 32);
       }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
@@ -673,8 +721,15 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                          stream, H, Wd, mask, T, d, d_ff, G, Y);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(decode_down_splitk_kernel, dim3((d / kSkRows) * kDecodeDownSplit),
-                     dim3(kSkThreads), 0, stream, H, Wd, mask, T, d, d_ff, G, part);
+  // G is a multiple of 16: below 32 it is 16, the case whose chunks can
+  // straddle an executed and a skipped group
+  if (G % 16 != 0) return hipErrorInvalidValue;
+  if (G == 16)
+    hipLaunchKernelGGL(decode_down_splitk_kernel<true>, dim3((d / kSkRows) * kDecodeDownSplit),
+                       dim3(kSkThreads), 0, stream, H, Wd, mask, T, d, d_ff, G, part);
+  else
+    hipLaunchKernelGGL(decode_down_splitk_kernel<false>, dim3((d / kSkRows) * kDecodeDownSplit),
+                       dim3(kSkThreads), 0, stream, H, Wd, mask, T, d, d_ff, G, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_down_reduce_kernel, dim3((T * d / 4 + 255) / 256), dim3(256), 0, stream,

@@ -111,19 +111,22 @@ __global__ __launch_bounds__(kThreads) void reorder_kernel(const uint8_t* __rest
 __global__ __launch_bounds__(256) void pack_mask_bits_kernel(const uint8_t* __restrict__ mask,
                                                              int T, int ng, int words,
                                                              uint32_t* __restrict__ maskbits) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)ng * words) return;
-  const int g = (int)(idx % ng);
-  const int w = (int)(idx / ng);
+  const unsigned idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= (unsigned)ng * (unsigned)words) return;
+  const int g = (int)(idx % (unsigned)ng);
+  const int w = (int)(idx / (unsigned)ng);
   const int t0 = 32 * w;
   const int n = min(32, T - t0);
-  // all 32 byte loads are issued before the first is used
+  // Rows past T are clamped to the last row (so every load is in bounds and
+  // none is predicated: the 32 loads are all issued before the first is used)
+  // and their bits are cleared afterwards.
   uint8_t v[32];
 #pragma unroll
-  for (int b = 0; b < 32; ++b) v[b] = b < n ? mask[(size_t)(t0 + b) * ng + g] : 0;
+  for (int b = 0; b < 32; ++b) v[b] = mask[(size_t)min(t0 + b, T - 1) * ng + g];
   uint32_t bits = 0;
 #pragma unroll
   for (int b = 0; b < 32; ++b) bits |= (v[b] != 0 ? 1u : 0u) << b;
+  if (n < 32) bits &= (1u << n) - 1u;
   maskbits[(size_t)g * words + w] = bits;
 }
 
@@ -232,6 +235,7 @@ hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* m
   const int words = (T + 31) / 32;
   const long long n = (long long)ng * words;
   if (n == 0) return hipSuccess;
+  if (n > 0xFFFFFF00LL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_mask_bits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      mask, T, ng, words, maskbits);
   return hipGetLastError();
