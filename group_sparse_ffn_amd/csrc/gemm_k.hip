@@ -61,11 +61,25 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
   const int ng = d_ff / G;
   const bool table = ng <= kDownMaxGroups;
 
-  // the tile's mask words, group-major (zero past the last word)
+  // the tile's mask words, group-major (zero past the last word). All of a
+  // thread's loads are issued before the first store: indexes are clamped
+  // into the bit rows and words past the last one are masked to zero, so no
+  // load sits in a divergent branch.
   if (table) {
-    for (int e = tid; e < ng * 8; e += 512) {
+    constexpr int kTab = kDownMaxGroups * 8 / 512;
+    uint32_t v[kTab];
+#pragma unroll
+    for (int i = 0; i < kTab; ++i) {
+      if (512 * i >= ng * 8) break;
+      const int e = min(tid + 512 * i, ng * 8 - 1);
       const int g = e >> 3, wi = e & 7;
-      s_mw[e] = (w0 + wi < words) ? maskbits[(size_t)g * words + w0 + wi] : 0u;
+      v[i] = maskbits[(size_t)g * words + min(w0 + wi, words - 1)] &
+             (w0 + wi < words ? 0xFFFFFFFFu : 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kTab; ++i) {
+      if (512 * i >= ng * 8) break;
+      if (tid + 512 * i < ng * 8) s_mw[tid + 512 * i] = v[i];
     }
     __syncthreads();
   }
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
           const uint32_t* mw = maskbits + (size_t)g * words;
 #pragma unroll
           for (int wi = 0; wi < 8; ++wi)
-            if (w0 + wi < words) acc |= mw[w0 + wi];
+            acc |= mw[min(w0 + wi, words - 1)] & (w0 + wi < words ? 0xFFFFFFFFu : 0u);
         }
       }
       any = acc != 0;

@@ -10,25 +10,26 @@
 //   mask[t,g]    = logit[t,g,0] >= logit[t,g,1]
 //
 // The first map reads every activation byte once and is bound by HBM, so the
-// kernel is built to stream X: a workgroup owns 64 tokens and its four waves
+// kernel is built to stream X: a workgroup owns 64 tokens and its eight waves
 // split D; each wave reads 16-byte pieces of X in the layout of a
 // v_mfma_f32_16x16x32_bf16 operand (16 tokens x 32 channels per load) against
 // the r / 16 matching fragments of W1 (shared by every workgroup, served from
 // L2, each fragment used for all four 16-token blocks), with the loads of the next
 // batch in flight during the current MFMAs. The partial sums meet in LDS,
-// where the activation is applied; the second map (W2 staged in LDS a chunk
-// of groups at a time), the argmax and the mask bytes follow in the same
-// kernel (no logits round trip through memory unless the caller asks).
+// where the activation is applied; the second map (a small fp32 MFMA
+// product), the argmax and the mask bytes follow in the same kernel (no
+// logits round trip through memory unless the caller asks).
 #include "common.h"
 
 namespace wide {
 
 namespace {
 
-// Two shapes of workgroup: for many tokens, 4 waves over 64 tokens (every W1
-// fragment serves four 16-token blocks); for at most 16 tokens, 16 waves over
-// one block, so that the chain of dependent loads along D is 16 times shorter.
-constexpr int kRtGC = 64;  // groups whose W2 rows are staged in LDS at a time
+// Two shapes of workgroup: for many tokens, 8 waves over 64 tokens (every W1
+// fragment serves four 16-token blocks; measured against 4 and 16 waves and
+// 16- or 32-token workgroups); for at most 16 tokens, 16 waves over one
+// block, so that the chain of dependent loads along D is 16 times shorter.
+constexpr int kRtGC = 64;  // groups whose mask bytes gather in LDS at a time
 
 // X pieces are read in the MFMA operand layout (half of a 128-byte line per
 // load, the other half with the next), so they keep the default cache policy.
@@ -47,7 +48,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
                                             int act, uint8_t* __restrict__ mask,
                                             float* __restrict__ logits,
                                             float (*s_part)[16 * kRtRB][R],
-                                            float (*s_z)[R + 1], float (*s_w2)[2 * kRtGC]) {
+                                            float (*s_z)[R + 1], uint8_t (*s_mask)[kRtGC]) {
   constexpr int kRtTok = 16 * kRtRB;
   constexpr int kRtThreads = 64 * kRtWaves;
   constexpr int NF = R / 16;  // W1 fragments of 16 outputs
@@ -65,16 +66,19 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   const int s_lo = (wave * nsub_all) / kRtWaves;
   const int s_hi = ((wave + 1) * nsub_all) / kRtWaves;
   const int kbase = s_lo * 32 + 8 * (lane >> 4);
+  // A operand row = token; rows past T - 1 repeat token T - 1 (each output
+  // row depends on its own A row only, and those rows are never stored), so
+  // no load sits in a branch and the wait counts stay exact across the
+  // double buffer
   const uint16_t* px[kRtRB];
 #pragma unroll
   for (int b = 0; b < kRtRB; ++b) {
-    const int tok = t0 + 16 * b + (lane & 15);
-    px[b] = tok < T ? X + (size_t)tok * D + kbase : nullptr;
+    const int tok = min(t0 + 16 * b + (lane & 15), T - 1);
+    px[b] = X + (size_t)tok * D + kbase;
   }
   const uint16_t* pw[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) pw[f] = W1 + (size_t)(16 * f + (lane & 15)) * D + kbase;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc[kRtRB][NF];
 #pragma unroll
   for (int b = 0; b < kRtRB; ++b)
@@ -88,10 +92,12 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
     for (int q = 0; q < kU; ++q) {
       const int k = 32 * (bt * kU + q);
 #pragma unroll
-      for (int b = 0; b < kRtRB; ++b) ax[set][b][q] = px[b] ? rt_ld(px[b] + k) : zero;
+      for (int b = 0; b < kRtRB; ++b) ax[set][b][q] = rt_ld(px[b] + k);
 #pragma unroll
       for (int f = 0; f < NF; ++f) bw[set][f][q] = *(const u32x4*)(pw[f] + k);
     }
+    // keeps the batch's loads together, ahead of the MFMAs that follow
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto mma_batch = [&](int set) {
 #pragma unroll
@@ -104,18 +110,28 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
               __builtin_bit_cast(bf16x8, ax[set][b][q]), __builtin_bit_cast(bf16x8, bw[set][f][q]),
               acc[b][f], 0, 0, 0);
   };
-  if (nb > 0) load_batch(0, 0);
-  for (int bt = 0; bt < nb; bt += 2) {
-    if (bt + 1 < nb) load_batch(bt + 1, 1);
-    mma_batch(0);
-    if (bt + 1 >= nb) break;
-    if (bt + 2 < nb) load_batch(bt + 2, 0);
-    mma_batch(1);
+  // no load is issued under a condition inside the loop
+  if (nb > 0) {
+    load_batch(0, 0);
+    int bt = 0;
+    for (; bt + 2 < nb; bt += 2) {
+      load_batch(bt + 1, 1);
+      mma_batch(0);
+      load_batch(bt + 2, 0);
+      mma_batch(1);
+    }
+    if (bt + 1 < nb) {
+      load_batch(bt + 1, 1);
+      mma_batch(0);
+      mma_batch(1);
+    } else {
+      mma_batch(0);
+    }
   }
   for (int s = nb * kU; s < nsub; ++s) {
 #pragma unroll
     for (int b = 0; b < kRtRB; ++b) {
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, px[b] ? rt_ld(px[b] + 32 * s) : zero);
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, rt_ld(px[b] + 32 * s));
 #pragma unroll
       for (int f = 0; f < NF; ++f)
         acc[b][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -139,43 +155,53 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
     s_z[t][j] = router_act(a, act);
   }
 
-  // ---- logits, argmax and mask, kRtGC groups at a time with their W2 rows in
-  // LDS, transposed to [j][2 g + c] fp32. Thread (token tid % 32, phase
-  // tid / 32) holds its token's z in registers and takes every eighth group
-  // of the chunk; the 32 lanes of a phase read the same W2 pair (broadcast).
+  // ---- logits, argmax and mask: [tokens x 2 N_G] = z [tokens x R] . W2^T on
+  // v_mfma_f32_16x16x4_f32 (fp32 products and fp32 sums, like a scalar fma
+  // chain). Work items are (16-token block, 16-column block = 8 groups x 2
+  // classes). The sum over k is order-free, so the MFMA's k slot is permuted:
+  // lane group q = lane / 16 takes k = KQ q + kk in step kk, which gives every
+  // lane contiguous pieces of z and of a W2 row. Groups go kRtGC at a time;
+  // their mask bytes gather in LDS and leave as contiguous row segments.
+  constexpr int KQ = R / 4;
   const int ntok = min(kRtTok, T - t0);
-  const int my_t = tid % kRtTok, phase = tid / kRtTok;
-  constexpr int kPhases = kRtThreads / kRtTok;
+  const int q = lane >> 4, c16 = lane & 15;
   __syncthreads();  // s_z complete
-  float zr[R];
-#pragma unroll
-  for (int j = 0; j < R; ++j) zr[j] = s_z[my_t][j];
   for (int g0 = 0; g0 < ng; g0 += kRtGC) {
     const int gc = min(kRtGC, ng - g0);
-    __syncthreads();  // the previous chunk's rows consumed
-    for (int e = tid; e < 2 * gc * (R / 8); e += kRtThreads) {
-      const int row = e / (R / 8), c8 = e % (R / 8);
-      const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(W2 + (size_t)(2 * g0 + row) * R + 8 * c8));
+    const int nob = (gc + 7) / 8;  // 16-column blocks of the chunk
+    for (int it = wave; it < kRtRB * nob; it += kRtWaves) {
+      const int tb = it / nob, ob = it % nob;
+      const int col = 16 * ob + c16;  // chunk-local column: group col / 2, class col % 2
+      const bool colok = col < 2 * gc;
+      // W2 row of this column (row 2 g0 stands in past the chunk; zeroed)
+      const uint32_t* pw2 =
+          (const uint32_t*)(W2 + (size_t)(2 * g0 + (colok ? col : 0)) * R + KQ * q);
+      uint32_t wv[KQ / 2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s_w2[8 * c8 + i][row] = (float)v[i];
+      for (int i = 0; i < KQ / 2; ++i) wv[i] = colok ? pw2[i] : 0u;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) {
+        const uint32_t bits = (kk & 1) ? (wv[kk >> 1] & 0xFFFF0000u) : (wv[kk >> 1] << 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s_z[16 * tb + c16][KQ * q + kk],
+                                                   __builtin_bit_cast(float, bits), acc, 0, 0, 0);
+      }
+      // lane holds tokens 16 tb + 4 q + e of column col; lane ^ 1 holds the
+      // other class of the same group and tokens
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float other = __shfl_xor(acc[e], 1);
+        const int t = 16 * tb + 4 * q + e;
+        if (colok && (c16 & 1) == 0) s_mask[t][col >> 1] = acc[e] >= other ? 1 : 0;
+        if (logits && colok && t < ntok) logits[((size_t)(t0 + t) * ng + g0) * 2 + col] = acc[e];
+      }
     }
     __syncthreads();
-    if (my_t >= ntok) continue;
-    for (int gl = phase; gl < gc; gl += kPhases) {
-      float l0 = 0.0f, l1 = 0.0f;
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        const float2 w = *(const float2*)&s_w2[j][2 * gl];
-        l0 = fmaf(w.x, zr[j], l0);
-        l1 = fmaf(w.y, zr[j], l1);
-      }
-      const size_t o = (size_t)(t0 + my_t) * ng + g0 + gl;
-      mask[o] = l0 >= l1 ? 1 : 0;
-      if (logits) {
-        logits[2 * o] = l0;
-        logits[2 * o + 1] = l1;
-      }
+    for (int e = tid; e < ntok * gc; e += kRtThreads) {
+      const int t = e / gc, gl = e % gc;
+      mask[(size_t)(t0 + t) * ng + g0 + gl] = s_mask[t][gl];
     }
+    __syncthreads();  // s_mask is refilled by the next chunk
   }
 }
 
@@ -186,12 +212,12 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
       uint8_t* __restrict__ mask, float* __restrict__ logits) {                                \
     __shared__ float s_part[NW][16 * RB][R];                                                   \
     __shared__ float s_z[16 * RB][R + 1];                                                      \
-    __shared__ __attribute__((aligned(8))) float s_w2[R][2 * kRtGC];                           \
-    router_body<R, RB, NW>(X, W1, W2, T, D, ng, act, mask, logits, s_part, s_z, s_w2);         \
+    __shared__ uint8_t s_mask[16 * RB][kRtGC];                                                 \
+    router_body<R, RB, NW>(X, W1, W2, T, D, ng, act, mask, logits, s_part, s_z, s_mask);       \
   }
-WIDE_ROUTER_KERNEL(router_kernel_16, 16, 4, 4)
-WIDE_ROUTER_KERNEL(router_kernel_32, 32, 4, 4)
-WIDE_ROUTER_KERNEL(router_kernel_64, 64, 4, 4)
+WIDE_ROUTER_KERNEL(router_kernel_16, 16, 4, 8)
+WIDE_ROUTER_KERNEL(router_kernel_32, 32, 4, 8)
+WIDE_ROUTER_KERNEL(router_kernel_64, 64, 4, 8)
 WIDE_ROUTER_KERNEL(router_small_kernel_16, 16, 1, 16)
 WIDE_ROUTER_KERNEL(router_small_kernel_32, 32, 1, 16)
 WIDE_ROUTER_KERNEL(router_small_kernel_64, 64, 1, 16)
@@ -216,7 +242,7 @@ hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint1
                          mask, logits);
     return hipGetLastError();
   }
-  const dim3 grid((T + 63) / 64), block(256);
+  const dim3 grid((T + 63) / 64), block(512);
   if (r == 16)
     hipLaunchKernelGGL(router_kernel_16, grid, block, 0, stream, X, W1, W2, T, D, ng, act, mask,
                        logits);
