@@ -244,6 +244,92 @@ def bench_masked_gemms(torch, wide, dg, steps: int):
     return out
 
 
+def bench_baselines(torch, wide, dg, sizes=(2048, 4096), G: int = 128, p: float = 0.5):
+    """Dense GEMM, the naive gather-scatter pipelines, the grouped GEMM on
+    reordered masks and the fused kernels on M = N = K = S, for pruning along
+    M (one decision per row), N and K (G = 128, random masks with half of
+    every token's groups active; M axis: half of the rows).
+
+    Per implementation: ms per call, effective TFLOP/s (the active products'
+    flops; dense counts all of them), the bytes the call allocates at its peak
+    (for the fused call: nothing, its output and workspace are passed in) and,
+    for the naive pipelines, the traffic and materialized storage of the
+    pages' closed forms."""
+    from group_sparse_ffn_amd import baselines as bl
+    out = {}
+    dev = "cuda:0"
+    try:
+        a = torch.ones((4, 16), dtype=torch.bfloat16, device=dev)
+        b = torch.ones((2, 16, 16), dtype=torch.bfloat16, device=dev)
+        torch._grouped_mm(a, b, offs=torch.tensor([2, 4], dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+        use_gmm = True
+    except Exception:  # no grouped GEMM in this torch build for this device
+        use_gmm = False
+
+    def measure(fn, reps, graph):
+        fn()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        r = fn()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del r
+        # dense and fused replay from a graph (the pages' protocol); the naive
+        # and grouped pipelines read sizes back to the host, so they run eagerly
+        ms = graph_step_ms(torch, fn, reps) if graph else time_events(torch, fn, reps)
+        return ms, peak
+
+    for S in sizes:
+        M = N = K = S
+        for axis in ("m", "n", "k"):
+            log(f"baselines {axis}-axis {S}^3")
+            Gx = N if axis == "m" else G
+            w = dg.GemmWorkload(f"baseline-{axis}-{S}", 60 + S % 97, M=M, N=N, K=K, G=Gx,
+                                axis="k" if axis == "k" else "mn",
+                                mask_kind="bernoulli" if axis == "m" else "topk", density=p)
+            inp = dg.make_gemm_inputs(w)
+            act = int(inp["mask"].sum())
+            A, B, mask = (inp[k].to(dev) for k in ("A", "B", "mask"))
+            del inp
+            dens = act / mask.numel()
+            flops = 2.0 * M * N * K * dens
+            impls = {"dense": (lambda: A @ B.t(), 2.0 * M * N * K)}
+            if axis == "m":
+                impls["naive"] = (lambda: bl.naive_gemm_m(A, B, mask), flops)
+                C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(wide.gemm_workspace_size(M, 1), dtype=torch.uint8, device=dev)
+                impls["fused"] = (lambda: wide.gemm_mn(A, B, mask, N, C=C, workspace=ws), flops)
+            elif axis == "n":
+                impls["naive"] = (lambda: bl.naive_gemm_mn(A, B, mask, G), flops)
+                impls["grouped"] = (lambda: bl.grouped_gemm_mn(A, B, mask, G, use_gmm), flops)
+                C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(wide.gemm_workspace_size(M, N // G), dtype=torch.uint8, device=dev)
+                impls["fused"] = (lambda: wide.gemm_mn(A, B, mask, G, C=C, workspace=ws), flops)
+            else:
+                impls["naive"] = (lambda: bl.naive_gemm_k(A, B, mask, G), flops)
+                impls["grouped"] = (lambda: bl.grouped_gemm_k(A, B, mask, G, use_gmm), flops)
+                C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(wide.gemm_workspace_size(M, K // G), dtype=torch.uint8, device=dev)
+                impls["fused"] = (lambda: wide.gemm_k(A, B, mask, G, C=C, workspace=ws), flops)
+            row = {"M": M, "N": N, "K": K, "G": Gx, "density": round(dens, 4),
+                   "table4_traffic_bytes": int(2 * bl.traffic_elements(axis, M, N, K, dens)),
+                   "table4_materialized_bytes": int(2 * bl.materialized_elements(axis, M, N, K, dens))}
+            for name, (fn, fl) in impls.items():
+                eager = name in ("naive", "grouped")
+                ms, peak = measure(fn, 3 if eager else 20, not eager)
+                row[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                             "peak_alloc_bytes": int(peak), "timing": "eager" if eager else "graph"}
+                torch.cuda.empty_cache()
+            if "grouped" in row:
+                row["grouped"]["impl"] = "torch._grouped_mm" if use_gmm else "one torch.mm per group"
+            out[f"{axis}{S}"] = row
+            del A, B, mask, C, ws
+            torch.cuda.empty_cache()
+    return out
+
+
 def bench_router(torch, wide, dg, steps: int):
     """The bottleneck router (mask production) at the Llama3.1-8B FFN shape:
     D = 4096, r = 32, 112 groups, SiLU, for the prefill length and T = 1."""
@@ -643,6 +729,93 @@ def summarize(directory: str, command: str, steps: int):
         print(f"wrote {out}")
 
 
+BASELINE_PROFILE_S = 2048
+BASELINE_PROFILE_AXES = ("n", "k")
+
+
+def run_profile_baselines():
+    """Short run for rocprofv3 counters: one naive gather-scatter call per
+    axis at S^3, each bracketed by a marker kernel (a 4-element zeta, a name
+    nothing else here launches), then the calibration copy."""
+    import torch
+    from group_sparse_ffn_amd import baselines as bl
+    from group_sparse_ffn_amd import datagen as dg
+    dev = "cuda:0"
+    S, G = BASELINE_PROFILE_S, 128
+    marker_x = torch.full((4,), 2.0, device=dev)
+    for axis in BASELINE_PROFILE_AXES:
+        w = dg.GemmWorkload(f"baseline-{axis}-{S}", 60 + S % 97, M=S, N=S, K=S, G=G,
+                            axis="k" if axis == "k" else "mn", mask_kind="topk", density=0.5)
+        inp = {k: v.to(dev) for k, v in dg.make_gemm_inputs(w).items()}
+        fn = bl.naive_gemm_mn if axis == "n" else bl.naive_gemm_k
+        torch.cuda.synchronize()
+        torch.special.zeta(marker_x, marker_x)
+        C = fn(inp["A"], inp["B"], inp["mask"], G)
+        torch.special.zeta(marker_x, marker_x)
+        torch.cuda.synchronize()
+        del C, inp
+        torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"baseline profile run done: axes {BASELINE_PROFILE_AXES} at {S}^3, one {COPY_BYTES} B copy")
+
+
+def summarize_baselines(directory: str, command: str):
+    """Measured HBM bytes of each naive call (every dispatch between its two
+    markers, FETCH_SIZE + WRITE_SIZE scaled by the calibration copy) beside the
+    closed form of the pipeline's traffic."""
+    from group_sparse_ffn_amd import baselines as bl
+    rows = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            rows.setdefault(r["Counter_Name"], []).append(
+                (int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    lines = ["# Naive gather-scatter pipelines: measured HBM bytes vs the closed forms", "",
+             f"One call per axis at M = N = K = {BASELINE_PROFILE_S}, G = 128, half of every "
+             "token's groups active (top-k masks: the same count per token).",
+             "Measured: FETCH_SIZE and WRITE_SIZE summed over every dispatch between the call's",
+             f"two marker kernels, scaled by what each counter reads for a {COPY_BYTES}-byte",
+             "device copy in the same run. Closed form: the pipeline's data-tensor traffic",
+             "(masks, indices and offsets excluded), bf16 elements.", "",
+             "```", command.replace("PMC", "FETCH_SIZE"), command.replace("PMC", "WRITE_SIZE"), "```", "",
+             "The gather reads the weight matrix (S * S * 2 bytes, on-chip-cache sized) once per",
+             "token, so HBM sees two of the closed form's three p*M*N*K terms (the gathered",
+             "subset written, then read by the batched product); the last two columns drop",
+             "the gather's read.", "",
+             "| axis | kernels | fetch (GB) | write (GB) | measured (GB) | closed form (GB) | measured / closed form "
+             "| closed form without the gather's read (GB) | measured / that |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    meas = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        if counter not in rows:
+            raise SystemExit(f"no {counter} rows under {directory}")
+        rs = sorted(rows[counter])
+        copies = [v for _, n, v in rs if "copy" in n.lower() and v > COPY_BYTES / 1024 * 0.5]
+        if not copies:
+            raise SystemExit("the calibration copy is missing from the counter runs")
+        scale = (COPY_BYTES / 1024) / (sum(copies) / len(copies))
+        marks = [i for i, (_, n, _) in enumerate(rs) if "zeta" in n.lower()]
+        if len(marks) != 2 * len(BASELINE_PROFILE_AXES):
+            raise SystemExit(f"expected {2 * len(BASELINE_PROFILE_AXES)} markers, found {len(marks)}")
+        for a, axis in enumerate(BASELINE_PROFILE_AXES):
+            seg = rs[marks[2 * a] + 1:marks[2 * a + 1]]
+            meas.setdefault(axis, {})[counter] = (len(seg), sum(v for _, _, v in seg) * 1024 * scale)
+    S = BASELINE_PROFILE_S
+    for axis in BASELINE_PROFILE_AXES:
+        n, fetch = meas[axis]["FETCH_SIZE"]
+        _, write = meas[axis]["WRITE_SIZE"]
+        closed = 2 * bl.traffic_elements(axis, S, S, S, 0.5)
+        hbm = closed - 2 * 0.5 * S * S * S
+        lines.append(f"| {axis.upper()} | {n} | {fetch / 1e9:.2f} | {write / 1e9:.2f} | "
+                     f"{(fetch + write) / 1e9:.2f} | {closed / 1e9:.2f} | {(fetch + write) / closed:.3f} | "
+                     f"{hbm / 1e9:.2f} | {(fetch + write) / hbm:.3f} |")
+    out = os.path.join(ROOT, "profiles", f"traffic_naive_gather_scatter_{S}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -652,12 +825,18 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--profile-baselines", action="store_true")
+    ap.add_argument("--summarize-baselines", metavar="DIR")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.command, args.steps)
+        return
+    if args.summarize_baselines:
+        summarize_baselines(args.summarize_baselines, args.command)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the group-sparse FFN "
@@ -665,6 +844,9 @@ def main():
         sys.exit(2)
     if args.profile:
         run_profile(args.steps)
+        return
+    if args.profile_baselines:
+        run_profile_baselines()
         return
 
     import torch
@@ -726,6 +908,8 @@ def main():
     if not args.no_gemm:
         line["masked_gemms"] = bench_masked_gemms(torch, wide, dg, args.steps)
         line["router"] = bench_router(torch, wide, dg, args.steps)
+    if not args.no_baselines:
+        line["gemm_baselines"] = bench_baselines(torch, wide, dg)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         import oracle
