@@ -46,6 +46,8 @@ def _load():
         lib.oracle_gemm_k.restype = ctypes.c_int
         lib.oracle_router.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_int, p, i64, p, p]
         lib.oracle_router.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i64, p]
+        lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -178,3 +180,32 @@ def router(X, W1, W2, act: str = "silu", rows=None):
     if rc != 0:
         raise ValueError(f"oracle_router rejected its arguments (rc={rc})")
     return logits, mask
+
+
+def attention(Q, K, V, mask, Hq: int, Hk: int, rows=None):
+    """Head-group-pruned causal attention in fp64 -> O [n, Hq*dh] float64.
+
+    Q [T, Hq*dh], K and V [T, Hk*dh], mask [T, Hk] (group g = KV head g =
+    query heads g*Hq/Hk .. (g+1)*Hq/Hk - 1). For an active (t, g) and each of
+    its query heads h: O[t,h] = softmax_j<=t(Q[t,h].K[j,g] / sqrt(dh)) V[:,g];
+    a skipped pair gives +0.0.
+    """
+    q, k, v = _as_f32(Q), _as_f32(K), _as_f32(V)
+    m = _as_u8(mask)
+    T = q.shape[0]
+    if Hq <= 0 or Hk <= 0 or Hq % Hk or q.ndim != 2 or q.shape[1] % Hq:
+        raise ValueError("Q must be [T, Hq*dh] with Hk dividing Hq")
+    dh = q.shape[1] // Hq
+    if k.shape != (T, Hk * dh) or v.shape != (T, Hk * dh) or m.shape != (T, Hk):
+        raise ValueError("K and V must be [T, Hk*dh] and mask [T, Hk]")
+    if rows is None:
+        r, n = None, T
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = r.shape[0]
+    O = np.empty((n, Hq * dh), dtype=np.float64)
+    rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(m), T, Hq, Hk, dh,
+                                  None if r is None else _ptr(r), n, _ptr(O))
+    if rc != 0:
+        raise ValueError(f"oracle_attention rejected its arguments (rc={rc})")
+    return O

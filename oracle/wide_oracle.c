@@ -35,6 +35,7 @@
  * representable in float32); every product and sum is taken in double.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -220,6 +221,77 @@ int oracle_router(const float* X, const float* W1, const float* W2, int64_t T, i
     }
   }
   return ORACLE_OK;
+}
+
+/*
+ * Head-group-pruned causal attention for prefill: the attention side of the
+ * method (ai.info summary, "What gets pruned": the attention unit is a group
+ * of H_q/H_k query heads aligned with GQA, and each token keeps or skips each
+ * group; WIDE paper App. B "Implementation of Attention": a query tile of one
+ * query head, the head fixing its KV head and routing group, the softmax
+ * organised as in FlashAttention, the query side predicated and K/V dense).
+ * Readings taken where the text is silent: causal self-attention over one
+ * sequence (key j is valid for query t when j <= t), scale 1/sqrt(dh), group g
+ * = KV head g = query heads [g*H_q/H_k, (g+1)*H_q/H_k), and a skipped
+ * (token, group) pair has no output (+0.0 here):
+ *   for t and query head h with mask[t, g] != 0, g = h / (H_q/H_k):
+ *     s_j      = (Q[t,h,:] . K[j,g,:]) / sqrt(dh)          j = 0..t
+ *     O[t,h,:] = sum_j exp(s_j) V[j,g,:] / sum_j exp(s_j)
+ * (exp(s_j - max s) in both sums: the same ratio, without overflow).
+ * Q [T, H_q*dh], K and V [T, H_k*dh], mask [T, H_k]; O [nrows, H_q*dh] for the
+ * tokens listed in rows[0..nrows) (NULL: 0..nrows-1).
+ */
+int oracle_attention(const float* Q, const float* K, const float* V, const uint8_t* mask,
+                     int64_t T, int64_t Hq, int64_t Hk, int64_t dh, const int64_t* rows,
+                     int64_t nrows, double* O) {
+  if (!Q || !K || !V || !mask || !O || T < 0 || Hq <= 0 || Hk <= 0 || Hq % Hk != 0 || dh <= 0 ||
+      nrows < 0)
+    return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t t = rows ? rows[i] : i;
+    if (t < 0 || t >= T) return ORACLE_BAD_ARG;
+  }
+  const int64_t hpg = Hq / Hk;
+  const double scale = 1.0 / sqrt((double)dh);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t t = rows ? rows[i] : i;
+    double* s = (double*)malloc((size_t)(t + 1) * sizeof(double));
+    if (!s) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t g = h / hpg;
+      double* o = O + (i * Hq + h) * dh;
+      if (!mask[t * Hk + g]) {
+        for (int64_t e = 0; e < dh; ++e) o[e] = 0.0;
+        continue;
+      }
+      const float* q = Q + (t * Hq + h) * dh;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j <= t; ++j) {
+        const float* k = K + (j * Hk + g) * dh;
+        double d = 0.0;
+        for (int64_t e = 0; e < dh; ++e) d += (double)q[e] * (double)k[e];
+        s[j] = d * scale;
+        if (s[j] > mx) mx = s[j];
+      }
+      double z = 0.0;
+      for (int64_t e = 0; e < dh; ++e) o[e] = 0.0;
+      for (int64_t j = 0; j <= t; ++j) {
+        const double w = exp(s[j] - mx);
+        z += w;
+        const float* v = V + (j * Hk + g) * dh;
+        for (int64_t e = 0; e < dh; ++e) o[e] += w * (double)v[e];
+      }
+      for (int64_t e = 0; e < dh; ++e) o[e] /= z;
+    }
+    free(s);
+  }
+  return bad ? ORACLE_BAD_ARG : ORACLE_OK;
 }
 
 /* Number of OpenMP threads the oracle runs with (1 when built without OpenMP). */

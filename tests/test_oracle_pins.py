@@ -20,6 +20,7 @@ import os
 import mpmath
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from group_sparse_ffn_amd import datagen as dg
@@ -613,6 +614,157 @@ def test_router_pins_catch_planted_mistake(bug):
     results = {}
     for pin in ROUTER_PINS:
         if pin is rpin_mpmath:
+            continue
+        try:
+            results[pin.__name__] = bool(pin(fn))
+        except (ValueError, IndexError):
+            results[pin.__name__] = False
+    assert not all(results.values()), f"no pin caught '{bug}': {results}"
+
+
+# ----------------------------------------------------------------------------- attention
+# Head-group-pruned causal attention (ai.info summary, "What gets pruned";
+# WIDE paper App. B, "Implementation of Attention"). Pins: a hand-derived
+# fixture, torch's causal scaled-dot-product attention when every pair is
+# active, the closed forms of a zero query (prefix mean of V) and of the first
+# token (v0), skipped pairs giving exact zeros while every other pair is
+# unchanged, and 50-digit brute force.
+
+def attention_problem(seed, T, Hq, Hk, dh):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Q = rng.standard_normal((T, Hq * dh)).astype(np.float32)
+    K = rng.standard_normal((T, Hk * dh)).astype(np.float32)
+    V = rng.standard_normal((T, Hk * dh)).astype(np.float32)
+    return Q, K, V
+
+
+def oracle_attention_fn(Q, K, V, mask, Hq, Hk):
+    return oracle.attention(Q, K, V, mask, Hq, Hk)
+
+
+def apin_hand_fixture(fn):
+    f = json.load(open(os.path.join(GOLDEN, "attention_hand.json")))
+    Q, K, V = (np.array(f[k], np.float32) for k in ("Q", "K", "V"))
+    ok = True
+    for case in f["cases"]:
+        O = fn(Q, K, V, np.array(case["mask"], np.uint8), f["Hq"], f["Hk"])
+        ok &= np.allclose(O, np.array(case["O"]), rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+def apin_sdpa(fn):
+    T, Hq, Hk, dh = 37, 4, 2, 16
+    Q, K, V = attention_problem(21, T, Hq, Hk, dh)
+    O = fn(Q, K, V, np.ones((T, Hk), np.uint8), Hq, Hk)
+    q = torch.from_numpy(Q.astype(np.float64)).view(T, Hq, dh).transpose(0, 1)
+    k = torch.from_numpy(K.astype(np.float64)).view(T, Hk, dh).transpose(0, 1)
+    v = torch.from_numpy(V.astype(np.float64)).view(T, Hk, dh).transpose(0, 1)
+    k = k.repeat_interleave(Hq // Hk, dim=0).contiguous()
+    v = v.repeat_interleave(Hq // Hk, dim=0).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True)
+    ref = ref[0].transpose(0, 1).reshape(T, Hq * dh).numpy()
+    return bool(np.allclose(O, ref, rtol=0, atol=1e-10))
+
+
+def apin_zero_query_prefix_mean(fn):
+    T, Hq, Hk, dh = 20, 2, 2, 8
+    _, K, V = attention_problem(22, T, Hq, Hk, dh)
+    O = fn(np.zeros((T, Hq * dh), np.float32), K, V, np.ones((T, Hk), np.uint8), Hq, Hk)
+    v = V.astype(np.float64).reshape(T, Hk, dh)
+    mean = np.cumsum(v, axis=0) / np.arange(1, T + 1)[:, None, None]
+    return bool(np.allclose(O.reshape(T, Hq, dh), mean, rtol=0, atol=1e-12)
+                and np.array_equal(O.reshape(T, Hq, dh)[0], v[0]))
+
+
+def apin_skip_is_zero_and_local(fn):
+    T, Hq, Hk, dh = 30, 6, 3, 8
+    Q, K, V = attention_problem(23, T, Hq, Hk, dh)
+    full = fn(Q, K, V, np.ones((T, Hk), np.uint8), Hq, Hk).reshape(T, Hq, dh)
+    mask = (np.random.Generator(np.random.PCG64(5)).random((T, Hk)) < 0.5).astype(np.uint8)
+    O = fn(Q, K, V, mask, Hq, Hk).reshape(T, Hq, dh)
+    on = np.repeat(mask.astype(bool), Hq // Hk, axis=1)  # [T, Hq]
+    return bool(np.all(O[~on] == 0.0) and np.array_equal(O[on], full[on]))
+
+
+def apin_mpmath(fn):
+    mpmath.mp.dps = 50
+    T, Hq, Hk, dh = 3, 2, 1, 3
+    Q, K, V = attention_problem(24, T, Hq, Hk, dh)
+    O = fn(Q, K, V, np.ones((T, Hk), np.uint8), Hq, Hk).reshape(T, Hq, dh)
+    ok = True
+    sc = 1 / mpmath.sqrt(dh)
+    for t in range(T):
+        for h in range(Hq):
+            s = [mpmath.fsum(mpmath.mpf(float(Q[t, h * dh + e])) * mpmath.mpf(float(K[j, e]))
+                             for e in range(dh)) * sc for j in range(t + 1)]
+            w = [mpmath.exp(x) for x in s]
+            z = mpmath.fsum(w)
+            for e in range(dh):
+                ref = mpmath.fsum(w[j] * mpmath.mpf(float(V[j, e])) for j in range(t + 1)) / z
+                ok &= abs(float(ref) - O[t, h, e]) <= 1e-14
+    return bool(ok)
+
+
+ATTENTION_PINS = [apin_hand_fixture, apin_sdpa, apin_zero_query_prefix_mean,
+                  apin_skip_is_zero_and_local, apin_mpmath]
+
+
+@pytest.mark.parametrize("pin", ATTENTION_PINS, ids=lambda p: p.__name__)
+def test_oracle_attention_pins(pin):
+    assert pin(oracle_attention_fn)
+
+
+def test_oracle_attention_rows_subset_and_rejects_bad_arguments():
+    Q, K, V = attention_problem(25, 12, 4, 2, 8)
+    mask = np.ones((12, 2), np.uint8)
+    O = oracle.attention(Q, K, V, mask, 4, 2)
+    rows = [11, 0, 5]
+    assert np.array_equal(oracle.attention(Q, K, V, mask, 4, 2, rows=rows), O[rows])
+    with pytest.raises(ValueError):
+        oracle.attention(Q, K, V, mask, 4, 2, rows=[12])
+    with pytest.raises(ValueError):
+        oracle.attention(Q, K, V, mask, 4, 3)
+    with pytest.raises(ValueError):
+        oracle.attention(Q, K[:, :8], V, mask, 4, 2)
+
+
+def _np_attention(Q, K, V, mask, Hq, Hk, bug=None):
+    T = Q.shape[0]
+    dh = Q.shape[1] // Hq
+    q = Q.astype(np.float64).reshape(T, Hq, dh)
+    k = K.astype(np.float64).reshape(T, Hk, dh)
+    v = V.astype(np.float64).reshape(T, Hk, dh)
+    O = np.zeros((T, Hq, dh))
+    scale = 1.0 if bug == "no_scale" else 1.0 / np.sqrt(dh)
+    for t in range(T):
+        for h in range(Hq):
+            g = h % Hk if bug == "gqa_modulo" else h // (Hq // Hk)
+            if not mask[t, g] and bug != "mask_ignored":
+                continue
+            hi = T if bug == "not_causal" else (t if bug == "causal_off_by_one" else t + 1)
+            keys = [j for j in range(hi) if bug != "mask_on_keys" or mask[j, g]]
+            if not keys:
+                continue
+            s = np.array([q[t, h] @ k[j, g] for j in keys]) * scale
+            w = np.exp(s - s.max())
+            O[t, h] = (w[:, None] * v[keys, g]).sum(0) / w.sum()
+    return O.reshape(T, Hq * dh)
+
+
+ATTENTION_MUTANTS = ["not_causal", "causal_off_by_one", "no_scale", "gqa_modulo", "mask_ignored",
+                     "mask_on_keys"]
+
+
+def test_attention_pins_pass_on_correct_numpy_variant():
+    assert all(pin(_np_attention) for pin in ATTENTION_PINS if pin is not apin_mpmath)
+
+
+@pytest.mark.parametrize("bug", ATTENTION_MUTANTS)
+def test_attention_pins_catch_planted_mistake(bug):
+    fn = lambda *a: _np_attention(*a, bug=bug)  # noqa: E731
+    results = {}
+    for pin in ATTENTION_PINS:
+        if pin is apin_mpmath:
             continue
         try:
             results[pin.__name__] = bool(pin(fn))
