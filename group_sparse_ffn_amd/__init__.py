@@ -197,3 +197,47 @@ def router_forward(X, W1, W2, act: str = "silu", return_logits: bool = False, ma
         X.data_ptr(), W1.data_ptr(), W2.data_ptr(), T, D, r, ng, _ACTS[act], WIDE_BF16,
         mask.data_ptr(), None if logits is None else logits.data_ptr(), _stream_ptr(dev)))
     return (mask, logits) if return_logits else mask
+
+
+# ---------------------------------------------------------------- attention
+
+
+def attention_workspace_size(T: int, Hk: int, dh: int) -> int:
+    return int(_lib.load().wide_attention_workspace_size(T, Hk, dh))
+
+
+def attention_prefill(Q, K, V, mask, Hq: int, Hk: int, O=None, workspace=None,
+                      zero_inactive: bool = False):
+    """Head-group-pruned causal attention -> O [T, Hq*dh] bf16.
+
+    Q [T, Hq*dh], K and V [T, Hk*dh] bf16; mask [T, Hk] uint8 (group g = KV
+    head g and its Hq/Hk query heads). O is written where the token keeps the
+    group (and +0.0 elsewhere with zero_inactive; else left as it was).
+    """
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("mask", mask)):
+        _need_cuda(name, t)
+    if any(t.dtype != torch.bfloat16 for t in (Q, K, V)):
+        raise ValueError("Q, K and V must be bfloat16")
+    if mask.dtype != torch.uint8:
+        raise ValueError("mask must be uint8")
+    if Q.dim() != 2 or Hq <= 0 or Hk <= 0 or Hq % Hk or Q.shape[1] % Hq:
+        raise ValueError("expected Q [T, Hq*dh] with Hk dividing Hq")
+    T = Q.shape[0]
+    dh = Q.shape[1] // Hq
+    if K.shape != (T, Hk * dh) or V.shape != (T, Hk * dh) or mask.shape != (T, Hk):
+        raise ValueError("expected K and V [T, Hk*dh] and mask [T, Hk]")
+    dev = Q.device
+    if O is None:
+        # a fresh output holds +0.0 at skipped pairs either way
+        alloc = torch.empty if zero_inactive else torch.zeros
+        O = alloc((T, Hq * dh), dtype=Q.dtype, device=dev)
+    _need_cuda("O", O)
+    nbytes = attention_workspace_size(T, Hk, dh)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    flags = _lib.WIDE_ATTN_ZERO_INACTIVE if zero_inactive else 0
+    _lib.check(_lib.load().wide_attention_prefill(
+        Q.data_ptr(), K.data_ptr(), V.data_ptr(), mask.data_ptr(), T, Hq, Hk, dh, WIDE_BF16,
+        O.data_ptr(), flags, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_ptr(dev)))
+    return O

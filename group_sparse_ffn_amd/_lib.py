@@ -32,6 +32,7 @@ WIDE_FLAG_FORCE_DECODE = 0x2
 WIDE_ACT_IDENTITY = 0
 WIDE_ACT_RELU = 1
 WIDE_ACT_SILU = 2
+WIDE_ATTN_ZERO_INACTIVE = 1
 
 WIDE_STAGE_REORDER = 0
 WIDE_STAGE_GATE_UP = 1
@@ -56,6 +57,9 @@ SIGNATURES = {
     "wide_gemm_k": (ctypes.c_int, _GEMM_ARGS),
     "wide_router_forward": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                            ctypes.c_int, _p, _p, _p]),
+    "wide_attention_workspace_size": (_sz, [_i32, _i32, _i32]),
+    "wide_attention_prefill": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                              _p, ctypes.c_uint32, _p, _sz, _p]),
     "wide_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "wide_last_error": (ctypes.c_char_p, []),
     "wide_decode_max_t": (_i32, []),

@@ -67,6 +67,18 @@ hipError_t launch_reorder_from_bits(const uint32_t* maskbits, int T, int ng, int
 hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* maskbits,
                                  hipStream_t stream);
 
+// Keys of the transposed V copy per KV head (T rounded up to the key tile).
+int attention_tpad(int T);
+
+// Head-group-pruned causal attention, prefill (dh = 128): V is transposed into
+// Vt [Hk, dh, attention_tpad(T)], then one workgroup per (query tile of the
+// group's reordered tokens, query head). perm/counts: the reorder of the
+// [T, Hk] mask with tiles of 128.
+hipError_t launch_attention_prefill_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                         const int32_t* perm, const int32_t* counts, int T, int Hq,
+                                         int Hk, int dh, uint16_t* O, bool zero_inactive,
+                                         uint16_t* Vt, hipStream_t stream);
+
 // Largest group count for which the bf16 down kernel keeps the token tile's
 // mask bits in an LDS table (beyond it, it reads them from global memory).
 constexpr int kDownMaxGroups = 768;

@@ -383,6 +383,75 @@ WIDE_API wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* 
   return ok();
 }
 
+namespace {
+
+// Workspace of the attention: the reorder of the [T, Hk] mask (the masked
+// GEMMs' layout) followed by the transposed V copy [Hk, dh, Tpad] bf16.
+constexpr int kAttnTile = 128;
+
+struct AttnLayout {
+  GemmLayout g;
+  size_t vt, total;
+};
+
+AttnLayout attn_layout(int64_t T, int64_t Hk, int64_t dh) {
+  AttnLayout L{};
+  L.g = gemm_layout(T, Hk);
+  L.vt = L.g.total;
+  L.total = round_up(L.vt + (size_t)(Hk * dh) * (size_t)wide::attention_tpad((int)T) * 2, 256);
+  return L;
+}
+
+}  // namespace
+
+WIDE_API size_t wide_attention_workspace_size(int32_t T, int32_t Hk, int32_t dh) {
+  if (T < 0 || Hk < 1 || dh < 1) return 0;
+  return attn_layout(T, Hk, dh).total;
+}
+
+WIDE_API wide_status_t wide_attention_prefill(const void* Q, const void* K, const void* V,
+                                              const uint8_t* mask, int32_t T, int32_t Hq,
+                                              int32_t Hk, int32_t dh, wide_dtype_t dtype, void* O,
+                                              uint32_t flags, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  if (T != 0 && (!Q || !K || !V || !mask || !O))
+    return fail(WIDE_ERR_NULL, "Q, K, V, mask and O must be non-NULL when T > 0");
+  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (T < 0 || Hq < 1 || Hk < 1 || dh < 1 || Hq % Hk != 0)
+    return fail(WIDE_ERR_SHAPE, "need T >= 0, Hq, Hk, dh >= 1 and Hk dividing Hq (T=%d Hq=%d Hk=%d dh=%d)",
+                T, Hq, Hk, dh);
+  if ((flags & ~WIDE_ATTN_ZERO_INACTIVE) != 0) return fail(WIDE_ERR_SHAPE, "unknown flags 0x%x", flags);
+  if (dtype != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel runs bf16 only");
+  if (dh != 128) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel needs dh == 128 (dh=%d)", dh);
+  if ((int64_t)T * Hq * dh >= (1ll << 31))
+    return fail(WIDE_ERR_UNSUPPORTED, "T*Hq*dh must stay below 2^31");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(WIDE_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
+  const AttnLayout L = attn_layout(T, Hk, dh);
+  if (!workspace) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  if (T == 0) return ok();
+  char* ws = static_cast<char*>(workspace);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.g.perm);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.g.counts);
+  int32_t* padded = reinterpret_cast<int32_t*>(ws + L.g.padded);
+  uint32_t* maskbits = reinterpret_cast<uint32_t*>(ws + L.g.maskbits);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = wide::launch_pack_mask_bits(mask, T, Hk, maskbits, s);
+  if (e != hipSuccess) return hip_status(e, "mask pack launch");
+  e = wide::launch_reorder_from_bits(maskbits, T, Hk, kAttnTile, perm, counts, padded, s);
+  if (e != hipSuccess) return hip_status(e, "mask reorder launch");
+  e = wide::launch_attention_prefill_bf16(
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, counts, T, Hq, Hk, dh,
+      (uint16_t*)O, (flags & WIDE_ATTN_ZERO_INACTIVE) != 0,
+      reinterpret_cast<uint16_t*>(ws + L.vt), s);
+  if (e != hipSuccess) return hip_status(e, "attention launch");
+  return ok();
+}
+
 WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
                                            int32_t T, int32_t D, int32_t r, int32_t ngroups,
                                            wide_act_t act, wide_dtype_t dtype, uint8_t* mask,

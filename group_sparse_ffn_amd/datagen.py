@@ -292,3 +292,51 @@ def make_router_weights(seed: int, D: int, r: int, ngroups: int) -> dict:
     logits of a group are exchangeable, so about half the groups execute."""
     return {"W1": to_dtype(normal_f32(seed, (r, D), 1.0 / np.sqrt(D)), "bf16"),
             "W2": to_dtype(normal_f32(seed + 1, (2 * ngroups, r), 1.0 / np.sqrt(r)), "bf16")}
+
+
+# ---------------------------------------------------------------- attention
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """Head-group-pruned causal attention over one sequence: Q [T, Hq*dh],
+    K and V [T, Hk*dh], mask [T, Hk] (one routing group per KV head)."""
+    name: str
+    seed: int
+    T: int
+    Hq: int
+    Hk: int
+    dh: int = 128
+    mask_kind: str = "bernoulli"
+    density: float = 0.5
+
+
+# Llama3.1-8B attention at the prefill length: 32 query heads, 8 KV heads,
+# head dim 128 (G_attn = 4 * 128 = 512 channels of W_q per group).
+LLAMA8B_ATTN_PREFILL = AttnWorkload("llama3.1-8b-attention-prefill", 9, T=16384, Hq=32, Hk=8)
+
+
+def make_attention_inputs(w: AttnWorkload, T: Optional[int] = None,
+                          mask_kind: Optional[str] = None) -> dict:
+    """Q, K, V ~ N(0, 1) rounded to bf16 (scores q.k / sqrt(dh) ~ N(0, 1)) and
+    the [T, Hk] mask, as CPU tensors."""
+    T = w.T if T is None else T
+    kind = mask_kind or w.mask_kind
+    s = w.seed
+    out = {"Q": to_dtype(normal_f32(s, (T, w.Hq * w.dh)), "bf16"),
+           "K": to_dtype(normal_f32(s + 1, (T, w.Hk * w.dh)), "bf16"),
+           "V": to_dtype(normal_f32(s + 2, (T, w.Hk * w.dh)), "bf16")}
+    ms = s + 3
+    if kind == "bernoulli":
+        m = mask_bernoulli(T, w.Hk, w.density, ms)
+    elif kind == "topk":
+        m = mask_topk(T, w.Hk, int(round(w.Hk * w.density)), ms)
+    elif kind == "beta":
+        m = mask_beta(T, w.Hk, w.density, ms)
+    elif kind == "ones":
+        m = np.ones((T, w.Hk), dtype=np.uint8)
+    elif kind == "zeros":
+        m = np.zeros((T, w.Hk), dtype=np.uint8)
+    else:
+        raise ValueError(kind)
+    out["mask"] = torch.from_numpy(m)
+    return out

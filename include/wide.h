@@ -252,6 +252,49 @@ wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
                                   int32_t D, int32_t r, int32_t ngroups, wide_act_t act,
                                   wide_dtype_t dtype, uint8_t* mask, float* logits, void* stream);
 
+/*
+ * wide_attention_prefill - head-group-pruned causal attention for one sequence
+ * (ai.info summary, "What gets pruned": the attention unit is a GQA-aligned
+ * group of H_q/H_k query heads, and each token keeps or skips each group;
+ * WIDE paper App. B, "Implementation of Attention": query tiles of one query
+ * head are admitted, gathered, run through a dense K/V mainloop with the
+ * FlashAttention online softmax, and scattered back). Readings where the text
+ * is silent: causal (key j is valid for query t when j <= t), scale
+ * 1/sqrt(dh), group g = KV head g = query heads [g*H_q/H_k, (g+1)*H_q/H_k):
+ *   for t and query head h with mask[t, g] != 0:
+ *     O[t,h,:] = sum_{j<=t} softmax_j(Q[t,h,:].K[j,g,:] / sqrt(dh)) V[j,g,:]
+ * The mask is reordered on the device (the per-group stable partition of
+ * wide_reorder_masks, tiles of 128 queries); K and V stay dense.
+ *
+ *   Q     [T, Hq*dh]  device, bf16, read only (the W_q projection's output).
+ *   K, V  [T, Hk*dh]  device, bf16, read only.
+ *   mask  [T, Hk]     device, uint8, nonzero = the token keeps the head group.
+ *   O     [T, Hq*dh]  device, bf16, written at every (t, h) whose group t
+ *                     keeps; with WIDE_ATTN_ZERO_INACTIVE also +0.0 at the
+ *                     others, else they are left untouched (wide_gemm_k with
+ *                     G = (Hq/Hk)*dh never reads them for the W_o projection).
+ *   workspace         device, 256-byte aligned, at least
+ *                     wide_attention_workspace_size(T, Hk, dh) bytes; holds the
+ *                     reorder and a transposed copy of V. Overwritten; the
+ *                     caller owns it.
+ * P is rounded to bf16 before the P.V product (fp32 accumulation, fp32
+ * softmax statistics); O is rounded once to bf16.
+ * Sizes: T >= 0 (T == 0 enqueues nothing), Hk >= 1, Hq a multiple of Hk; the
+ * kernel needs dh == 128 and T*Hq*dh < 2^31, else WIDE_ERR_UNSUPPORTED. bf16
+ * only. Q, K, V and O 16-byte aligned. Asynchronous on `stream`; nothing is
+ * allocated and the host never waits, so the call can be captured in a graph.
+ * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_DTYPE, WIDE_ERR_ALIGN,
+ * WIDE_ERR_WORKSPACE, WIDE_ERR_UNSUPPORTED, WIDE_ERR_HIP.
+ */
+#define WIDE_ATTN_ZERO_INACTIVE 1u
+
+size_t wide_attention_workspace_size(int32_t T, int32_t Hk, int32_t dh);
+
+wide_status_t wide_attention_prefill(const void* Q, const void* K, const void* V,
+                                     const uint8_t* mask, int32_t T, int32_t Hq, int32_t Hk,
+                                     int32_t dh, wide_dtype_t dtype, void* O, uint32_t flags,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* wide_status_string(wide_status_t status);
 
