@@ -61,6 +61,8 @@ KERNEL_SOURCES = {
     "decode_down_reduce": ["decode.hip", "common.h"],
     "decode_gate_up_valu": ["decode.hip", "common.h"],
     "decode_down_valu": ["decode.hip", "common.h"],
+    "attention_prefill": ["attention.hip", "common.h"],
+    "attention_vt": ["attention.hip", "common.h"],
 }
 # substrings of the device symbol names of each kernel
 KERNEL_SYMBOLS = {
@@ -77,6 +79,8 @@ KERNEL_SYMBOLS = {
     "decode_down_reduce": "decode_down_reduce_kernel",
     "decode_gate_up_valu": "decode_gate_up_valu_kernel",
     "decode_down_valu": "decode_down_valu_kernel",
+    "attention_prefill": "attention_prefill_kernel",
+    "attention_vt": "attention_vt_kernel",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read + 1 GiB written
 
@@ -330,6 +334,61 @@ def bench_baselines(torch, wide, dg, sizes=(2048, 4096), G: int = 128, p: float 
     return out
 
 
+def bench_attention(torch, wide, dg, steps: int):
+    """Head-group-pruned causal attention at the Llama3.1-8B shape (T = 16384,
+    32 query heads, 8 KV heads, dh = 128, half of the (token, group) pairs
+    kept): the library call by graph replay, the same call on an all-ones mask,
+    and torch's SDPA (causal, GQA; flash or memory-efficient backend only) on
+    every head."""
+    w = dg.LLAMA8B_ATTN_PREFILL
+    dev = "cuda:0"
+    log(f"attention {w.name}")
+    inp = dg.make_attention_inputs(w)
+    alg, exe = attention_work(inp["mask"], w)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    O = torch.empty((w.T, w.Hq * w.dh), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(wide.attention_workspace_size(w.T, w.Hk, w.dh), dtype=torch.uint8, device=dev)
+    call = lambda m: wide.attention_prefill(d["Q"], d["K"], d["V"], m, w.Hq, w.Hk, O=O,  # noqa: E731
+                                            workspace=ws)
+    call(d["mask"])
+    ms = graph_step_ms(torch, lambda: call(d["mask"]), steps)
+    ones = torch.ones_like(d["mask"])
+    oms = graph_step_ms(torch, lambda: call(ones), max(5, steps // 2))
+    dense = 4.0 * w.dh * w.Hq * w.T * (w.T + 1) / 2
+    out = {"T": w.T, "Hq": w.Hq, "Hk": w.Hk, "dh": w.dh,
+           "density": round(float(inp["mask"].float().mean()), 4),
+           "ms": round(ms, 4), "active_tflop": round(alg / 1e12, 4),
+           "executed_mfma_tflop": round(exe / 1e12, 4),
+           "effective_tflops": round(alg / (ms * 1e-3) / 1e12, 1),
+           "frac_of_bf16_peak": round(alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "all_ones_mask_ms": round(oms, 4),
+           "all_ones_tflops": round(dense / (oms * 1e-3) / 1e12, 1),
+           "ideal_speedup": round(dense / alg, 3)}
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        q = d["Q"].view(w.T, w.Hq, w.dh).transpose(0, 1).contiguous()[None]
+        k = d["K"].view(w.T, w.Hk, w.dh).transpose(0, 1).contiguous()[None]
+        v = d["V"].view(w.T, w.Hk, w.dh).transpose(0, 1).contiguous()[None]
+
+        def sdpa():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                                        enable_gqa=True)
+        sdpa()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            sdpa()
+        sms = time_events(torch, sdpa, max(5, steps // 2))
+        out.update({"sdpa_ms": round(sms, 4), "sdpa_tflops": round(dense / (sms * 1e-3) / 1e12, 1),
+                    "speedup_vs_sdpa": round(sms / ms, 3)})
+        del q, k, v
+    except Exception as e:  # no fused SDPA backend for this device / build
+        out["sdpa_error"] = f"{type(e).__name__}: {str(e)[:200]}"
+    del d, O, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_router(torch, wide, dg, steps: int):
     """The bottleneck router (mask production) at the Llama3.1-8B FFN shape:
     D = 4096, r = 32, 112 groups, SiLU, for the prefill length and T = 1."""
@@ -507,6 +566,12 @@ def run_profile(steps: int):
             wide.router_forward(X, W1, W2, "silu")
         torch.cuda.synchronize()
         del X
+    aw = dg.LLAMA8B_ATTN_PREFILL
+    ad = {k: v.to("cuda:0") for k, v in dg.make_attention_inputs(aw).items()}
+    for _ in range(PROFILE_GEMM_CALLS):
+        wide.attention_prefill(ad["Q"], ad["K"], ad["V"], ad["mask"], aw.Hq, aw.Hk)
+    torch.cuda.synchronize()
+    del ad
     src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -550,6 +615,9 @@ def profile_plan(dg, steps: int):
                      (w.name, "down", PROFILE_GEMM_CALLS)]
     plan += [(ROUTER_WORKLOADS[16384], "router", PROFILE_GEMM_CALLS),
              (ROUTER_WORKLOADS[1], "router_small", PROFILE_GEMM_CALLS)]
+    aw = dg.LLAMA8B_ATTN_PREFILL.name
+    plan += [(aw, "pack_mask_bits", PROFILE_GEMM_CALLS), (aw, "reorder_bits", PROFILE_GEMM_CALLS),
+             (aw, "attention_vt", PROFILE_GEMM_CALLS), (aw, "attention_prefill", PROFILE_GEMM_CALLS)]
     return plan
 
 
@@ -573,7 +641,8 @@ def split_by_plan(plan, dispatches):
 # flops of one MFMA instruction of each kernel (its instruction shape)
 MFMA_FLOPS = {"gate_up": 2 * 32 * 32 * 16, "down": 2 * 32 * 32 * 16, "gemm_mn": 2 * 32 * 32 * 16,
               "decode_gate_up": 2 * 16 * 16 * 32, "decode_down_splitk": 2 * 16 * 16 * 32,
-              "router": 2 * 16 * 16 * 32, "router_small": 2 * 16 * 16 * 32}
+              "router": 2 * 16 * 16 * 32, "router_small": 2 * 16 * 16 * 32,
+              "attention_prefill": 2 * 32 * 32 * 16}
 
 
 def work_closed_forms(dg):
@@ -594,7 +663,28 @@ def work_closed_forms(dg):
     out[(t16.name, "decode_down_splitk")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
     out[("llama3.1-8b-router-prefill", "router")] = (2.0 * 16384 * 4096 * 32,) * 2
     out[("llama3.1-8b-router-decode-t1", "router_small")] = (2.0 * 16 * 4096 * 32,) * 2
+    aw = dg.LLAMA8B_ATTN_PREFILL
+    out[(aw.name, "attention_prefill")] = attention_work(dg.make_attention_inputs(aw)["mask"], aw)
     return out
+
+
+def attention_work(mask, w):
+    """(algorithmic flops, flops the kernel executes) of one attention call.
+
+    Algorithmic: 4 dh (t + 1) per kept (token t, query head). Executed: every
+    wave with a kept query runs 32 MFMAs of 32x32x16 per 64-key tile up to
+    its last query's position (queries in reordered order, 32 per wave)."""
+    import numpy as np
+    m = mask.numpy().astype(bool)
+    T = m.shape[0]
+    hpg = w.Hq // w.Hk
+    alg = exe = 0.0
+    for g in range(w.Hk):
+        toks = np.nonzero(m[:, g])[0]  # ascending: the partition's active prefix
+        alg += hpg * 4.0 * w.dh * float((toks + 1).sum())
+        last = toks[np.minimum(np.arange(31, len(toks) + 31, 32), len(toks) - 1)] if len(toks) else toks
+        exe += hpg * float((last // 64 + 1).sum()) * 32 * 2 * 32 * 32 * 16
+    return alg, exe
 
 
 def mfma_summary(directory, command, plan, split_fn):
@@ -908,6 +998,7 @@ def main():
     if not args.no_gemm:
         line["masked_gemms"] = bench_masked_gemms(torch, wide, dg, args.steps)
         line["router"] = bench_router(torch, wide, dg, args.steps)
+        line["attention"] = bench_attention(torch, wide, dg, args.steps)
     if not args.no_baselines:
         line["gemm_baselines"] = bench_baselines(torch, wide, dg)
     if not args.no_cpu:

@@ -58,6 +58,14 @@ __device__ __forceinline__ int key_of_row(int i) { return (i & ~12) | ((i & 4) <
 
 __device__ __forceinline__ u32x4 at_ld(const uint16_t* p) { return *(const u32x4*)p; }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int32_t* __restrict__ perm,
@@ -100,6 +108,10 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
   const int qpos = wrow < nrow ? prow[r0 + wrow] : -1;  // -1: no valid key anywhere
   const int wave_rows = min(32, nrow - wave * 32);
   const int wave_nkt = wave_rows > 0 ? prow[r0 + wave * 32 + wave_rows - 1] / kAtBK + 1 : 0;
+  // key tiles below this one are valid for every kept query of the wave (the
+  // wave's first row has its smallest position); only later tiles need the
+  // causal compare
+  const int wave_full = wave_rows > 0 ? (prow[r0 + wave * 32] + 1) / kAtBK : 0;
 
   // Q prologue: the B operand of S^T = K Q^T, k-step kk holds dims 16 kk + 8 hh .. + 7
   bf16x8 qf[kAtDh / 16];
@@ -171,22 +183,32 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
       }
     }
     // online softmax in base 2; element e of block b is key
-    // kt*64 + 32 b + 16 (e / 8) + 8 hh + e % 8
+    // kt*64 + 32 b + 16 (e / 8) + 8 hh + e % 8. Keys past a query's position
+    // get -inf (only on the wave's diagonal tiles).
+    if (kt >= wave_full) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * kAtBK + 32 * b + 16 * (e >> 3) + 8 * hh + (e & 7);
+          s[b][e] = key <= qpos ? s[b][e] * scale_log2 : -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) s[b] *= scale_log2;
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kt * kAtBK + 32 * b + 16 * (e >> 3) + 8 * hh + (e & 7);
-        const float v = key <= qpos ? s[b][e] * scale_log2 : -INFINITY;
-        s[b][e] = v;
-        mt = fmaxf(mt, v);
-      }
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[b][e]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
-    // alpha = 0 while nothing was valid (then O and l are still zero);
-    // a key that is not valid gets P = 0, also while m_new is -inf
-    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // While no key is valid the running max is -inf: the exponent base 0
+    // then gives exp2(-inf) = 0 for every P and for alpha, never NaN (O and l
+    // stay zero). A key that is not valid gets P = 0 the same way.
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float psum = 0.0f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -196,19 +218,22 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v0 = s[b][8 * c + 2 * i], v1 = s[b][8 * c + 2 * i + 1];
-          const float p0 = v0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v0 - m_new);
-          const float p1 = v1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v1 - m_new);
+          const float p0 = __builtin_amdgcn_exp2f(s[b][8 * c + 2 * i] - m_use);
+          const float p1 = __builtin_amdgcn_exp2f(s[b][8 * c + 2 * i + 1] - m_use);
           psum += p0 + p1;
-          w[i] = pack_bf16x2(p0, p1);
+          w[i] = cvt_bf16x2(p0, p1);
         }
         const u32x4 wv = {w[0], w[1], w[2], w[3]};
         pf[b][c] = __builtin_bit_cast(bf16x8, wv);
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // the running max of most queries stops moving after the first tiles:
+    // rescale only when some lane's max changed
+    if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int j = 0; j < kAtDh / 32; ++j) o[j] *= alpha;
+      for (int j = 0; j < kAtDh / 32; ++j) o[j] *= alpha;
+    }
     // O^T += V^T P^T: A = V^T rows (dims), B = P^T (k-step (b, c): keys 32 b + 16 c + 8 hh ..)
 #pragma unroll
     for (int j = 0; j < kAtDh / 32; ++j) {
@@ -248,8 +273,8 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // dims 32 j + 8 r + 4 hh .. + 3 of row wrow
-        const u32x2 v = {pack_bf16x2(o[j][4 * r] * inv, o[j][4 * r + 1] * inv),
-                         pack_bf16x2(o[j][4 * r + 2] * inv, o[j][4 * r + 3] * inv)};
+        const u32x2 v = {cvt_bf16x2(o[j][4 * r] * inv, o[j][4 * r + 1] * inv),
+                         cvt_bf16x2(o[j][4 * r + 2] * inv, o[j][4 * r + 3] * inv)};
         const int chunk = 4 * j + r;
         *(u32x2*)(smem + wrow * 256 + ((chunk ^ kswz(wrow)) << 4) + 8 * hh) = v;
       }
