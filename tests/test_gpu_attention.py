@@ -143,3 +143,31 @@ def test_attention_t0():
     O = wide.attention_prefill(e, kv, kv, torch.empty((0, 2), dtype=torch.uint8, device=DEV), 4, 2)
     torch.cuda.synchronize()
     assert O.shape == (0, 512)
+
+
+def test_attention_block_composes_with_the_masked_gemms():
+    """W_q (N-axis GEMM, G = (Hq/Hk)*dh) -> attention -> W_o (K-axis GEMM, same
+    G) on one head-group mask. The skipped O entries are left as planted NaN:
+    the K-axis GEMM never reads them, so Y stays finite and matches the
+    oracle's composition."""
+    T, Hq, Hk, dh, dm = 300, 8, 2, 128, 512
+    G = (Hq // Hk) * dh
+    w = dg.AttnWorkload("attn-block", 47, T=T, Hq=Hq, Hk=Hk)
+    inp = dg.make_attention_inputs(w)
+    X = dg.to_dtype(dg.normal_f32(48, (T, dm)), "bf16")
+    Wq = dg.to_dtype(dg.normal_f32(49, (Hq * dh, dm), dm ** -0.5), "bf16")
+    Wo = dg.to_dtype(dg.normal_f32(50, (dm, Hq * dh), (Hq * dh) ** -0.5), "bf16")
+    mask = inp["mask"]
+    d = {"X": X.to(DEV), "Wq": Wq.to(DEV), "Wo": Wo.to(DEV), "K": inp["K"].to(DEV),
+         "V": inp["V"].to(DEV), "mask": mask.to(DEV)}
+    Q = wide.gemm_mn(d["X"], d["Wq"], d["mask"], G)
+    O = torch.full((T, Hq * dh), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide.attention_prefill(Q, d["K"], d["V"], d["mask"], Hq, Hk, O=O)
+    Y = wide.gemm_k(O, d["Wo"], d["mask"], G)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y.float()).all())
+    Qr = oracle.gemm_mn(X, Wq, mask, G)
+    Or = oracle.attention(Qr.astype(np.float32), inp["K"], inp["V"], mask, Hq, Hk)
+    Yr = oracle.gemm_k(Or.astype(np.float32), Wo, mask, G)
+    # three bf16 roundings in a row (Q, O, Y)
+    assert rel_err(Y, Yr) <= 3e-2
