@@ -384,9 +384,54 @@ def bench_attention(torch, wide, dg, steps: int):
         del q, k, v
     except Exception as e:  # no fused SDPA backend for this device / build
         out["sdpa_error"] = f"{type(e).__name__}: {str(e)[:200]}"
+    out["decode"] = bench_attention_decode(torch, wide, d, w, steps)
     del d, O, ws
     torch.cuda.empty_cache()
     return out
+
+
+def bench_attention_decode(torch, wide, d, w, steps: int):
+    """One decoding step over the T-token cache (query at position T - 1),
+    half of the KV groups kept, against every group kept and torch's SDPA for
+    one query. A graph of 16 calls is replayed (the binding's host-side checks
+    would otherwise dominate); bytes = the kept groups' K and V rows."""
+    dev = "cuda:0"
+    q = d["Q"][w.T - 1].contiguous()
+    keep = torch.tensor([1, 0] * (w.Hk // 2) + [1] * (w.Hk % 2), dtype=torch.uint8, device=dev)
+    ones = torch.ones_like(keep)
+    O = torch.empty((w.Hq * w.dh,), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(wide.attention_decode_workspace_size(w.T, w.Hq, w.dh), dtype=torch.uint8,
+                     device=dev)
+    res = {}
+    for name, m in (("half_groups", keep), ("all_groups", ones)):
+        call = lambda: wide.attention_decode(q, d["K"], d["V"], m, w.Hq, w.Hk, O=O,  # noqa: E731
+                                             workspace=ws)
+        call()
+
+        def calls16():
+            for _ in range(16):
+                call()
+        us = graph_step_ms(torch, calls16, max(steps, 10)) / 16 * 1e3
+        nbytes = int(m.sum()) * 2 * w.T * w.dh * 2
+        res[name] = {"us": round(us, 2), "kv_bytes": nbytes,
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        qq = q.view(1, w.Hq, 1, w.dh)
+        k = d["K"].view(w.T, w.Hk, w.dh).transpose(0, 1).contiguous()[None]
+        v = d["V"].view(w.T, w.Hk, w.dh).transpose(0, 1).contiguous()[None]
+
+        def sdpa():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                return torch.nn.functional.scaled_dot_product_attention(qq, k, v, enable_gqa=True)
+        sdpa()
+        torch.cuda.synchronize()
+        res["sdpa_us"] = round(time_events(torch, sdpa, max(steps, 10)) * 1e3, 2)
+        del k, v
+    except Exception as e:
+        res["sdpa_error"] = f"{type(e).__name__}: {str(e)[:200]}"
+    return res
 
 
 def bench_router(torch, wide, dg, steps: int):

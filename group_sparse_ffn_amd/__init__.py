@@ -241,3 +241,40 @@ def attention_prefill(Q, K, V, mask, Hq: int, Hk: int, O=None, workspace=None,
         O.data_ptr(), flags, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream_ptr(dev)))
     return O
+
+
+def attention_decode_workspace_size(T: int, Hq: int, dh: int) -> int:
+    return int(_lib.load().wide_attention_decode_workspace_size(T, Hq, dh))
+
+
+def attention_decode(q, K, V, mask, Hq: int, Hk: int, O=None, workspace=None,
+                     zero_inactive: bool = False):
+    """One decoding step: q [Hq*dh] (position T - 1) over the cache K, V
+    [T, Hk*dh]; mask [Hk] uint8. Returns O [Hq*dh] bf16 (kept heads written;
+    +0.0 elsewhere with zero_inactive or on a fresh output)."""
+    for name, t in (("q", q), ("K", K), ("V", V), ("mask", mask)):
+        _need_cuda(name, t)
+    if any(t.dtype != torch.bfloat16 for t in (q, K, V)):
+        raise ValueError("q, K and V must be bfloat16")
+    if mask.dtype != torch.uint8:
+        raise ValueError("mask must be uint8")
+    if q.dim() != 1 or Hq <= 0 or Hk <= 0 or Hq % Hk or q.shape[0] % Hq:
+        raise ValueError("expected q [Hq*dh] with Hk dividing Hq")
+    dh = q.shape[0] // Hq
+    T = K.shape[0]
+    if K.shape != (T, Hk * dh) or V.shape != (T, Hk * dh) or mask.shape != (Hk,):
+        raise ValueError("expected K and V [T, Hk*dh] and mask [Hk]")
+    dev = q.device
+    if O is None:
+        alloc = torch.empty if zero_inactive else torch.zeros
+        O = alloc((Hq * dh,), dtype=q.dtype, device=dev)
+    _need_cuda("O", O)
+    nbytes = attention_decode_workspace_size(T, Hq, dh)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    flags = _lib.WIDE_ATTN_ZERO_INACTIVE if zero_inactive else 0
+    _lib.check(_lib.load().wide_attention_decode(
+        q.data_ptr(), K.data_ptr(), V.data_ptr(), mask.data_ptr(), T, Hq, Hk, dh, WIDE_BF16,
+        O.data_ptr(), flags, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_ptr(dev)))
+    return O

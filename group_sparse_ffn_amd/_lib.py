@@ -60,6 +60,9 @@ SIGNATURES = {
     "wide_attention_workspace_size": (_sz, [_i32, _i32, _i32]),
     "wide_attention_prefill": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                               _p, ctypes.c_uint32, _p, _sz, _p]),
+    "wide_attention_decode_workspace_size": (_sz, [_i32, _i32, _i32]),
+    "wide_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                             _p, ctypes.c_uint32, _p, _sz, _p]),
     "wide_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "wide_last_error": (ctypes.c_char_p, []),
     "wide_decode_max_t": (_i32, []),

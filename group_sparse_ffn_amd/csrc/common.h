@@ -79,6 +79,16 @@ hipError_t launch_attention_prefill_bf16(const uint16_t* Q, const uint16_t* K, c
                                          int Hk, int dh, uint16_t* O, bool zero_inactive,
                                          uint16_t* Vt, hipStream_t stream);
 
+// One decoding step of the head-group-pruned attention (dh = 128, Hq/Hk in
+// {1, 2, 4, 8}): per (128-key split, kept KV group) fp32 partials into `part`
+// (attention_decode_part_floats(T, Hq) floats), then a per-head merge.
+int attention_decode_splits(int T);
+size_t attention_decode_part_floats(int T, int Hq);
+hipError_t launch_attention_decode_bf16(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                                        const uint8_t* mask, int T, int Hq, int Hk, int dh,
+                                        uint16_t* O, bool zero_inactive, float* part,
+                                        hipStream_t stream);
+
 // Largest group count for which the bf16 down kernel keeps the token tile's
 // mask bits in an LDS table (beyond it, it reads them from global memory).
 constexpr int kDownMaxGroups = 768;

@@ -452,6 +452,44 @@ WIDE_API wide_status_t wide_attention_prefill(const void* Q, const void* K, cons
   return ok();
 }
 
+WIDE_API size_t wide_attention_decode_workspace_size(int32_t T, int32_t Hq, int32_t dh) {
+  if (T < 1 || Hq < 1 || dh != 128) return 0;
+  return round_up(wide::attention_decode_part_floats(T, Hq) * 4, 256);
+}
+
+WIDE_API wide_status_t wide_attention_decode(const void* q, const void* K, const void* V,
+                                             const uint8_t* mask, int32_t T, int32_t Hq,
+                                             int32_t Hk, int32_t dh, wide_dtype_t dtype, void* O,
+                                             uint32_t flags, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  if (!q || !K || !V || !mask || !O) return fail(WIDE_ERR_NULL, "q, K, V, mask and O must be non-NULL");
+  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (T < 1 || Hq < 1 || Hk < 1 || dh < 1 || Hq % Hk != 0)
+    return fail(WIDE_ERR_SHAPE, "need T >= 1, Hq, Hk, dh >= 1 and Hk dividing Hq (T=%d Hq=%d Hk=%d dh=%d)",
+                T, Hq, Hk, dh);
+  if ((flags & ~WIDE_ATTN_ZERO_INACTIVE) != 0) return fail(WIDE_ERR_SHAPE, "unknown flags 0x%x", flags);
+  if (dtype != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel runs bf16 only");
+  const int hpg = Hq / Hk;
+  if (dh != 128 || (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8))
+    return fail(WIDE_ERR_UNSUPPORTED, "the decode kernel needs dh == 128 and Hq/Hk in {1, 2, 4, 8} (dh=%d Hq/Hk=%d)",
+                dh, hpg);
+  if ((int64_t)T * Hk * dh >= (1ll << 31)) return fail(WIDE_ERR_UNSUPPORTED, "T*Hk*dh must stay below 2^31");
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(WIDE_ERR_ALIGN, "q, K, V and O must be 16-byte aligned");
+  const size_t need = wide_attention_decode_workspace_size(T, Hq, dh);
+  if (!workspace) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const hipError_t e = wide::launch_attention_decode_bf16(
+      (const uint16_t*)q, (const uint16_t*)K, (const uint16_t*)V, mask, T, Hq, Hk, dh, (uint16_t*)O,
+      (flags & WIDE_ATTN_ZERO_INACTIVE) != 0, static_cast<float*>(workspace),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "attention decode launch");
+  return ok();
+}
+
 WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
                                            int32_t T, int32_t D, int32_t r, int32_t ngroups,
                                            wide_act_t act, wide_dtype_t dtype, uint8_t* mask,

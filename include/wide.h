@@ -295,6 +295,38 @@ wide_status_t wide_attention_prefill(const void* Q, const void* K, const void* V
                                      int32_t dh, wide_dtype_t dtype, void* O, uint32_t flags,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * wide_attention_decode - one decoding step of the head-group-pruned attention
+ * (WIDE paper App. B, "Implementation of Attention": for decoding the routing
+ * is checked directly, without mask reordering, and the softmax is split over
+ * the keys): the new token's query at position T - 1 attends to the T cached
+ * keys 0..T-1 (its own included), the definition of wide_attention_prefill at
+ * query row T - 1:
+ *   for query head h with mask[g] != 0, g = h / (Hq/Hk):
+ *     O[h,:] = sum_{j<T} softmax_j(q[h,:].K[j,g,:] / sqrt(dh)) V[j,g,:]
+ * A group the token skips costs nothing: its K/V rows are never read.
+ *
+ *   q     [Hq*dh]     device, bf16, read only.
+ *   K, V  [T, Hk*dh]  device, bf16, read only (the cache, new token included).
+ *   mask  [Hk]        device, uint8, nonzero = the token keeps the head group.
+ *   O     [Hq*dh]     device, bf16, written at kept heads (and +0.0 at the
+ *                     others with WIDE_ATTN_ZERO_INACTIVE, else untouched).
+ *   workspace         device, 256-byte aligned, at least
+ *                     wide_attention_decode_workspace_size(T, Hq, dh) bytes:
+ *                     the fp32 partials of the key splits.
+ * fp32 scores, softmax statistics and sums from bf16 operands; O rounded once.
+ * Sizes: T >= 1, Hk >= 1, Hq a multiple of Hk; the kernel needs dh == 128 and
+ * Hq/Hk in {1, 2, 4, 8}, else WIDE_ERR_UNSUPPORTED. bf16 only; q, K, V, O
+ * 16-byte aligned. Asynchronous, allocation-free, capturable in a graph.
+ * Errors: as wide_attention_prefill.
+ */
+size_t wide_attention_decode_workspace_size(int32_t T, int32_t Hq, int32_t dh);
+
+wide_status_t wide_attention_decode(const void* q, const void* K, const void* V,
+                                    const uint8_t* mask, int32_t T, int32_t Hq, int32_t Hk,
+                                    int32_t dh, wide_dtype_t dtype, void* O, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* wide_status_string(wide_status_t status);
 

@@ -171,3 +171,49 @@ def test_attention_block_composes_with_the_masked_gemms():
     Yr = oracle.gemm_k(Or.astype(np.float32), Wo, mask, G)
     # three bf16 roundings in a row (Q, O, Y)
     assert rel_err(Y, Yr) <= 3e-2
+
+
+def decode_ref(inp, mask_row, Hq, Hk):
+    """The oracle's causal definition at query row T - 1 with this step's mask."""
+    T = inp["K"].shape[0]
+    m = torch.zeros((T, Hk), dtype=torch.uint8)
+    m[T - 1] = mask_row
+    return oracle.attention(inp["Q"], inp["K"], inp["V"], m, Hq, Hk, rows=[T - 1])[0]
+
+
+@pytest.mark.parametrize("T,Hq,Hk", [(1, 4, 4), (2, 8, 2), (127, 4, 1), (128, 8, 8), (129, 16, 2),
+                                     (1000, 32, 8), (16384, 32, 8), (300, 64, 8)])
+def test_attention_decode_matches_oracle(T, Hq, Hk):
+    w = dg.AttnWorkload(f"dec-{T}", 60 + T, T=T, Hq=Hq, Hk=Hk)
+    inp = dg.make_attention_inputs(w)
+    rng = np.random.Generator(np.random.PCG64(T))
+    mask_row = torch.from_numpy((rng.random(Hk) < 0.6).astype(np.uint8))
+    mask_row[rng.integers(0, Hk)] = 1  # at least one kept group
+    q = inp["Q"][T - 1].contiguous()
+    O = torch.full((Hq * 128,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide.attention_decode(q.to(DEV), inp["K"].to(DEV), inp["V"].to(DEV), mask_row.to(DEV), Hq, Hk,
+                          O=O)
+    torch.cuda.synchronize()
+    ref = decode_ref(inp, mask_row, Hq, Hk)
+    on = mask_row.bool().repeat_interleave((Hq // Hk) * 128)
+    Oc = O.cpu()
+    assert bool(torch.isfinite(Oc[on].float()).all()) and bool(torch.isnan(Oc[~on].float()).all())
+    err = np.abs(Oc.float().numpy().astype(np.float64) - ref)[on.numpy()]
+    assert err.max() / np.abs(ref[on.numpy()]).max() <= TOL
+
+
+def test_attention_decode_equals_prefill_last_row_and_zero_inactive():
+    T, Hq, Hk = 513, 8, 2
+    w = dg.AttnWorkload("dec-vs-pre", 71, T=T, Hq=Hq, Hk=Hk, mask_kind="ones")
+    inp = {k: v.to(DEV) for k, v in dg.make_attention_inputs(w).items()}
+    Op = wide.attention_prefill(inp["Q"], inp["K"], inp["V"], inp["mask"], Hq, Hk)
+    mask_row = torch.tensor([1, 0], dtype=torch.uint8, device=DEV)
+    Od = torch.full((Hq * 128,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide.attention_decode(inp["Q"][T - 1].contiguous(), inp["K"], inp["V"], mask_row, Hq, Hk, O=Od,
+                          zero_inactive=True)
+    torch.cuda.synchronize()
+    half = (Hq // Hk) * 128
+    assert bool((Od[half:] == 0).all())
+    # the two paths round differently (P to bf16 in prefill); both are within the bar
+    a, b = Od[:half].float(), Op[T - 1, :half].float()
+    assert float((a - b).abs().max() / b.abs().max()) <= 2 * TOL
