@@ -225,3 +225,65 @@ def test_router_validation(lib, kw, status):
 
 def test_router_t0_is_a_no_op(lib):
     assert router_call(lib, T=0, X=None, mask=None) == _lib.WIDE_OK
+
+
+def attn_call(lib, fn, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, mask=FAKE, T=300, Hq=32, Hk=8, dh=128, dtype=_lib.WIDE_BF16,
+             O=FAKE, flags=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return getattr(lib, fn)(a["Q"], a["K"], a["V"], a["mask"], a["T"], a["Hq"], a["Hk"], a["dh"],
+                            a["dtype"], a["O"], a["flags"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+ATTN_BAD = [
+    (dict(Q=None), _lib.WIDE_ERR_NULL),
+    (dict(mask=None), _lib.WIDE_ERR_NULL),
+    (dict(O=None), _lib.WIDE_ERR_NULL),
+    (dict(dtype=9), _lib.WIDE_ERR_DTYPE),
+    (dict(dtype=_lib.WIDE_F32), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(Hk=0), _lib.WIDE_ERR_SHAPE),
+    (dict(Hq=12, Hk=8), _lib.WIDE_ERR_SHAPE),                 # Hk does not divide Hq
+    (dict(flags=4), _lib.WIDE_ERR_SHAPE),
+    (dict(dh=64), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(Q=FAKE + 8), _lib.WIDE_ERR_ALIGN),
+    (dict(O=FAKE + 2), _lib.WIDE_ERR_ALIGN),
+    (dict(ws=FAKE + 64), _lib.WIDE_ERR_ALIGN),
+    (dict(ws=None), _lib.WIDE_ERR_WORKSPACE),
+    (dict(ws_bytes=256), _lib.WIDE_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,status", ATTN_BAD + [
+    (dict(T=-1), _lib.WIDE_ERR_SHAPE),
+    (dict(T=1 << 20), _lib.WIDE_ERR_UNSUPPORTED),             # T*Hq*dh >= 2^31
+])
+def test_attention_prefill_validation(lib, kw, status):
+    assert attn_call(lib, "wide_attention_prefill", **kw) == status
+    assert lib.wide_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", ATTN_BAD + [
+    (dict(T=0), _lib.WIDE_ERR_SHAPE),                          # a step needs its own key
+    (dict(Hq=48, Hk=3), _lib.WIDE_ERR_UNSUPPORTED),            # 16 heads per group
+])
+def test_attention_decode_validation(lib, kw, status):
+    assert attn_call(lib, "wide_attention_decode", **kw) == status
+    assert lib.wide_last_error().decode() != ""
+
+
+def test_attention_prefill_t0_is_a_no_op(lib):
+    assert attn_call(lib, "wide_attention_prefill", T=0, Q=None, K=None, V=None, mask=None,
+                     O=None) == _lib.WIDE_OK
+
+
+def test_attention_workspace_sizes(lib):
+    T, Hk, Hq, dh = 16384, 8, 32, 128
+    ws = lib.wide_attention_workspace_size(T, Hk, dh)
+    reorder = Hk * T * 4 + 2 * Hk * 4 + Hk * (T // 32) * 4
+    vt = Hk * dh * T * 2  # T is a multiple of the 64-key tile here
+    assert reorder + vt <= ws <= reorder + vt + 5 * 256
+    assert lib.wide_attention_workspace_size(-1, Hk, dh) == 0
+    d = lib.wide_attention_decode_workspace_size(T, Hq, dh)
+    assert (T // 128) * Hq * (dh + 2) * 4 <= d <= (T // 128) * Hq * (dh + 2) * 4 + 256
+    assert lib.wide_attention_decode_workspace_size(0, Hq, dh) == 0
+    assert lib.wide_attention_decode_workspace_size(T, Hq, 64) == 0
