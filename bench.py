@@ -63,6 +63,8 @@ KERNEL_SOURCES = {
     "decode_down_valu": ["decode.hip", "common.h"],
     "attention_prefill": ["attention.hip", "common.h"],
     "attention_vt": ["attention.hip", "common.h"],
+    "attention_decode_split": ["attention_decode.hip", "common.h"],
+    "attention_decode_merge": ["attention_decode.hip", "common.h"],
 }
 # substrings of the device symbol names of each kernel
 KERNEL_SYMBOLS = {
@@ -81,6 +83,8 @@ KERNEL_SYMBOLS = {
     "decode_down_valu": "decode_down_valu_kernel",
     "attention_prefill": "attention_prefill_kernel",
     "attention_vt": "attention_vt_kernel",
+    "attention_decode_split": "attention_decode_split_kernel",
+    "attention_decode_merge": "attention_decode_merge_kernel",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read + 1 GiB written
 
@@ -616,6 +620,12 @@ def run_profile(steps: int):
     for _ in range(PROFILE_GEMM_CALLS):
         wide.attention_prefill(ad["Q"], ad["K"], ad["V"], ad["mask"], aw.Hq, aw.Hk)
     torch.cuda.synchronize()
+    # decode steps over the same cache, half of the KV groups kept
+    keep = torch.tensor([1, 0] * (aw.Hk // 2), dtype=torch.uint8, device="cuda:0")
+    qd = ad["Q"][aw.T - 1].contiguous()
+    for _ in range(PROFILE_DECODE_CALLS):
+        wide.attention_decode(qd, ad["K"], ad["V"], keep, aw.Hq, aw.Hk)
+    torch.cuda.synchronize()
     del ad
     src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
@@ -629,6 +639,7 @@ PROFILE_GEMM_CALLS = 3
 PROFILE_DECODE_CALLS = 16
 PROFILE_ROUTER_T = (16384, 1)
 ROUTER_WORKLOADS = {16384: "llama3.1-8b-router-prefill", 1: "llama3.1-8b-router-decode-t1"}
+ATTN_DECODE_WORKLOAD = "llama3.1-8b-attention-decode-t16384-half-groups"
 
 
 def PROFILE_GEMMS(dg):
@@ -662,7 +673,9 @@ def profile_plan(dg, steps: int):
              (ROUTER_WORKLOADS[1], "router_small", PROFILE_GEMM_CALLS)]
     aw = dg.LLAMA8B_ATTN_PREFILL.name
     plan += [(aw, "pack_mask_bits", PROFILE_GEMM_CALLS), (aw, "reorder_bits", PROFILE_GEMM_CALLS),
-             (aw, "attention_vt", PROFILE_GEMM_CALLS), (aw, "attention_prefill", PROFILE_GEMM_CALLS)]
+             (aw, "attention_vt", PROFILE_GEMM_CALLS), (aw, "attention_prefill", PROFILE_GEMM_CALLS),
+             (ATTN_DECODE_WORKLOAD, "attention_decode_split", PROFILE_DECODE_CALLS),
+             (ATTN_DECODE_WORKLOAD, "attention_decode_merge", PROFILE_DECODE_CALLS)]
     return plan
 
 

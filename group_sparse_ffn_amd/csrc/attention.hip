@@ -58,13 +58,6 @@ __device__ __forceinline__ int key_of_row(int i) { return (i & ~12) | ((i & 4) <
 
 __device__ __forceinline__ u32x4 at_ld(const uint16_t* p) { return *(const u32x4*)p; }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -221,7 +214,7 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
           const float p0 = __builtin_amdgcn_exp2f(s[b][8 * c + 2 * i] - m_use);
           const float p1 = __builtin_amdgcn_exp2f(s[b][8 * c + 2 * i + 1] - m_use);
           psum += p0 + p1;
-          w[i] = cvt_bf16x2(p0, p1);
+          w[i] = pack_bf16x2(p0, p1);
         }
         const u32x4 wv = {w[0], w[1], w[2], w[3]};
         pf[b][c] = __builtin_bit_cast(bf16x8, wv);
@@ -273,8 +266,8 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // dims 32 j + 8 r + 4 hh .. + 3 of row wrow
-        const u32x2 v = {cvt_bf16x2(o[j][4 * r] * inv, o[j][4 * r + 1] * inv),
-                         cvt_bf16x2(o[j][4 * r + 2] * inv, o[j][4 * r + 3] * inv)};
+        const u32x2 v = {pack_bf16x2(o[j][4 * r] * inv, o[j][4 * r + 1] * inv),
+                         pack_bf16x2(o[j][4 * r + 2] * inv, o[j][4 * r + 3] * inv)};
         const int chunk = 4 * j + r;
         *(u32x2*)(smem + wrow * 256 + ((chunk ^ kswz(wrow)) << 4) + 8 * hh) = v;
       }

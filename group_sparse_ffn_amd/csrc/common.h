@@ -36,9 +36,14 @@ __device__ __forceinline__ float silu_mul(float a, float b) {
   return a * __builtin_amdgcn_rcpf(1.0f + e) * b;
 }
 
-// Pack two floats into two bf16 in one 32-bit word (low = first).
+// Pack two floats into two bf16 in one 32-bit word (low = first): one
+// v_cvt_pk_bf16_f32 (round to nearest even, NaN stays NaN). The bit-level
+// f32_to_bf16_bits above compiles to a branch per value on its NaN test.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  const f32x2_v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
 
 // LDS tiles hold rows of 64 bf16 (128 bytes = 8 chunks of 16 bytes). Chunk c
