@@ -178,17 +178,17 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     // online softmax in base 2; element e of block b is key
     // kt*64 + 32 b + 16 (e / 8) + 8 hh + e % 8. Keys past a query's position
     // get -inf (only on the wave's diagonal tiles).
+    // The maximum is taken on the raw scores (the scale is positive, so the
+    // order is the same) and the scale and the subtraction of the maximum meet
+    // in one fma inside exp2: p = 2^(s c - m c), c = log2(e) / sqrt(dh).
     if (kt >= wave_full) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kt * kAtBK + 32 * b + 16 * (e >> 3) + 8 * hh + (e & 7);
-          s[b][e] = key <= qpos ? s[b][e] * scale_log2 : -INFINITY;
+          s[b][e] = key <= qpos ? s[b][e] : -INFINITY;
         }
-    } else {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) s[b] *= scale_log2;
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -196,12 +196,14 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[b][e]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = fmaxf(m_run, mt);  // raw-score units
     // While no key is valid the running max is -inf: the exponent base 0
     // then gives exp2(-inf) = 0 for every P and for alpha, never NaN (O and l
     // stay zero). A key that is not valid gets P = 0 the same way.
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float mc = (m_new == -INFINITY ? 0.0f : m_new) * scale_log2;
+    // exactly 1 when the maximum did not move (the fma would leave m c's
+    // rounding error in the exponent)
+    const float alpha = m_run == m_new ? 1.0f : __builtin_amdgcn_exp2f(fmaf(m_run, scale_log2, -mc));
     float psum = 0.0f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(s[b][8 * c + 2 * i] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(s[b][8 * c + 2 * i + 1] - m_use);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * c + 2 * i], scale_log2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][8 * c + 2 * i + 1], scale_log2, -mc));
           psum += p0 + p1;
           w[i] = pack_bf16x2(p0, p1);
         }
