@@ -217,3 +217,40 @@ def test_attention_decode_equals_prefill_last_row_and_zero_inactive():
     # the two paths round differently (P to bf16 in prefill); both are within the bar
     a, b = Od[:half].float(), Op[T - 1, :half].float()
     assert float((a - b).abs().max() / b.abs().max()) <= 2 * TOL
+
+
+@pytest.mark.parametrize("qscale", [8.0, 32.0])
+def test_attention_peaked_softmax_stays_exact(qscale):
+    """Scores of several hundred (a very peaked softmax): the running maximum
+    keeps every exponent <= 0, so nothing overflows in prefill or decode."""
+    T, Hq, Hk = 300, 4, 2
+    w = dg.AttnWorkload("attn-peaked", 52, T=T, Hq=Hq, Hk=Hk)
+    inp = dg.make_attention_inputs(w)
+    inp["Q"] = (inp["Q"].float() * qscale).to(torch.bfloat16)  # exact: a power of two
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    O = wide.attention_prefill(d["Q"], d["K"], d["V"], d["mask"], Hq, Hk, zero_inactive=True)
+    Od = wide.attention_decode(d["Q"][T - 1].contiguous(), d["K"], d["V"], d["mask"][T - 1], Hq, Hk,
+                               zero_inactive=True)
+    torch.cuda.synchronize()
+    ref = oracle.attention(inp["Q"], inp["K"], inp["V"], inp["mask"], Hq, Hk)
+    assert bool(torch.isfinite(O.float()).all()) and bool(torch.isfinite(Od.float()).all())
+    assert rel_err(O, ref) <= TOL
+    on = inp["mask"][T - 1].bool().repeat_interleave((Hq // Hk) * 128).numpy()
+    if on.any():
+        e = np.abs(Od.float().cpu().numpy() - ref[T - 1])[on].max() / np.abs(ref[T - 1][on]).max()
+        assert e <= TOL
+
+
+def test_attention_ragged_length_skewed_groups_sampled():
+    """T not a multiple of the query or key tile; group rates spread by a
+    Beta(2, 2) profile (some groups almost always kept, some almost never)."""
+    w = dg.AttnWorkload("attn-ragged", 53, T=5000, Hq=32, Hk=8, mask_kind="beta", density=0.5)
+    inp = dg.make_attention_inputs(w)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    O = wide.attention_prefill(d["Q"], d["K"], d["V"], d["mask"], w.Hq, w.Hk, zero_inactive=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 63, 64, 127, 128, 129, 2500, 4991, 4992, 4999])
+    ref = oracle.attention(inp["Q"], inp["K"], inp["V"], inp["mask"], w.Hq, w.Hk, rows=rows)
+    assert rel_err(O[torch.from_numpy(rows).to(DEV)], ref) <= TOL
+    on = active_cols(inp["mask"], w.Hq, w.Hk, w.dh).to(DEV)
+    assert bool((O[~on] == 0).all()) and bool(torch.isfinite(O.float()).all())
