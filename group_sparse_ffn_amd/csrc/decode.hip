@@ -497,6 +497,27 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nact = list_active<kValuThreads, NT>(
       mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
+  const int nj = d / 512;
+  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
+  const int nitems = nact * G;
+  // blocks past the row's end re-read its last block (never used), so no
+  // load sits in a branch
+  u32x4 vg[kJ], vu[kJ];
+  auto load_rows = [&](int it, int j0) {
+    const int c = (int)s_groups[it / G] * G + it % G;
+    const uint16_t* pg = Wg + (size_t)c * d + 8 * lane;
+    const uint16_t* pu = Wu + (size_t)c * d + 8 * lane;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int jj = min(j0 + j, nj - 1);
+      vg[j] = ld16_nt(pg + 512 * jj);
+      vu[j] = ld16_nt(pu + 512 * jj);
+    }
+  };
+  // the first batch of this wave's first row is requested before X is
+  // staged, so the two latencies overlap (a wave without rows re-reads the
+  // last row; the values are never used)
+  if (nitems > 0) load_rows(min(gw, nitems - 1), 0);
   // X rows of the NT tokens (rows past T are zeros)
   const int cpr = d / 8;
   for (int e = tid; e < NT * cpr; e += kValuThreads) {
@@ -506,27 +527,16 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
     *(u32x4*)(s_x + t * d + 8 * c) = t < T ? v : z;
   }
   __syncthreads();
-  const int nj = d / 512;
-  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
-  const int nitems = nact * G;
+  bool loaded = true;
   for (int it = gw; it < nitems; it += nw) {
     const int g = s_groups[it / G];
     const int c = g * G + it % G;
-    const uint16_t* pg = Wg + (size_t)c * d + 8 * lane;
-    const uint16_t* pu = Wu + (size_t)c * d + 8 * lane;
     float sg[NT], su[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) sg[t] = su[t] = 0.0f;
     for (int j0 = 0; j0 < nj; j0 += kJ) {
-      // blocks past the row's end re-read its last block (never used), so
-      // no load sits in a branch
-      u32x4 vg[kJ], vu[kJ];
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const int jj = min(j0 + j, nj - 1);
-        vg[j] = ld16_nt(pg + 512 * jj);
-        vu[j] = ld16_nt(pu + 512 * jj);
-      }
+      if (!loaded) load_rows(it, j0);
+      loaded = false;
 #pragma unroll
       for (int j = 0; j < kJ; ++j) {
         if (j0 + j < nj) {
@@ -589,6 +599,24 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
       },
       s_chunks, s_wave_cnt);
   const int stride = nch * 32;  // compacted channels per token
+  const int ninstr = (nch + 15) / 16;
+  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
+  const int piece = 8 * (lane & 3);
+  // chunk slots past the list's end re-read its last chunk (never used), so
+  // no load sits in a branch
+  u32x4 w[kBatch];
+  auto load_row = [&](int n, int i0) {
+    const uint16_t* pw = Wd + (size_t)n * d_ff + piece;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int j = min(16 * (i0 + q) + (lane >> 2), nch - 1);
+      w[q] = ld16_nt(pw + (int)s_chunks[j] * 32);
+    }
+  };
+  // the first batch of this wave's first row is requested before H is
+  // compacted, so the two latencies overlap (a wave without rows re-reads
+  // the last row; the values are never used)
+  if (nch > 0) load_row(min(gw, d - 1), 0);
   for (int e = tid; e < NT * nch * 4; e += kValuThreads) {
     const int t = e / (nch * 4), r = e % (nch * 4);
     const int j = r >> 2, q = r & 3;
@@ -604,23 +632,14 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
     *(u32x4*)(s_h + t * stride + 32 * j + 8 * q) = (t < T && live) ? v : z;
   }
   __syncthreads();
-  const int ninstr = (nch + 15) / 16;
-  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
-  const int piece = 8 * (lane & 3);
+  bool loaded = true;
   for (int n = gw; n < d; n += nw) {
-    const uint16_t* pw = Wd + (size_t)n * d_ff + piece;
     float y[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = 0.0f;
     for (int i0 = 0; i0 < ninstr; i0 += kBatch) {
-      u32x4 w[kBatch];
-      // chunk slots past the list's end re-read its last chunk (never used),
-      // so no load sits in a branch
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const int j = min(16 * (i0 + q) + (lane >> 2), nch - 1);
-        w[q] = ld16_nt(pw + (int)s_chunks[j] * 32);
-      }
+      if (!loaded) load_row(n, i0);
+      loaded = false;
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int j = 16 * (i0 + q) + (lane >> 2);
