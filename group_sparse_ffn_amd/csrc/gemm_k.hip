@@ -37,6 +37,9 @@ namespace {
 constexpr int kTile = 256;
 constexpr int kMaxSteps = 1024;  // d_ff / 64 limit (d_ff <= 65536)
 using DS = core::Shape<kTile, kTile, 2, 4>;
+constexpr int kCopyWaves = 4;
+constexpr int kCB = DS::PBLOCKS / kCopyWaves;  // blocks per operand per copying wave
+static_assert(DS::PBLOCKS == DS::QBLOCKS && 8 * kCopyWaves == 32, "mask word i covers block i");
 
 __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
@@ -121,65 +124,70 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
     __syncthreads();
   }
 
-  // Copies: wave w fills 1 KB blocks w, w+8, w+16, w+24 of the Wdown rows
-  // and the same blocks of the H rows; rows past d or T get an out-of-range
-  // offset (zeros). The lane's 16-byte chunk is the same in all its blocks.
+  // Copies: only waves 0..kCopyWaves-1 issue them, so each SIMD runs one
+  // copying and one MFMA-only wave, and the MFMA-only wave keeps the matrix
+  // core busy while the other waits to issue its copies. Copying wave w
+  // fills 1 KB blocks w, w+4, ..., w+28 of the Wdown rows and the same blocks
+  // of the H rows; rows past d or T get an out-of-range offset (zeros). The
+  // lane's 16-byte chunk is the same in all its blocks.
+  const bool copier = wave < kCopyWaves;
   const int chunk = core::copy_chunk(wave, lane);
-  uint32_t voff_p[4], voff_q[4];
+  uint32_t voff_p[kCB], voff_q[kCB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = wave + 8 * i;
+  for (int i = 0; i < kCB; ++i) {
+    const int b = wave + kCopyWaves * i;
     const int r = 8 * b + (lane >> 3);
     voff_p[i] = (n0 + r < d) ? (uint32_t)((n0 + r) * d_ff + chunk * 8) * 2u : 0x80000000u;
     voff_q[i] = (t0 + r < T) ? (uint32_t)((t0 + r) * d_ff + chunk * 8) * 2u : 0x80000000u;
   }
-  // row r = 8*(wave + 8i) + lane/8 of the tile: mask word 2i + rw/32, bit rw%32
+  // block i of a copying wave holds tile rows rw + 32 i (rw = 8 * wave +
+  // lane / 8 < 32): mask word i of the tile, bit rw
   const int rw = 8 * wave + (lane >> 3);
   const uint32_t w_bytes = (uint32_t)d * (uint32_t)d_ff * 2u;
   const uint32_t h_bytes = (uint32_t)T * (uint32_t)d_ff * 2u;
   // H copy offsets of the next stage to issue, with inactive (token, group)
   // pairs turned into out-of-range offsets; computed by prepare() while the
   // MFMAs of an earlier stage run.
-  uint32_t vq_next[4];
-  // Without the LDS table: this lane's 4 mask words (tile rows rw, rw + 64,
-  // rw + 128, rw + 192) for the next stage to prepare, loaded by
-  // the prepare() of the stage before (or before the mainloop for stage 0).
-  uint32_t mw0 = 0u, mw1 = 0u, mw2 = 0u, mw3 = 0u;
+  uint32_t vq_next[kCB];
+  // Without the LDS table: this lane's 8 mask words of the tile for the next
+  // stage to prepare, loaded by the prepare() of the stage before (or before
+  // the mainloop for stage 0). Words past the last one read as zero (the
+  // index is clamped, so no load sits in a branch).
+  uint32_t mwv[kCB];
   auto fetch = [&](int s) {
     const int k0 = (int)s_steps[s] * 64;
     const uint32_t* mw = maskbits + (size_t)((k0 + chunk * 8) / G) * words;
-    const int wi = w0 + (rw >> 5);
-    mw0 = wi < words ? mw[wi] : 0u;
-    mw1 = wi + 2 < words ? mw[wi + 2] : 0u;
-    mw2 = wi + 4 < words ? mw[wi + 4] : 0u;
-    mw3 = wi + 6 < words ? mw[wi + 6] : 0u;
+#pragma unroll
+    for (int i = 0; i < kCB; ++i)
+      mwv[i] = mw[min(w0 + i, words - 1)] & (w0 + i < words ? 0xFFFFFFFFu : 0u);
   };
   auto prepare = [&](int s) {
+    if (!copier) return;
+    const uint32_t sh = rw & 31;
     if (table) {
       const int k0 = (int)s_steps[s] * 64;
       const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * 8;  // this lane's group
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vq_next[i] = ((mw[2 * i + (rw >> 5)] >> (rw & 31)) & 1u) ? voff_q[i] : 0x80000000u;
+      for (int i = 0; i < kCB; ++i)
+        vq_next[i] = ((mw[i] >> sh) & 1u) ? voff_q[i] : 0x80000000u;
     } else {
-      const uint32_t sh = rw & 31;
-      vq_next[0] = ((mw0 >> sh) & 1u) ? voff_q[0] : 0x80000000u;
-      vq_next[1] = ((mw1 >> sh) & 1u) ? voff_q[1] : 0x80000000u;
-      vq_next[2] = ((mw2 >> sh) & 1u) ? voff_q[2] : 0x80000000u;
-      vq_next[3] = ((mw3 >> sh) & 1u) ? voff_q[3] : 0x80000000u;
+#pragma unroll
+      for (int i = 0; i < kCB; ++i)
+        vq_next[i] = ((mwv[i] >> sh) & 1u) ? voff_q[i] : 0x80000000u;
       if (s + 1 < nst) fetch(s + 1);
     }
   };
-  if (!table && nst > 0) fetch(0);
+  if (copier && !table && nst > 0) fetch(0);
   auto issue = [&](int s, uint8_t* stage) {
+    if (!copier) return;
     const int k0 = (int)s_steps[s] * 64;
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Wd + k0), 0, (int)(w_bytes - 2u * k0), 0x00020000);
     const __amdgpu_buffer_rsrc_t hr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(H + k0), 0, (int)(h_bytes - 2u * k0), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wave + 8 * i;
+    for (int i = 0; i < kCB; ++i) {
+      const int b = wave + kCopyWaves * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void*)(stage + b * 1024), 16, voff_p[i], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (void*)(stage + DS::PBYTES + b * 1024), 16,
                                                vq_next[i], 0, 0, 0);

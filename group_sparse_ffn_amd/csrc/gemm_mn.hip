@@ -31,6 +31,7 @@ namespace wide {
 namespace {
 
 constexpr int kTokTile = 256;
+constexpr int kCopyWaves = 4;
 
 template <int CW, bool SWIGLU>
 struct MnShape {
@@ -41,7 +42,10 @@ struct MnShape {
   using S = core::Shape<TP, kTokTile, WP, WQ>;
   static constexpr int PBLK = S::PBLOCKS, QBLK = S::QBLOCKS;
   static constexpr int NBLK = PBLK + QBLK;
-  static constexpr int MAXB = (NBLK + 7) / 8;  // copy blocks per wave (upper bound)
+  // Only waves 0..kCopyWaves-1 issue copies: each SIMD then runs one copying
+  // and one MFMA-only wave, and the MFMA-only wave keeps the matrix core
+  // busy while the other waits to issue its copies.
+  static constexpr int MAXB = (NBLK + kCopyWaves - 1) / kCopyWaves;  // copy blocks per copying wave
   static constexpr int HALF = S::PW / 2;       // SwiGLU: channels per wave
   // epilogue staging: [256 positions][CW] bf16, split over the two stages
   static constexpr int ROWB = CW * 2;
@@ -98,11 +102,13 @@ __device__ __forceinline__ void mn_body(
   if (nact == 0) return;  // level 0
 
   // ---- copies: blocks [0, PBLK) are weight rows, [PBLK, NBLK) gathered rows.
-  // Wave w issues blocks w, w+8, ...; lane offsets are fixed per block.
+  // Copying wave w issues blocks w, w + kCopyWaves, ...; lane offsets are
+  // fixed per block.
+  const bool copier = wave < kCopyWaves;
   uint32_t voff[SH::MAXB];
 #pragma unroll
   for (int i = 0; i < SH::MAXB; ++i) {
-    const int b = wave + 8 * i;
+    const int b = wave + kCopyWaves * i;
     const int chunk = core::copy_chunk(b, lane);
     if (b < SH::PBLK) {
       const int r = 8 * b + (lane >> 3);
@@ -125,13 +131,14 @@ __device__ __forceinline__ void mn_body(
   const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2u;
   const uint32_t b_bytes = (uint32_t)N * (uint32_t)K * 2u;
   auto issue = [&](int s, uint8_t* stage) {
+    if (!copier) return;
     const int k0 = s * core::kBK;
     // gathered rows: out-of-range offsets fill zeros (level 1)
     const __amdgpu_buffer_rsrc_t ar =
         __builtin_amdgcn_make_buffer_rsrc((void*)(A + k0), 0, (int)(a_bytes - 2u * k0), 0x00020000);
 #pragma unroll
     for (int i = 0; i < SH::MAXB; ++i) {
-      const int b = wave + 8 * i;
+      const int b = wave + kCopyWaves * i;
       if (b < SH::PBLK) {
         if constexpr (SWIGLU) {
           const int r0 = 8 * b;
