@@ -86,6 +86,7 @@ __device__ __forceinline__ void mn_body(
   const int32_t* __restrict__ prow = perm + (size_t)g * M + tile0;
   const int nrows = min(kTokTile, M - tile0);          // positions that exist
   const int nact = max(0, min(nrows, count - tile0));  // active positions
+  if (nact == 0 && !zero_inactive) return;  // level 0, nothing to clear
 
   if (tid < kTokTile) s_tok[tid] = tid < nrows ? prow[tid] : 0;
   __syncthreads();
