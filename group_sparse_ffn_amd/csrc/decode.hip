@@ -739,10 +739,11 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                                    hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (valu_shape(T, d, d_ff)) {
-    // two workgroups per CU (measured best of one, two and four), waves
-    // strided over the output rows
+    // waves strided over the output rows; one token: three workgroups per CU
+    // (measured best of two, three and four), two tokens: two (the LDS copy
+    // of H holds two workgroups per CU)
     if (T == 1)
-      hipLaunchKernelGGL(decode_down_valu_kernel_1, dim3(2 * num_cus()), dim3(kValuThreads), 0,
+      hipLaunchKernelGGL(decode_down_valu_kernel_1, dim3(3 * num_cus()), dim3(kValuThreads), 0,
                          stream, H, Wd, mask, T, d, d_ff, G, Y);
     else
       hipLaunchKernelGGL(decode_down_valu_kernel_2, dim3(2 * num_cus()), dim3(kValuThreads), 0,
