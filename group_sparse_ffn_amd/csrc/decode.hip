@@ -708,11 +708,12 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
                                       const uint8_t* mask, int T, int d, int d_ff, int G,
                                       uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  // one or two tokens: whole-row streaming on a persistent grid of three
-  // workgroups per CU (measured best of one to four at the Llama3.1-8B shape)
+  // one or two tokens: whole-row streaming on a persistent grid of four
+  // workgroups per CU for one token (measured best of three, four, five and
+  // seven at the Llama3.1-8B shape), three for two tokens
   if (valu_shape(T, d, d_ff)) {
     if (T == 1)
-      hipLaunchKernelGGL(decode_gate_up_valu_kernel_1, dim3(3 * num_cus()), dim3(kValuThreads), 0,
+      hipLaunchKernelGGL(decode_gate_up_valu_kernel_1, dim3(4 * num_cus()), dim3(kValuThreads), 0,
                          stream, X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
     else
       hipLaunchKernelGGL(decode_gate_up_valu_kernel_2, dim3(3 * num_cus()), dim3(kValuThreads), 0,
