@@ -783,6 +783,77 @@ def mfma_summary(directory, command, plan, split_fn):
     print(f"wrote {out}")
 
 
+def busy_summary(directory, command, plan, split_fn):
+    """profiles/mfma_busy_llama8b.md: from one counter run with SQ_VALU_MFMA_BUSY_CYCLES
+    and GRBM_GUI_ACTIVE, the shader clock each kernel ran at and the share of
+    SIMD cycles its matrix cores were busy."""
+    from group_sparse_ffn_amd import datagen as dg
+    agents = glob.glob(os.path.join(directory, "**", "*agent_info.csv"), recursive=True)
+    gpu = None
+    for path in agents:
+        for r in csv.DictReader(open(path)):
+            if r.get("Agent_Type") == "GPU":
+                gpu = r
+    if gpu is None:
+        return
+    nxcc, nsimd = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    vals = {}  # counter -> kernel -> [(dispatch id, value)]
+    durs = {}  # kernel -> [(dispatch id, ns)]
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = r["Counter_Name"]
+            if name not in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"):
+                continue
+            k = next((kk for kk, v in KERNEL_SYMBOLS.items() if v in r["Kernel_Name"]), None)
+            if k is None:
+                continue
+            did = int(r["Dispatch_Id"])
+            vals.setdefault(name, {}).setdefault(k, []).append((did, float(r["Counter_Value"])))
+            if name == "GRBM_GUI_ACTIVE":
+                durs.setdefault(k, []).append(
+                    (did, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    if len(vals) < 2:
+        return
+    busy = split_fn(plan, vals["SQ_VALU_MFMA_BUSY_CYCLES"])
+    gui = split_fn(plan, vals["GRBM_GUI_ACTIVE"])
+    dur = split_fn(plan, durs)
+    forms = work_closed_forms(dg)
+    lines = ["# Shader clock and MFMA busy share per launch", "",
+             "One rocprofv3 counter run of the command below with SQ_VALU_MFMA_BUSY_CYCLES and",
+             f"GRBM_GUI_ACTIVE, averaged over each kernel's dispatches for the workload.",
+             f"GRBM_GUI_ACTIVE is summed over the {nxcc} XCDs, so one XCD's active cycles are",
+             f"the value / {nxcc}; the clock is those cycles over the dispatch's duration (shown",
+             "for kernels of 100 us or more: for shorter ones the counter window is much longer",
+             f"than the kernel). MFMA busy = busy cycles summed over the {nsimd} SIMDs /",
+             f"({nsimd} x one XCD's active cycles). `peak at clock` scales the 2.5 PFLOP/s",
+             "bf16 dense peak (quoted at 2.4 GHz) to the measured clock; `designed TFLOP/s`",
+             "is the kernel's designed MFMA work over its duration.", "",
+             "```", command.replace("PMC", "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"), "```", "",
+             "| kernel | workload | duration (us) | clock (GHz) | MFMA busy | peak at clock (TFLOP/s) "
+             "| designed TFLOP/s |",
+             "|---|---|---|---|---|---|---|"]
+    for workload, kernel, _ in plan:
+        b, g, t = (busy.get((workload, kernel), []), gui.get((workload, kernel), []),
+                   dur.get((workload, kernel), []))
+        if not b or not g or not t:
+            continue
+        ns = sum(t) / len(t)
+        cyc = sum(g) / len(g) / nxcc
+        clk = cyc / ns
+        frac = (sum(b) / len(b)) / (nsimd * cyc)
+        des = forms.get((workload, kernel), (0.0, 0.0))[1]
+        rate = f"{des / (ns * 1e-9) / 1e12:.0f}" if des else "-"
+        if ns < 100e3:  # the counter window dwarfs the kernel: no clock to read
+            lines.append(f"| {kernel} | {workload} | {ns / 1e3:.1f} | - | - | - | {rate} |")
+            continue
+        peak = PEAK_BF16_TFLOPS * clk / 2.4
+        lines.append(f"| {kernel} | {workload} | {ns / 1e3:.1f} | {clk:.2f} | {100 * frac:.1f}% | "
+                     f"{peak:.0f} | {rate} |")
+    out = os.path.join(ROOT, "profiles", "mfma_busy_llama8b.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def summarize(directory: str, command: str, steps: int):
     """Turn rocprofv3 CSVs (kernel trace, FETCH_SIZE and WRITE_SIZE counter runs) into profiles/*.md.
 
@@ -822,6 +893,7 @@ def summarize(directory: str, command: str, steps: int):
         open(out, "w").write("\n".join(lines) + "\n")
         print(f"wrote {out}")
     mfma_summary(directory, command, plan, split_by_plan)
+    busy_summary(directory, command, plan, split_by_plan)
     per = {}     # counter -> kernel name -> values (KiB per dispatch), for the copy calibration
     per_id = {}  # counter -> kernel -> [(dispatch id, value)]
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
