@@ -783,7 +783,7 @@ def mfma_summary(directory, command, plan, split_fn):
     print(f"wrote {out}")
 
 
-def busy_summary(directory, command, plan, split_fn):
+def busy_summary(directory, command, plan, split_fn, out_dir=None):
     """profiles/mfma_busy_llama8b.md: from one counter run with SQ_VALU_MFMA_BUSY_CYCLES
     and GRBM_GUI_ACTIVE, the shader clock each kernel ran at and the share of
     SIMD cycles its matrix cores were busy."""
@@ -849,7 +849,7 @@ def busy_summary(directory, command, plan, split_fn):
         peak = PEAK_BF16_TFLOPS * clk / 2.4
         lines.append(f"| {kernel} | {workload} | {ns / 1e3:.1f} | {clk:.2f} | {100 * frac:.1f}% | "
                      f"{peak:.0f} | {rate} |")
-    out = os.path.join(ROOT, "profiles", "mfma_busy_llama8b.md")
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "mfma_busy_llama8b.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print(f"wrote {out}")
 
