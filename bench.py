@@ -58,6 +58,8 @@ KERNEL_SOURCES = {
     "router": ["router.hip", "common.h"],
     "router_small": ["router.hip", "common.h"],
     "decode_down_splitk": ["decode.hip", "common.h"],
+    "decode_gate_up_packed": ["decode.hip", "common.h"],
+    "decode_down_splitk_packed": ["decode.hip", "common.h"],
     "decode_down_reduce": ["decode.hip", "common.h"],
     "decode_gate_up_valu": ["decode.hip", "common.h"],
     "decode_down_valu": ["decode.hip", "common.h"],
@@ -77,7 +79,9 @@ KERNEL_SYMBOLS = {
     "reorder_bits": "reorder_bits_kernel",
     "router": "router_kernel_",
     "router_small": "router_small_kernel_",
-    "decode_down_splitk": "decode_down_splitk_kernel",
+    "decode_down_splitk": "decode_down_splitk_kernel<false, false>",
+    "decode_gate_up_packed": "decode_gate_up_packed_kernel",
+    "decode_down_splitk_packed": "decode_down_splitk_kernel<false, true>",
     "decode_down_reduce": "decode_down_reduce_kernel",
     "decode_gate_up_valu": "decode_gate_up_valu_kernel",
     "decode_down_valu": "decode_down_valu_kernel",
@@ -536,6 +540,16 @@ def decode_setup(torch, wide, dg, w, copies: int):
     return calls, ws, union
 
 
+def prepared_calls(wide, calls, ws):
+    """The calls of decode_setup on operand-order copies of their weights."""
+    out = []
+    for c, w in zip(calls, ws):
+        X, _, _, _, mask = c.args
+        prep = wide.decode_prepare_weights(w["Wg"], w["Wu"], w["Wd"])
+        out.append(wide.FfnCall(X, w["Wg"], w["Wu"], w["Wd"], mask, c.G, prepared=prep))
+    return out
+
+
 def bench_decode(torch, wide, dg, steps: int, copies: int = 8):
     res = {}
     for w in (dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16):
@@ -577,6 +591,30 @@ def bench_decode(torch, wide, dg, steps: int, copies: int = 8):
                           "weight_copies": copies,
                           "gate_up_us": ms_gu * 1e3, "gate_up_GBps": gu_bytes / ms_gu / 1e6,
                           "down_us": ms_dn * 1e3, "down_GBps": dn_bytes / ms_dn / 1e6}
+        if w is dg.LLAMA8B_DECODE_T16:
+            # operand-order weights (wide_ffn_decode_prepared): same results
+            # bit for bit, contiguous 1 KB weight operands
+            pcalls = prepared_calls(wide, calls, ws)
+            for c in pcalls:
+                c.run()
+            pidx = [0]
+
+            def pstep():
+                pcalls[pidx[0] % copies].run()
+                pidx[0] += 1
+            pms = time_events(torch, pstep, n)
+
+            def all_prepared():
+                for c in pcalls:
+                    c.run()
+            pgms = graph_step_ms(torch, all_prepared, max(steps, 4)) / copies
+            res[f"T{w.T}"]["operand_order_weights"] = {
+                "us_per_step": pms * 1e3, "active_weight_GBps": act_bytes / pms / 1e6,
+                "hbm_frac": act_bytes / pms / 1e6 / PEAK_HBM_GBS,
+                "graph_us_per_step": pgms * 1e3,
+                "prepared_MB": wide.decode_weights_size(w.d, w.d_ff) / 1e6,
+                "entry": "wide_ffn_decode_prepared"}
+            del pcalls
         del calls, ws
         torch.cuda.empty_cache()
     return res
@@ -596,6 +634,14 @@ def run_profile(steps: int):
             for c in calls:
                 c.run()
         torch.cuda.synchronize()
+        if w is dg.LLAMA8B_DECODE_T16:
+            # the same steps with operand-order weights
+            pcalls = prepared_calls(wide, calls, ws)
+            for _ in range(2):
+                for c in pcalls:
+                    c.run()
+            torch.cuda.synchronize()
+            del pcalls
         del calls, ws
         torch.cuda.empty_cache()
     for w in PROFILE_GEMMS(dg):
@@ -637,6 +683,7 @@ def run_profile(steps: int):
 
 PROFILE_GEMM_CALLS = 3
 PROFILE_DECODE_CALLS = 16
+T16_PREPARED = "llama3.1-8b-ffn-decode-t16-operand-order-weights"
 PROFILE_ROUTER_T = (16384, 1)
 ROUTER_WORKLOADS = {16384: "llama3.1-8b-router-prefill", 1: "llama3.1-8b-router-decode-t1"}
 ATTN_DECODE_WORKLOAD = "llama3.1-8b-attention-decode-t16384-half-groups"
@@ -660,7 +707,10 @@ def profile_plan(dg, steps: int):
              (t1, "decode_down_valu", PROFILE_DECODE_CALLS),
              (t16, "decode_gate_up", PROFILE_DECODE_CALLS),
              (t16, "decode_down_splitk", PROFILE_DECODE_CALLS),
-             (t16, "decode_down_reduce", PROFILE_DECODE_CALLS)]
+             (t16, "decode_down_reduce", PROFILE_DECODE_CALLS),
+             (T16_PREPARED, "decode_gate_up_packed", PROFILE_DECODE_CALLS),
+             (T16_PREPARED, "decode_down_splitk_packed", PROFILE_DECODE_CALLS),
+             (T16_PREPARED, "decode_down_reduce", PROFILE_DECODE_CALLS)]
     for w in PROFILE_GEMMS(dg):
         if w.axis == "mn":
             plan += [(w.name, "pack_mask_bits", PROFILE_GEMM_CALLS),
@@ -699,6 +749,8 @@ def split_by_plan(plan, dispatches):
 # flops of one MFMA instruction of each kernel (its instruction shape)
 MFMA_FLOPS = {"gate_up": 2 * 32 * 32 * 16, "down": 2 * 32 * 32 * 16, "gemm_mn": 2 * 32 * 32 * 16,
               "decode_gate_up": 2 * 16 * 16 * 32, "decode_down_splitk": 2 * 16 * 16 * 32,
+              "decode_gate_up_packed": 2 * 16 * 16 * 32,
+              "decode_down_splitk_packed": 2 * 16 * 16 * 32,
               "router": 2 * 16 * 16 * 32, "router_small": 2 * 16 * 16 * 32,
               "attention_prefill": 2 * 32 * 32 * 16}
 
@@ -719,6 +771,8 @@ def work_closed_forms(dg):
     # 16 token columns per MFMA; every group is live at T = 16
     out[(t16.name, "decode_gate_up")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
     out[(t16.name, "decode_down_splitk")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
+    out[(T16_PREPARED, "decode_gate_up_packed")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
+    out[(T16_PREPARED, "decode_down_splitk_packed")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
     out[("llama3.1-8b-router-prefill", "router")] = (2.0 * 16384 * 4096 * 32,) * 2
     out[("llama3.1-8b-router-decode-t1", "router_small")] = (2.0 * 16 * 4096 * 32,) * 2
     aw = dg.LLAMA8B_ATTN_PREFILL

@@ -22,7 +22,8 @@ __all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decod
            "FfnCall", "WideError", "WIDE_TOKEN_TILE", "WIDE_DECODE_T_LIMIT",
            "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
            "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
-           "WIDE_STAGE_DECODE_DOWN"]
+           "WIDE_STAGE_DECODE_DOWN", "decode_weights_size", "decode_prepare_weights",
+           "ffn_decode_prepared"]
 
 _DTYPES = {torch.bfloat16: WIDE_BF16, torch.float32: WIDE_F32}
 
@@ -70,7 +71,8 @@ class FfnCall:
 
     def __init__(self, X, Wg, Wu, Wd, mask, G: int, return_h: bool = False, flags: int = 0,
                  Y: Optional[torch.Tensor] = None, H: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None,
+                 prepared: Optional[torch.Tensor] = None):
         for name, t in (("X", X), ("Wgate", Wg), ("Wup", Wu), ("Wdown", Wd), ("mask", mask)):
             _need_cuda(name, t)
         if X.dtype not in _DTYPES or any(w.dtype != X.dtype for w in (Wg, Wu, Wd)):
@@ -98,6 +100,13 @@ class FfnCall:
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         self.workspace = workspace
         self.ws_bytes = workspace.numel() * workspace.element_size()
+        # operand-order weights (decode_prepare_weights): run() then takes the
+        # decode path through wide_ffn_decode_prepared
+        self.prepared = prepared
+        if prepared is not None:
+            _need_cuda("prepared", prepared)
+            if flags != 0:
+                raise ValueError("a call with prepared weights takes no flags (it is decode only)")
 
     def _ffn_args(self):
         X, Wg, Wu, Wd, mask = self.args
@@ -107,10 +116,20 @@ class FfnCall:
                 self.ws_bytes, self.flags, _stream_ptr(X.device))
 
     def run(self):
-        _lib.check(_lib.load().wide_ffn_forward(*self._ffn_args()))
+        if self.prepared is not None:
+            X, Wg, Wu, Wd, mask = self.args
+            _lib.check(_lib.load().wide_ffn_decode_prepared(
+                X.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), self.prepared.data_ptr(),
+                mask.data_ptr(), self.T, self.d, self.d_ff, self.G, self.Y.data_ptr(),
+                None if self.H is None else self.H.data_ptr(), self.workspace.data_ptr(),
+                self.ws_bytes, _stream_ptr(X.device)))
+        else:
+            _lib.check(_lib.load().wide_ffn_forward(*self._ffn_args()))
         return self.Y
 
     def stage(self, stage: int):
+        if self.prepared is not None:
+            raise ValueError("stages run the nn.Linear weights; time a prepared call with run()")
         _lib.check(_lib.load().wide_ffn_stage(stage, *self._ffn_args()))
 
 
@@ -123,6 +142,36 @@ def ffn_forward(X, Wg, Wu, Wd, mask, G: int, return_h: bool = False, flags: int 
 
 def ffn_stage(stage: int, call: FfnCall) -> None:
     call.stage(stage)
+
+
+def decode_weights_size(d: int, d_ff: int) -> int:
+    return int(_lib.load().wide_decode_weights_size(d, d_ff))
+
+
+def decode_prepare_weights(Wg, Wu, Wd, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Operand-order copy of the bf16 weights for the decode kernels (uint8 bytes)."""
+    for name, t in (("Wgate", Wg), ("Wup", Wu), ("Wdown", Wd)):
+        _need_cuda(name, t)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    d_ff, d = Wg.shape
+    if Wu.shape != (d_ff, d) or Wd.shape != (d, d_ff):
+        raise ValueError("expected Wgate, Wup [d_ff, d] and Wdown [d, d_ff]")
+    nbytes = decode_weights_size(d, d_ff)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=Wg.device)
+    _need_cuda("out", out)
+    _lib.check(_lib.load().wide_decode_prepare_weights(
+        Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), d, d_ff, out.data_ptr(),
+        out.numel() * out.element_size(), _stream_ptr(Wg.device)))
+    return out
+
+
+def ffn_decode_prepared(X, Wg, Wu, Wd, prepared, mask, G: int, return_h: bool = False):
+    """The decode path of ffn_forward with the matrix-core kernels reading `prepared`."""
+    call = FfnCall(X, Wg, Wu, Wd, mask, G, return_h=return_h, prepared=prepared)
+    Y = call.run()
+    return (Y, call.H) if return_h else Y
 
 
 # ---------------------------------------------------------------- masked GEMMs

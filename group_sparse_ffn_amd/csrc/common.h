@@ -117,17 +117,28 @@ hipError_t launch_gemm_mn_bf16(const uint16_t* A, const uint16_t* B, const int32
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
                             int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
 
-// bf16 decode GEMVs (T <= 16).
+// Operand-order copy of a bf16 [rows, cols] matrix (rows % 16 == 0, cols % 32
+// == 0): each 16-row x 32-column MFMA operand becomes one contiguous 1 KB
+// block (lane l's 16 bytes at byte 16 l: row l % 16, columns 8 (l / 16) ..),
+// blocks ordered by 16-row block, then by 32-column slice.
+hipError_t launch_decode_pack_bf16(const uint16_t* W, int rows, int cols, uint16_t* out,
+                                   hipStream_t stream);
+
+// bf16 decode GEMVs (T <= 16). Wg_op / Wu_op / Wd_op: operand-order copies of
+// the weights, or NULL. With them the MFMA kernels (T > 2, or shapes the
+// whole-row kernels do not take) read contiguous 1 KB operands; the
+// whole-row kernels always read the nn.Linear layout.
 hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                      const uint16_t* Wg_op, const uint16_t* Wu_op,
                                       const uint8_t* mask, int T, int d, int d_ff, int G,
                                       uint16_t* H, bool zero_inactive, hipStream_t stream);
 // For T > 2 (or shapes the whole-row kernels do not take) the down GEMV is
 // split over the live channel chunks: `part` holds kDecodeDownSplit * T * d
 // fp32 partial sums (workspace; contents on entry ignored).
 constexpr int kDecodeDownSplit = 8;
-hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
-                                   int T, int d, int d_ff, int G, uint16_t* Y, float* part,
-                                   hipStream_t stream);
+hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint16_t* Wd_op,
+                                   const uint8_t* mask, int T, int d, int d_ff, int G, uint16_t* Y,
+                                   float* part, hipStream_t stream);
 
 // Bottleneck router: mask[t, g] = argmax over the two logits of group g is
 // class 0 (act 0 identity, 1 relu, 2 silu); logits [T, ng, 2] optional.

@@ -143,7 +143,11 @@ constexpr int kGuWaves = kGuThreads / 64;
 // almost nothing). UC = 16 / 32: UC/16 gate operands and UC/16 up operands of
 // 16 rows share each activation fragment (a half / a quarter of the
 // activation traffic per weight byte, for many tokens).
-template <int UC>
+// PACKED (UC >= 16): Wg and Wu are operand-order copies, in which the 16 rows
+// x 32 columns of each MFMA operand are one contiguous 1 KB block (lane l's
+// 16 bytes at byte 16 l), blocks ordered by 16-row block, then by 32-column
+// slice; every weight load then reads 1 KB of contiguous memory.
+template <int UC, bool PACKED = false>
 __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
                                              const uint16_t* __restrict__ Wg,
                                              const uint16_t* __restrict__ Wu,
@@ -199,14 +203,19 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   // operand rows: UC == 8: rows 0..7 gate, 8..15 up of channels c0..c0+7;
   //   else operand f < NF/2: gate rows c0 + 16 f + r, operand f + NF/2: the up
   //   rows of the same channels
+  static_assert(!PACKED || NF >= 2, "operand-order weights need 16-row gate and up operands");
+  // elements between the operands of consecutive 32-wide K slices
+  constexpr int kStep = PACKED ? 512 : 32;
   const uint16_t* pw[NF];
   if (NF == 1) {
     pw[0] = (r < 8 ? Wg : Wu) + (size_t)(c0 + (r & 7)) * d + kbase;
   } else {
 #pragma unroll
     for (int f = 0; f < NF / 2; ++f) {
-      pw[f] = Wg + (size_t)(c0 + 16 * f + r) * d + kbase;
-      pw[f + NF / 2] = Wu + (size_t)(c0 + 16 * f + r) * d + kbase;
+      const size_t off = PACKED ? ((size_t)((c0 + 16 * f) / 16) * (d / 32) + s_lo) * 512 + 8 * lane
+                                : (size_t)(c0 + 16 * f + r) * d + kbase;
+      pw[f] = Wg + off;
+      pw[f + NF / 2] = Wu + off;
     }
   }
   // B operand column = token; columns past T - 1 repeat token T - 1's row
@@ -231,7 +240,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
 #pragma unroll
     for (int q = 0; q < kU; ++q) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16(pw[f] + 32 * (b * kU + q));
+      for (int f = 0; f < NF; ++f) aw[set][f][q] = ld16(pw[f] + kStep * (b * kU + q));
       bx[set][q] = ld16(px + 32 * (b * kU + q));
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -268,7 +277,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
     const bf16x8 bv = __builtin_bit_cast(bf16x8, ld16(px + 32 * s));
 #pragma unroll
     for (int f = 0; f < NF; ++f)
-      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[f] + 32 * s)),
+      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[f] + kStep * s)),
                                                        bv, acc[f], 0, 0, 0);
   }
 
@@ -304,20 +313,22 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   }
 }
 
-#define WIDE_DECODE_GATE_UP_KERNEL(UC)                                                          \
-  __global__ __launch_bounds__(kGuThreads) void decode_gate_up_kernel_##UC(                      \
+#define WIDE_DECODE_GATE_UP_KERNEL(NAME, UC, PACKED)                                            \
+  __global__ __launch_bounds__(kGuThreads) void NAME(                                           \
       const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,                          \
       const uint16_t* __restrict__ Wu, const uint8_t* __restrict__ mask, int T, int d,          \
       int d_ff, int G, uint16_t* __restrict__ H, int zero_inactive) {                           \
     __shared__ uint16_t s_groups[kMaxGroups];                                                   \
     __shared__ int s_wave_cnt[kGuWaves];                                                        \
     __shared__ float s_red[kGuWaves][64][16];                                                   \
-    gate_up_unit<UC>(X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive, s_groups, s_wave_cnt,    \
-                     s_red);                                                                    \
+    gate_up_unit<UC, PACKED>(X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive, s_groups,        \
+                             s_wave_cnt, s_red);                                                \
   }
-WIDE_DECODE_GATE_UP_KERNEL(8)
-WIDE_DECODE_GATE_UP_KERNEL(16)
-WIDE_DECODE_GATE_UP_KERNEL(32)
+WIDE_DECODE_GATE_UP_KERNEL(decode_gate_up_kernel_8, 8, false)
+WIDE_DECODE_GATE_UP_KERNEL(decode_gate_up_kernel_16, 16, false)
+WIDE_DECODE_GATE_UP_KERNEL(decode_gate_up_kernel_32, 32, false)
+WIDE_DECODE_GATE_UP_KERNEL(decode_gate_up_packed_kernel_16, 16, true)
+WIDE_DECODE_GATE_UP_KERNEL(decode_gate_up_packed_kernel_32, 32, true)
 #undef WIDE_DECODE_GATE_UP_KERNEL
 
 // Down GEMV for T > 2: split over the live chunks. A workgroup owns 64
@@ -334,7 +345,9 @@ constexpr int kMaxChunks = 2048;  // d_ff / 32 limit
 
 // HALVES (G == 16): a live 32-channel chunk can hold a group that no token
 // executes; its H was never written, so those lanes use zeros instead.
-template <bool HALVES>
+// PACKED: Wd is the operand-order copy (see gate_up_unit): the 16 rows x 32
+// channels of each operand are one contiguous 1 KB block.
+template <bool HALVES, bool PACKED = false>
 __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G, float* __restrict__ part) {
@@ -371,9 +384,14 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
 
   const int koff = 8 * (lane >> 4);
   const int tok = lane & 15;
+  // weight operand of chunk k (its first channel) for row block rb: pw[rb] +
+  // k, or with the operand-order copy pw[rb] + 16 k (1 KB per 32 channels)
   const uint16_t* pw[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) pw[rb] = Wd + (size_t)(n0 + 16 * rb + (lane & 15)) * d_ff + koff;
+  for (int rb = 0; rb < 4; ++rb)
+    pw[rb] = PACKED ? Wd + (size_t)((n0 + 16 * rb) / 16) * (d_ff / 32) * 512 + 8 * lane
+                    : Wd + (size_t)(n0 + 16 * rb + (lane & 15)) * d_ff + koff;
+  constexpr int kScale = PACKED ? 16 : 1;
   // token columns past T - 1 repeat token T - 1 (never stored, see gate/up)
   const uint16_t* ph = H + (size_t)min(tok, T - 1) * d_ff + koff;
   const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -403,7 +421,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     for (int q = 0; q < kSkU; ++q) {
       const int k = chunk_k(b * kSkU + q);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[set][rb][q] = ld16(pw[rb] + k);
+      for (int rb = 0; rb < 4; ++rb) a[set][rb][q] = ld16(pw[rb] + kScale * k);
       bb[set][q] = ld16(ph + k);
       hm[set][q] = h_mask(k);
     }
@@ -442,7 +460,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     const bf16x8 hv = HALVES ? masked(ld16(ph + k), h_mask(k)) : __builtin_bit_cast(bf16x8, ld16(ph + k));
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
-      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[rb] + k)),
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[rb] + kScale * k)),
                                                         hv, acc[rb], 0, 0, 0);
   }
   // lane holds token (lane % 16) and rows 16 rb + 4 (lane / 16) + e
@@ -704,7 +722,36 @@ int num_cus() {
 
 }  // namespace
 
+namespace {
+
+// Operand-order copy of a [rows, cols] bf16 matrix: 16-byte chunk i of the
+// output is lane l = i % 64 of block b = i / 64, i.e. row 16 (b / (cols/32)) +
+// l % 16, columns 32 (b % (cols/32)) + 8 (l / 16) .. + 7 of the input.
+__global__ __launch_bounds__(256) void decode_pack_kernel(const uint16_t* __restrict__ W, int rows,
+                                                          int cols, uint16_t* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * cols / 8) return;
+  const size_t b = i / 64;
+  const int l = (int)(i % 64);
+  const size_t rb = b / (size_t)(cols / 32);
+  const int kc = (int)(b % (size_t)(cols / 32));
+  *(u32x4*)(out + 8 * i) = ld16(W + (16 * rb + (size_t)(l & 15)) * cols + 32 * kc + 8 * (l >> 4));
+}
+
+}  // namespace
+
+hipError_t launch_decode_pack_bf16(const uint16_t* W, int rows, int cols, uint16_t* out,
+                                   hipStream_t stream) {
+  if (rows % 16 != 0 || cols % 32 != 0) return hipErrorInvalidValue;
+  const size_t chunks = (size_t)rows * cols / 8;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                     stream, W, rows, cols, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                      const uint16_t* Wg_op, const uint16_t* Wu_op,
                                       const uint8_t* mask, int T, int d, int d_ff, int G,
                                       uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
@@ -718,6 +765,16 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
     else
       hipLaunchKernelGGL(decode_gate_up_valu_kernel_2, dim3(3 * num_cus()), dim3(kValuThreads), 0,
                          stream, X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+    return hipGetLastError();
+  }
+  // operand-order weights: 32-channel units (16 with G = 16) for any T
+  if (Wg_op != nullptr) {
+    if (G % 32 == 0)
+      hipLaunchKernelGGL(decode_gate_up_packed_kernel_32, dim3(d_ff / 32), dim3(kGuThreads), 0,
+                         stream, X, Wg_op, Wu_op, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
+    else
+      hipLaunchKernelGGL(decode_gate_up_packed_kernel_16, dim3(d_ff / 16), dim3(kGuThreads), 0,
+                         stream, X, Wg_op, Wu_op, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
     return hipGetLastError();
   }
   // few tokens: 8-channel units (finest balance); more tokens: 32-channel
@@ -735,9 +792,9 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
   return hipGetLastError();
 }
 
-hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint8_t* mask,
-                                   int T, int d, int d_ff, int G, uint16_t* Y, float* part,
-                                   hipStream_t stream) {
+hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint16_t* Wd_op,
+                                   const uint8_t* mask, int T, int d, int d_ff, int G, uint16_t* Y,
+                                   float* part, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (valu_shape(T, d, d_ff)) {
     // waves strided over the output rows; one token: three workgroups per CU
@@ -754,12 +811,19 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
   // G is a multiple of 16: below 32 it is 16, the case whose chunks can
   // straddle an executed and a skipped group
   if (G % 16 != 0) return hipErrorInvalidValue;
-  if (G == 16)
-    hipLaunchKernelGGL(decode_down_splitk_kernel<true>, dim3((d / kSkRows) * kDecodeDownSplit),
-                       dim3(kSkThreads), 0, stream, H, Wd, mask, T, d, d_ff, G, part);
+  const dim3 grid((d / kSkRows) * kDecodeDownSplit);
+  if (Wd_op != nullptr && G == 16)
+    hipLaunchKernelGGL((decode_down_splitk_kernel<true, true>), grid, dim3(kSkThreads), 0, stream, H,
+                       Wd_op, mask, T, d, d_ff, G, part);
+  else if (Wd_op != nullptr)
+    hipLaunchKernelGGL((decode_down_splitk_kernel<false, true>), grid, dim3(kSkThreads), 0, stream,
+                       H, Wd_op, mask, T, d, d_ff, G, part);
+  else if (G == 16)
+    hipLaunchKernelGGL(decode_down_splitk_kernel<true>, grid, dim3(kSkThreads), 0, stream, H, Wd,
+                       mask, T, d, d_ff, G, part);
   else
-    hipLaunchKernelGGL(decode_down_splitk_kernel<false>, dim3((d / kSkRows) * kDecodeDownSplit),
-                       dim3(kSkThreads), 0, stream, H, Wd, mask, T, d, d_ff, G, part);
+    hipLaunchKernelGGL(decode_down_splitk_kernel<false>, grid, dim3(kSkThreads), 0, stream, H, Wd,
+                       mask, T, d, d_ff, G, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_down_reduce_kernel, dim3((T * d / 4 + 255) / 256), dim3(256), 0, stream,

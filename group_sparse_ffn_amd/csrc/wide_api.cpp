@@ -103,7 +103,12 @@ struct Args {
   size_t ws_bytes;
   uint32_t flags;
   hipStream_t stream;
+  const void* prep = nullptr;  // operand-order weights for the decode MFMA kernels, or NULL
 };
+
+// Operand-order weight copy (wide_decode_prepare_weights): Wgate, Wup, Wdown
+// regions of d * d_ff bf16 each, 256-byte aligned.
+size_t prep_region(int64_t d, int64_t d_ff) { return round_up((size_t)(d * d_ff) * 2, 256); }
 
 // Host-side checks shared by wide_ffn_forward and wide_ffn_stage. Sets
 // *decode to the path the call takes.
@@ -191,15 +196,23 @@ wide_status_t run_stage(wide_stage_t stage, const Args& a) {
         e = wide::launch_down_f32((const float*)H, (const float*)a.Wd, maskbits, a.T, a.d, a.d_ff,
                                   a.G, (float*)a.Y, a.stream);
       return hip_status(e, "down launch");
-    case WIDE_STAGE_DECODE_GATE_UP:
-      e = wide::launch_decode_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
-                                           (const uint16_t*)a.Wu, a.mask, a.T, a.d, a.d_ff, a.G,
-                                           (uint16_t*)H, zero_h, a.stream);
+    case WIDE_STAGE_DECODE_GATE_UP: {
+      const char* pp = static_cast<const char*>(a.prep);
+      const size_t R = prep_region(a.d, a.d_ff);
+      e = wide::launch_decode_gate_up_bf16(
+          (const uint16_t*)a.X, (const uint16_t*)a.Wg, (const uint16_t*)a.Wu,
+          pp ? (const uint16_t*)pp : nullptr, pp ? (const uint16_t*)(pp + R) : nullptr, a.mask,
+          a.T, a.d, a.d_ff, a.G, (uint16_t*)H, zero_h, a.stream);
       return hip_status(e, "decode gate/up launch");
-    case WIDE_STAGE_DECODE_DOWN:
-      e = wide::launch_decode_down_bf16((const uint16_t*)H, (const uint16_t*)a.Wd, a.mask, a.T, a.d,
-                                        a.d_ff, a.G, (uint16_t*)a.Y, part, a.stream);
+    }
+    case WIDE_STAGE_DECODE_DOWN: {
+      const char* pp = static_cast<const char*>(a.prep);
+      const size_t R = prep_region(a.d, a.d_ff);
+      e = wide::launch_decode_down_bf16((const uint16_t*)H, (const uint16_t*)a.Wd,
+                                        pp ? (const uint16_t*)(pp + 2 * R) : nullptr, a.mask, a.T,
+                                        a.d, a.d_ff, a.G, (uint16_t*)a.Y, part, a.stream);
       return hip_status(e, "decode down launch");
+    }
   }
   return fail(WIDE_ERR_SHAPE, "unknown stage %d", (int)stage);
 }
@@ -270,6 +283,63 @@ WIDE_API wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const v
                 (int)stage, dec ? "decode" : "prefill");
   if (T == 0) return ok();
   st = run_stage(stage, a);
+  if (st != WIDE_OK) return st;
+  return ok();
+}
+
+WIDE_API size_t wide_decode_weights_size(int32_t d, int32_t d_ff) {
+  if (d <= 0 || d_ff <= 0 || d % 64 != 0 || d_ff % 64 != 0 || (int64_t)d * d_ff >= (1ll << 30))
+    return 0;
+  return 3 * prep_region(d, d_ff);
+}
+
+WIDE_API wide_status_t wide_decode_prepare_weights(const void* Wgate, const void* Wup,
+                                                   const void* Wdown, int32_t d, int32_t d_ff,
+                                                   void* prepared, size_t prepared_bytes,
+                                                   void* stream) {
+  if (!Wgate || !Wup || !Wdown || !prepared)
+    return fail(WIDE_ERR_NULL, "Wgate, Wup, Wdown and prepared must be non-NULL");
+  const size_t need = wide_decode_weights_size(d, d_ff);
+  if (need == 0)
+    return fail(WIDE_ERR_SHAPE, "need d, d_ff >= 64, multiples of 64, d*d_ff < 2^30 (d=%d d_ff=%d)",
+                d, d_ff);
+  if (!aligned16(Wgate) || !aligned16(Wup) || !aligned16(Wdown))
+    return fail(WIDE_ERR_ALIGN, "Wgate, Wup and Wdown must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(prepared) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "prepared must be 256-byte aligned");
+  if (prepared_bytes < need)
+    return fail(WIDE_ERR_WORKSPACE, "prepared has %zu bytes, needs %zu", prepared_bytes, need);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* out = static_cast<char*>(prepared);
+  const size_t R = prep_region(d, d_ff);
+  hipError_t e = wide::launch_decode_pack_bf16((const uint16_t*)Wgate, d_ff, d, (uint16_t*)out, s);
+  if (e == hipSuccess)
+    e = wide::launch_decode_pack_bf16((const uint16_t*)Wup, d_ff, d, (uint16_t*)(out + R), s);
+  if (e == hipSuccess)
+    e = wide::launch_decode_pack_bf16((const uint16_t*)Wdown, d, d_ff, (uint16_t*)(out + 2 * R), s);
+  if (e != hipSuccess) return hip_status(e, "weight packing launch");
+  return ok();
+}
+
+WIDE_API wide_status_t wide_ffn_decode_prepared(const void* X, const void* Wgate, const void* Wup,
+                                                const void* Wdown, const void* prepared,
+                                                const uint8_t* mask, int32_t T, int32_t d,
+                                                int32_t d_ff, int32_t G, void* Y, void* H_out,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, WIDE_BF16, Y, H_out, workspace,
+         workspace_bytes, WIDE_FLAG_FORCE_DECODE, static_cast<hipStream_t>(stream)};
+  bool dec = false;
+  wide_status_t st = validate(a, &dec);
+  if (st != WIDE_OK) return st;
+  if (!prepared) return fail(WIDE_ERR_NULL, "prepared must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(prepared) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "prepared must be 256-byte aligned");
+  a.prep = prepared;
+  if (T == 0) return ok();
+  st = run_stage(WIDE_STAGE_DECODE_GATE_UP, a);
+  if (st != WIDE_OK) return st;
+  st = run_stage(WIDE_STAGE_DECODE_DOWN, a);
   if (st != WIDE_OK) return st;
   return ok();
 }

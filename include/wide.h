@@ -166,6 +166,45 @@ wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const void* Wgat
                              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * Decode with operand-order weights (bf16). The decode GEMV kernels that run
+ * on the matrix cores (T > 2, or shapes the whole-row kernels do not take)
+ * load their weight operands as 16 rows x 32 columns; in the nn.Linear
+ * layout that is 16 separate 64-byte pieces per load. A copy of the weights
+ * in operand order makes each such load one contiguous 1 KB block. (The
+ * pages give decoding its own fast path and GEMV variants for small M: WIDE
+ * paper Sec. 1 and App. B, GEMM-MN / GEMM-K; the layout is chosen here for
+ * the gfx950 MFMA operand shape.)
+ *
+ * wide_decode_weights_size - bytes of the copy for [d_ff, d] Wgate and Wup and
+ *   [d, d_ff] Wdown: three regions of d * d_ff bf16, each 256-byte aligned.
+ *   Returns 0 unless d and d_ff are multiples of 64 and d * d_ff < 2^30.
+ *
+ * wide_decode_prepare_weights - writes the copy (device, caller-owned,
+ *   256-byte aligned, >= wide_decode_weights_size bytes) from the nn.Linear
+ *   weights on `stream`. Region r holds matrix r (Wgate, Wup, Wdown) of R rows
+ *   and C columns as 1 KB blocks ordered by 16-row block, then by 32-column
+ *   slice; within block (rb, kc) lane l's 16 bytes (at byte 16 l) are row
+ *   16 rb + l % 16, columns 32 kc + 8 (l / 16) .. + 7. A pure permutation: no
+ *   value changes. Run it again whenever the weights change.
+ *
+ * wide_ffn_decode_prepared - wide_ffn_forward forced onto the decode path
+ *   (bf16, 0 <= T <= 16; same arguments, workspace and results, bit for bit),
+ *   with the matrix-core kernels reading `prepared` instead of Wgate, Wup and
+ *   Wdown. The whole-row kernels (T <= 2 at shapes they take) still read the
+ *   nn.Linear weights, so both must be passed. Errors as wide_ffn_forward,
+ *   plus WIDE_ERR_NULL / WIDE_ERR_ALIGN for `prepared`.
+ */
+size_t wide_decode_weights_size(int32_t d, int32_t d_ff);
+wide_status_t wide_decode_prepare_weights(const void* Wgate, const void* Wup, const void* Wdown,
+                                          int32_t d, int32_t d_ff, void* prepared,
+                                          size_t prepared_bytes, void* stream);
+wide_status_t wide_ffn_decode_prepared(const void* X, const void* Wgate, const void* Wup,
+                                       const void* Wdown, const void* prepared,
+                                       const uint8_t* mask, int32_t T, int32_t d, int32_t d_ff,
+                                       int32_t G, void* Y, void* H_out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * The two group-masked GEMM families the FFN kernels are built from, exposed
  * on their own (WIDE paper App. B, "Implementation of GEMM-MN" and
  * "Implementation of GEMM-K"). C = A B^T with A [M, K] and B [N, K]; a mask

@@ -287,3 +287,45 @@ def test_attention_workspace_sizes(lib):
     assert (T // 128) * Hq * (dh + 2) * 4 <= d <= (T // 128) * Hq * (dh + 2) * 4 + 256
     assert lib.wide_attention_decode_workspace_size(0, Hq, dh) == 0
     assert lib.wide_attention_decode_workspace_size(T, Hq, 64) == 0
+
+
+# ---------------------------------------------------------------- operand-order decode weights
+
+def test_decode_weights_size(lib):
+    d, d_ff = 4096, 14336
+    assert lib.wide_decode_weights_size(d, d_ff) == 3 * d * d_ff * 2
+    assert lib.wide_decode_weights_size(4096 + 32, d_ff) == 0
+    assert lib.wide_decode_weights_size(d, 0) == 0
+    assert lib.wide_decode_weights_size(32768, 32768) == 0  # d * d_ff >= 2^30
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Wg=None), _lib.WIDE_ERR_NULL),
+    (dict(out=None), _lib.WIDE_ERR_NULL),
+    (dict(d=100), _lib.WIDE_ERR_SHAPE),
+    (dict(Wu=FAKE + 8), _lib.WIDE_ERR_ALIGN),
+    (dict(out=FAKE + 16), _lib.WIDE_ERR_ALIGN),
+    (dict(nbytes=1024), _lib.WIDE_ERR_WORKSPACE),
+])
+def test_decode_prepare_validation(lib, kw, status):
+    a = dict(Wg=FAKE, Wu=FAKE, Wd=FAKE, d=256, d_ff=1024, out=FAKE, nbytes=1 << 40)
+    a.update(kw)
+    assert lib.wide_decode_prepare_weights(a["Wg"], a["Wu"], a["Wd"], a["d"], a["d_ff"], a["out"],
+                                           a["nbytes"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prep=None), _lib.WIDE_ERR_NULL),
+    (dict(prep=FAKE + 16), _lib.WIDE_ERR_ALIGN),
+    (dict(T=17), _lib.WIDE_ERR_UNSUPPORTED),   # decode only: T <= 16
+    (dict(X=None), _lib.WIDE_ERR_NULL),
+    (dict(G=8), _lib.WIDE_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), _lib.WIDE_ERR_WORKSPACE),
+])
+def test_decode_prepared_validation(lib, kw, status):
+    a = dict(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, prep=FAKE, mask=FAKE, T=4, d=256, d_ff=1024,
+             G=64, Y=FAKE, H=None, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    assert lib.wide_ffn_decode_prepared(a["X"], a["Wg"], a["Wu"], a["Wd"], a["prep"], a["mask"],
+                                        a["T"], a["d"], a["d_ff"], a["G"], a["Y"], a["H"], a["ws"],
+                                        a["ws_bytes"], None) == status
