@@ -402,9 +402,12 @@ def bench_attention_decode(torch, wide, d, w, steps: int):
     """One decoding step over the T-token cache (query at position T - 1),
     half of the KV groups kept, against every group kept and torch's SDPA for
     one query. A graph of 16 calls is replayed (the binding's host-side checks
-    would otherwise dominate); bytes = the kept groups' K and V rows."""
+    would otherwise dominate), the calls rotating over 8 copies of the cache so
+    each reads HBM rather than the last call's cache lines; bytes = the kept
+    groups' K and V rows."""
     dev = "cuda:0"
     q = d["Q"][w.T - 1].contiguous()
+    kv = [(d["K"], d["V"])] + [(d["K"].clone(), d["V"].clone()) for _ in range(7)]
     keep = torch.tensor([1, 0] * (w.Hk // 2) + [1] * (w.Hk % 2), dtype=torch.uint8, device=dev)
     ones = torch.ones_like(keep)
     O = torch.empty((w.Hq * w.dh,), dtype=torch.bfloat16, device=dev)
@@ -412,13 +415,13 @@ def bench_attention_decode(torch, wide, d, w, steps: int):
                      device=dev)
     res = {}
     for name, m in (("half_groups", keep), ("all_groups", ones)):
-        call = lambda: wide.attention_decode(q, d["K"], d["V"], m, w.Hq, w.Hk, O=O,  # noqa: E731
-                                             workspace=ws)
-        call()
+        for K, V in kv:
+            wide.attention_decode(q, K, V, m, w.Hq, w.Hk, O=O, workspace=ws)
 
         def calls16():
-            for _ in range(16):
-                call()
+            for i in range(16):
+                K, V = kv[i % len(kv)]
+                wide.attention_decode(q, K, V, m, w.Hq, w.Hk, O=O, workspace=ws)
         us = graph_step_ms(torch, calls16, max(steps, 10)) / 16 * 1e3
         nbytes = int(m.sum()) * 2 * w.T * w.dh * 2
         res[name] = {"us": round(us, 2), "kv_bytes": nbytes,
@@ -439,6 +442,7 @@ def bench_attention_decode(torch, wide, d, w, steps: int):
         del k, v
     except Exception as e:
         res["sdpa_error"] = f"{type(e).__name__}: {str(e)[:200]}"
+    del kv
     return res
 
 
