@@ -448,30 +448,34 @@ def bench_attention_decode(torch, wide, d, w, steps: int):
 
 def bench_router(torch, wide, dg, steps: int):
     """The bottleneck router (mask production) at the Llama3.1-8B FFN shape:
-    D = 4096, r = 32, 112 groups, SiLU, for the prefill length and T = 1."""
+    D = 4096, r = 32, 112 groups, SiLU, for the prefill length and T = 1,
+    over 8 copies of X in turn."""
     out = {}
     dev = "cuda:0"
     D, r, ng = 4096, 32, 112
     rw = dg.make_router_weights(7, D, r, ng)
     W1, W2 = rw["W1"].to(dev), rw["W2"].to(dev)
     for T in (16384, 1):
-        X = dg.to_dtype(dg.normal_f32(8, (T, D)), "bf16").to(dev)
+        X0 = dg.to_dtype(dg.normal_f32(8, (T, D)), "bf16").to(dev)
+        # the calls rotate over 8 copies of X, so each reads HBM rather than
+        # the previous call's lines in the 256 MB MALL
+        xs = [X0] + [X0.clone() for _ in range(7)]
         mask = torch.empty((T, ng), dtype=torch.uint8, device=dev)
-        call = lambda: wide.router_forward(X, W1, W2, "silu", mask=mask)
-        for _ in range(3):
-            call()
+        for X in xs:
+            wide.router_forward(X, W1, W2, "silu", mask=mask)
+
         # replay of a graph holding 16 calls: the binding's host-side checks
         # (and one graph launch per call) would dominate at T = 1
         def calls16():
-            for _ in range(16):
-                call()
+            for i in range(16):
+                wide.router_forward(xs[i % len(xs)], W1, W2, "silu", mask=mask)
         ms = graph_step_ms(torch, calls16, max(steps, 10)) / 16
         nbytes = T * D * 2 + T * ng + r * D * 2 + 2 * ng * r * 2
         out[f"T{T}"] = {"us": round(ms * 1e3, 2), "bytes": nbytes,
                         "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                         "execute_fraction": round(float(mask.float().mean()), 4)}
-        del X, mask
+        del xs, X0, mask
     return out
 
 
