@@ -120,7 +120,8 @@ class FfnCall:
             X, Wg, Wu, Wd, mask = self.args
             _lib.check(_lib.load().wide_ffn_decode_prepared(
                 X.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), self.prepared.data_ptr(),
-                mask.data_ptr(), self.T, self.d, self.d_ff, self.G, self.Y.data_ptr(),
+                self.prepared.numel() * self.prepared.element_size(), mask.data_ptr(), self.T,
+                self.d, self.d_ff, self.G, self.Y.data_ptr(),
                 None if self.H is None else self.H.data_ptr(), self.workspace.data_ptr(),
                 self.ws_bytes, _stream_ptr(X.device)))
         else:

@@ -54,8 +54,8 @@ SIGNATURES = {
     "wide_ffn_stage": (ctypes.c_int, [ctypes.c_int] + _FFN_ARGS),
     "wide_decode_weights_size": (_sz, [_i32, _i32]),
     "wide_decode_prepare_weights": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _sz, _p]),
-    "wide_ffn_decode_prepared": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p,
-                                                _p, _p, _sz, _p]),
+    "wide_ffn_decode_prepared": (ctypes.c_int, [_p, _p, _p, _p, _p, _sz, _p, _i32, _i32, _i32,
+                                                _i32, _p, _p, _p, _sz, _p]),
     "wide_gemm_workspace_size": (_sz, [_i32, _i32]),
     "wide_gemm_mn": (ctypes.c_int, _GEMM_ARGS),
     "wide_gemm_k": (ctypes.c_int, _GEMM_ARGS),

@@ -323,7 +323,8 @@ WIDE_API wide_status_t wide_decode_prepare_weights(const void* Wgate, const void
 
 WIDE_API wide_status_t wide_ffn_decode_prepared(const void* X, const void* Wgate, const void* Wup,
                                                 const void* Wdown, const void* prepared,
-                                                const uint8_t* mask, int32_t T, int32_t d,
+                                                size_t prepared_bytes, const uint8_t* mask,
+                                                int32_t T, int32_t d,
                                                 int32_t d_ff, int32_t G, void* Y, void* H_out,
                                                 void* workspace, size_t workspace_bytes,
                                                 void* stream) {
@@ -335,6 +336,9 @@ WIDE_API wide_status_t wide_ffn_decode_prepared(const void* X, const void* Wgate
   if (!prepared) return fail(WIDE_ERR_NULL, "prepared must be non-NULL");
   if ((reinterpret_cast<uintptr_t>(prepared) & 255u) != 0)
     return fail(WIDE_ERR_ALIGN, "prepared must be 256-byte aligned");
+  const size_t need = wide_decode_weights_size(d, d_ff);
+  if (prepared_bytes < need)
+    return fail(WIDE_ERR_WORKSPACE, "prepared has %zu bytes, needs %zu", prepared_bytes, need);
   a.prep = prepared;
   if (T == 0) return ok();
   st = run_stage(WIDE_STAGE_DECODE_GATE_UP, a);

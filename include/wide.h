@@ -191,8 +191,10 @@ wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const void* Wgat
  *   (bf16, 0 <= T <= 16; same arguments, workspace and results, bit for bit),
  *   with the matrix-core kernels reading `prepared` instead of Wgate, Wup and
  *   Wdown. The whole-row kernels (T <= 2 at shapes they take) still read the
- *   nn.Linear weights, so both must be passed. Errors as wide_ffn_forward,
- *   plus WIDE_ERR_NULL / WIDE_ERR_ALIGN for `prepared`.
+ *   nn.Linear weights, so both must be passed. `prepared_bytes` is the size
+ *   of `prepared`. Errors as wide_ffn_forward, plus WIDE_ERR_NULL /
+ *   WIDE_ERR_ALIGN for `prepared` and WIDE_ERR_WORKSPACE when it is smaller
+ *   than wide_decode_weights_size(d, d_ff).
  */
 size_t wide_decode_weights_size(int32_t d, int32_t d_ff);
 wide_status_t wide_decode_prepare_weights(const void* Wgate, const void* Wup, const void* Wdown,
@@ -200,7 +202,8 @@ wide_status_t wide_decode_prepare_weights(const void* Wgate, const void* Wup, co
                                           size_t prepared_bytes, void* stream);
 wide_status_t wide_ffn_decode_prepared(const void* X, const void* Wgate, const void* Wup,
                                        const void* Wdown, const void* prepared,
-                                       const uint8_t* mask, int32_t T, int32_t d, int32_t d_ff,
+                                       size_t prepared_bytes, const uint8_t* mask, int32_t T,
+                                       int32_t d, int32_t d_ff,
                                        int32_t G, void* Y, void* H_out, void* workspace,
                                        size_t workspace_bytes, void* stream);
 

@@ -321,11 +321,13 @@ def test_decode_prepare_validation(lib, kw, status):
     (dict(X=None), _lib.WIDE_ERR_NULL),
     (dict(G=8), _lib.WIDE_ERR_UNSUPPORTED),
     (dict(ws_bytes=16), _lib.WIDE_ERR_WORKSPACE),
+    (dict(prep_bytes=3 * 256 * 1024 * 2 - 1), _lib.WIDE_ERR_WORKSPACE),
 ])
 def test_decode_prepared_validation(lib, kw, status):
-    a = dict(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, prep=FAKE, mask=FAKE, T=4, d=256, d_ff=1024,
-             G=64, Y=FAKE, H=None, ws=FAKE, ws_bytes=1 << 40)
+    a = dict(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, prep=FAKE, prep_bytes=1 << 40, mask=FAKE, T=4,
+             d=256, d_ff=1024, G=64, Y=FAKE, H=None, ws=FAKE, ws_bytes=1 << 40)
     a.update(kw)
-    assert lib.wide_ffn_decode_prepared(a["X"], a["Wg"], a["Wu"], a["Wd"], a["prep"], a["mask"],
-                                        a["T"], a["d"], a["d_ff"], a["G"], a["Y"], a["H"], a["ws"],
-                                        a["ws_bytes"], None) == status
+    assert lib.wide_ffn_decode_prepared(a["X"], a["Wg"], a["Wu"], a["Wd"], a["prep"],
+                                        a["prep_bytes"], a["mask"], a["T"], a["d"], a["d_ff"],
+                                        a["G"], a["Y"], a["H"], a["ws"], a["ws_bytes"],
+                                        None) == status
