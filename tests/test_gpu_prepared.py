@@ -109,3 +109,33 @@ def test_prepared_copy_follows_weight_changes():
     torch.cuda.synchronize()
     assert torch.equal(Ya, Ystale)
     assert torch.allclose(Yb.float(), 2 * Ya.float(), rtol=1e-2, atol=1e-3)
+
+
+def test_prepared_decode_graph_replay_matches_eager():
+    # the prepared call allocates nothing and never synchronises, so it can be
+    # captured; every replay (with eager work in between) equals the eager call
+    T, d, d_ff, G = 12, 512, 1024, 128
+    inp = dg.random_small(91, T, d, d_ff, G, "bf16", 0.5, wscale=0.05)
+    x = {k: v.to(DEV) for k, v in inp.items()}
+    prep = wide.decode_prepare_weights(x["Wg"], x["Wu"], x["Wd"])
+    call = wide.FfnCall(x["X"], x["Wg"], x["Wu"], x["Wd"], x["mask"], G, prepared=prep)
+    eager = call.run().clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call.run()
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        call.Y.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.Y, eager), f"replay {i} differs from eager"
+    # the mask is read at replay time
+    x["mask"].zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert bool((call.Y == 0).all())
