@@ -343,18 +343,20 @@ constexpr int kSkWaves = kSkThreads / 64;
 constexpr int kSkU = 4;  // chunks per batch per wave
 constexpr int kMaxChunks = 2048;  // d_ff / 32 limit
 
-// HALVES (G == 16): a live 32-channel chunk can hold a group that no token
-// executes; its H was never written, so those lanes use zeros instead.
+// PIECES (G % 32 != 0): a live 32-channel chunk can also hold a group that no
+// token executes (its H was never written), so each lane's 8-channel piece is
+// tested on its own group and uses zeros there. A piece never straddles two
+// groups: G is a multiple of 16 and pieces start at multiples of 8.
 // PACKED: Wd is the operand-order copy (see gate_up_unit): the 16 rows x 32
 // channels of each operand are one contiguous 1 KB block.
-template <bool HALVES, bool PACKED = false>
+template <bool PIECES, bool PACKED = false>
 __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G, float* __restrict__ part) {
   __shared__ uint16_t s_chunks[kMaxChunks];
   __shared__ int s_wave_cnt[kSkWaves];
   __shared__ float s_red[kSkWaves][64][16];
-  __shared__ uint8_t s_gact[kMaxGroups];  // G < 32: group executed by some token
+  __shared__ uint8_t s_gact[kMaxGroups];  // PIECES: group executed by some token
   const int ng = d_ff / G;
   const int n0 = (int)(blockIdx.x / kDecodeDownSplit) * kSkRows;
   const int split = (int)(blockIdx.x % kDecodeDownSplit);
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
         hi = (c * 32 + 31) / G;
       },
       s_chunks, s_wave_cnt);
-  if (HALVES) {
+  if (PIECES) {
     for (int g = tid; g < ng; g += kSkThreads) {
       uint32_t m = 0;
 #pragma unroll
@@ -404,13 +406,13 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   const int nb = mine / kSkU;
   u32x4 a[2][4][kSkU], bb[2][kSkU];
   auto chunk_k = [&](int i) { return (int)s_chunks[lo + wave + kSkWaves * i] * 32; };
-  // H loads are unconditional (inside H's bounds). With HALVES, the lanes of
+  // H loads are unconditional (inside H's bounds). With PIECES, the lanes of
   // a group no token executes get an all-zero AND mask, applied when the
   // fragment is used, so nothing unwritten reaches the sums and no load or
   // move of a loaded value sits in a branch.
   uint32_t hm[2][kSkU];
   auto h_mask = [&](int k) -> uint32_t {
-    return HALVES ? (s_gact[(k + koff) >> 4] ? 0xFFFFFFFFu : 0u) : 0xFFFFFFFFu;
+    return PIECES ? (s_gact[(k + koff) / G] ? 0xFFFFFFFFu : 0u) : 0xFFFFFFFFu;
   };
   auto masked = [](const u32x4& v, uint32_t m) {
     const u32x4 mv = {m, m, m, m};
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   auto mma_batch = [&](int set) {
 #pragma unroll
     for (int q = 0; q < kSkU; ++q) {
-      const bf16x8 hv = HALVES ? masked(bb[set][q], hm[set][q]) : __builtin_bit_cast(bf16x8, bb[set][q]);
+      const bf16x8 hv = PIECES ? masked(bb[set][q], hm[set][q]) : __builtin_bit_cast(bf16x8, bb[set][q]);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
         acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[set][rb][q]),
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   }
   for (int i = nb * kSkU; i < mine; ++i) {
     const int k = chunk_k(i);
-    const bf16x8 hv = HALVES ? masked(ld16(ph + k), h_mask(k)) : __builtin_bit_cast(bf16x8, ld16(ph + k));
+    const bf16x8 hv = PIECES ? masked(ld16(ph + k), h_mask(k)) : __builtin_bit_cast(bf16x8, ld16(ph + k));
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ld16(pw[rb] + kScale * k)),
@@ -808,17 +810,18 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                          stream, H, Wd, mask, T, d, d_ff, G, Y);
     return hipGetLastError();
   }
-  // G is a multiple of 16: below 32 it is 16, the case whose chunks can
-  // straddle an executed and a skipped group
+  // G is a multiple of 16; unless it is a multiple of 32, a 32-channel chunk
+  // can straddle an executed and a skipped group (G = 16, 48, 80, ...)
   if (G % 16 != 0) return hipErrorInvalidValue;
+  const bool pieces = G % 32 != 0;
   const dim3 grid((d / kSkRows) * kDecodeDownSplit);
-  if (Wd_op != nullptr && G == 16)
+  if (Wd_op != nullptr && pieces)
     hipLaunchKernelGGL((decode_down_splitk_kernel<true, true>), grid, dim3(kSkThreads), 0, stream, H,
                        Wd_op, mask, T, d, d_ff, G, part);
   else if (Wd_op != nullptr)
     hipLaunchKernelGGL((decode_down_splitk_kernel<false, true>), grid, dim3(kSkThreads), 0, stream,
                        H, Wd_op, mask, T, d, d_ff, G, part);
-  else if (G == 16)
+  else if (pieces)
     hipLaunchKernelGGL(decode_down_splitk_kernel<true>, grid, dim3(kSkThreads), 0, stream, H, Wd,
                        mask, T, d, d_ff, G, part);
   else

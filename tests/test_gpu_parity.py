@@ -149,6 +149,8 @@ SMALL = [
     (16, 512, 1024, 128, "bf16", 0.5, wide.WIDE_FLAG_FORCE_PREFILL),
     (200, 256, 512, 64, "f32", 0.6, 0),
     (5, 128, 256, 16, "f32", 0.5, 0),
+    (300, 256, 1536, 48, "bf16", 0.5, 0),     # G = 48: groups straddle the 64-channel K-blocks
+    (40, 128, 960, 80, "f32", 0.5, 0),
 ]
 
 
@@ -188,6 +190,9 @@ def test_decode_path_vs_oracle(T, G):
     (3, 1024, 2048, 16), (5, 1024, 2048, 16), (16, 512, 2048, 16), (1, 256, 2048, 16),
     (2, 8192, 1024, 64), (1, 512, 18432, 128), (2, 512, 14336, 128), (1, 512, 18496, 64),
     (2, 512, 14400, 64),
+    # G = 48: a 32-channel chunk can hold an executed and a skipped group at any
+    # offset, not only at its halves (matrix-core GEMVs at both T)
+    (5, 512, 1536, 48), (1, 576, 1536, 48), (16, 512, 1536, 48), (3, 256, 960, 80),
 ])
 def test_decode_never_reads_unwritten_h(T, d, d_ff, G):
     inp = dg.random_small(500 + T + G, T, d, d_ff, G, "bf16", 0.3, wscale=0.05)
@@ -235,17 +240,20 @@ def test_decode_edge_masks(T):
             assert bool((Y == 0).all())
 
 
-@pytest.mark.parametrize("T,G,flags", [(700, 128, 0), (300, 16, 0), (3, 128, 0), (12, 64, 0),
-                                       (12, 64, wide.WIDE_FLAG_FORCE_PREFILL)])
-def test_result_does_not_depend_on_h_out(T, G, flags):
+@pytest.mark.parametrize("T,G,d_ff,flags", [
+    (700, 128, 1024, 0), (300, 16, 1024, 0), (3, 128, 1024, 0), (12, 64, 1024, 0),
+    (12, 64, 1024, wide.WIDE_FLAG_FORCE_PREFILL), (300, 48, 1536, 0), (7, 48, 1536, 0),
+    (7, 48, 1536, wide.WIDE_FLAG_FORCE_PREFILL),
+])
+def test_result_does_not_depend_on_h_out(T, G, d_ff, flags):
     """Y with H kept in the workspace equals Y with H returned, bit for bit."""
-    d, d_ff = 256, 1024
+    d = 256
     inp = to_dev(dg.random_small(400 + T, T, d, d_ff, G, "bf16", 0.5, wscale=0.05))
     a = wide.FfnCall(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G, flags=flags)
     b = wide.FfnCall(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G, return_h=True,
                      flags=flags)
-    # workspace and outputs start as garbage
-    a.workspace.fill_(0xAB)
+    # workspace (H included) holds NaN bits and the outputs start as garbage
+    a.workspace.fill_(0xFF)
     a.Y.fill_(3.0)
     b.H.fill_(-5.0)
     Ya = a.run().clone()
@@ -339,27 +347,50 @@ def test_hip_graph_replay_matches_eager():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-def sample_rows(T, counts_tile_boundaries, n_random, seed):
+def sample_rows(T, must, n_random, seed, min_rows=0):
+    """Token rows to compare: 0, T/2, T-1, the `must` rows, and random ones
+    (at least n_random, and enough for min_rows rows in all)."""
     rng = np.random.default_rng(seed)
     rows = {0, T - 1, T // 2}
-    rows.update(int(r) for r in counts_tile_boundaries)
-    rows.update(int(r) for r in rng.choice(T, size=min(n_random, T), replace=False))
-    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+    rows.update(int(r) for r in must)
+    rows = {r for r in rows if 0 <= r < T}
+    rest = np.setdiff1d(np.arange(T), np.fromiter(rows, dtype=np.int64, count=len(rows)))
+    n = min(len(rest), max(n_random, min_rows - len(rows)))
+    rows.update(int(r) for r in rng.choice(rest, size=n, replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
 
 
-def full_size_check(w, n_random, mask_kind=None):
+def full_size_check(w, n_random, mask_kind=None, min_rows=0):
+    """One workload at its full size, in the launch configuration the bench times.
+
+    * Y at a seeded sample of tokens against the oracle (one token from the
+      boundary tile of EVERY group, i.e. its last active token, plus the first,
+      middle and last tokens and random ones);
+    * H exactly zero at every masked channel (whole H);
+    * the call without H_out, with the workspace (where H then lives) holding
+      NaN bits, gives the same Y bit for bit (whole Y): the bench times that
+      call, in which skipped (token, group) pairs of H are never written;
+    * a second identical call gives the same Y bit for bit.
+    """
     inp = dg.make_inputs(w, mask_kind=mask_kind)
     m = inp["mask"].numpy()
     d = to_dev(inp)
     call = wide.FfnCall(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], w.G, return_h=True)
     Y = call.run()
+    bare = wide.FfnCall(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], w.G)
+    bare.workspace.fill_(0xFF)
+    Yb = bare.run()
     torch.cuda.synchronize()
-    # tokens at the boundary tile of a few groups (last active token of the prefix)
+    assert torch.equal(Y.view(torch.int16), Yb.view(torch.int16)), \
+        f"{w.name}: Y without H_out differs from Y with H_out"
+    del bare
     perm, counts, _ = oracle.reorder(m, wide.WIDE_TOKEN_TILE)
-    bnd = [perm[g, c - 1] for g, c in enumerate(counts[:8]) if c > 0]
-    rows = sample_rows(w.T, bnd, n_random, seed=w.seed)
+    bnd = [perm[g, c - 1] for g, c in enumerate(counts) if c > 0]
+    rows = sample_rows(w.T, bnd, n_random, seed=w.seed, min_rows=min_rows)
+    assert set(bnd) <= set(rows.tolist())
     Hs, Ys = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], m, w.G, rows=rows)
     err = rel_err(Y[torch.from_numpy(rows).to(DEV)], Ys)
+    sys.__stderr__.write(f"[gpu-case] {w.name}: {len(rows)} rows, rel err {err:.3e}\n")
     assert err <= TOL[w.dtype], f"{w.name}: rel err {err}"
     check_h_zeros(call.H, inp["mask"], w.G)
     Y2 = call.run().clone()
@@ -369,7 +400,7 @@ def full_size_check(w, n_random, mask_kind=None):
 
 
 def test_llama8b_prefill_full_size_sampled():
-    full_size_check(dg.LLAMA8B_PREFILL, n_random=48)
+    full_size_check(dg.LLAMA8B_PREFILL, n_random=48, min_rows=256)
 
 
 @pytest.mark.parametrize("w", [dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16], ids=lambda w: w.name)
@@ -378,7 +409,7 @@ def test_llama8b_decode_full_size(w):
 
 
 def test_qwen14b_skewed_full_size_sampled():
-    full_size_check(dg.QWEN14B_SKEW, n_random=24)
+    full_size_check(dg.QWEN14B_SKEW, n_random=24, min_rows=256)
 
 
 def test_qwen14b_all_zero_and_all_ones():
@@ -400,8 +431,29 @@ def test_qwen14b_all_zero_and_all_ones():
     assert bool((Yz == 0).all()) and bool((Hz == 0).all())
 
 
-@pytest.mark.parametrize("cell_G,T", [(16, 2048), (512, 2048), (128, 8192), (64, 1)])
-def test_llama3b_sweep_cells_sampled(cell_G, T):
-    cells = [c for c in dg.llama3b_sweep_cells() if c.G == cell_G and c.T == T]
-    for w in cells[1:3]:  # two sparsity levels per (G, T)
-        full_size_check(w, n_random=12)
+# Llama3.2-3B-shaped sweep cells: every G of the sweep and every sparsity level
+# at a prefill length (T = 2048 or 8192), and T = 1 at three G.
+SWEEP_CELLS = [
+    (16, 10, 2048), (32, 25, 8192), (64, 50, 2048), (128, 70, 8192), (256, 10, 8192),
+    (512, 70, 2048), (128, 50, 8192), (16, 70, 8192), (512, 25, 8192), (256, 50, 2048),
+    (64, 50, 1), (256, 25, 1), (16, 10, 1),
+]
+
+
+def _sweep_cell(G, s, T):
+    for c in dg.llama3b_sweep_cells():
+        if c.G == G and round((1 - c.density) * 100) == s and c.T == T:
+            return c
+    raise KeyError((G, s, T))
+
+
+@pytest.mark.parametrize("G,s,T", SWEEP_CELLS, ids=lambda v: str(v))
+def test_llama3b_sweep_cell_sampled(G, s, T):
+    full_size_check(_sweep_cell(G, s, T), n_random=16)
+
+
+def test_sweep_cells_cover_every_g_and_sparsity():
+    pre = [(G, s) for G, s, T in SWEEP_CELLS if T > 1]
+    assert {G for G, _ in pre} == {16, 32, 64, 128, 256, 512}
+    assert {s for _, s in pre} == {10, 25, 50, 70}
+    assert len({G for G, _, T in SWEEP_CELLS if T == 1}) >= 2

@@ -58,7 +58,7 @@ CASES = [
     (16, 512, 1024, 128, 0.5), (5, 512, 1024, 128, 0.5), (3, 512, 1024, 128, 0.5),
     (16, 512, 1024, 16, 0.5), (9, 512, 1024, 32, 0.4), (1, 576, 1024, 128, 0.5),
     (2, 576, 512, 16, 0.6), (1, 512, 1024, 128, 0.5), (16, 512, 1024, 128, 0.0),
-    (16, 512, 1024, 128, 1.0),
+    (16, 512, 1024, 128, 1.0), (5, 512, 1536, 48, 0.3), (1, 576, 1536, 48, 0.3),
 ]
 
 
@@ -139,3 +139,28 @@ def test_prepared_decode_graph_replay_matches_eager():
     g.replay()
     torch.cuda.synchronize()
     assert bool((call.Y == 0).all())
+
+
+# No H_out: the workspace (H included) holds NaN bits. With G = 16 or 48 a
+# 32-channel chunk of the down GEMV can hold a group no token executes, whose
+# H is never written; Y must equal the unprepared decode bit for bit and be
+# finite.
+@pytest.mark.parametrize("T,d,d_ff,G", [(5, 512, 1536, 48), (1, 576, 1536, 48), (16, 512, 1024, 16),
+                                        (3, 512, 960, 80)])
+def test_prepared_never_reads_unwritten_h(T, d, d_ff, G):
+    inp = dg.random_small(900 + T + G, T, d, d_ff, G, "bf16", 0.3, wscale=0.05)
+    x = {k: v.to(DEV) for k, v in inp.items()}
+    prep = wide.decode_prepare_weights(x["Wg"], x["Wu"], x["Wd"])
+    a = wide.FfnCall(x["X"], x["Wg"], x["Wu"], x["Wd"], x["mask"], G,
+                     flags=wide.WIDE_FLAG_FORCE_DECODE)
+    b = wide.FfnCall(x["X"], x["Wg"], x["Wu"], x["Wd"], x["mask"], G, prepared=prep)
+    a.workspace.fill_(0xFF)
+    b.workspace.fill_(0xFF)
+    Ya = a.run().clone()
+    Yb = b.run().clone()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Yb.float()).all())
+    assert torch.equal(Ya.view(torch.int16), Yb.view(torch.int16))
+    _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], inp["mask"], G)
+    err = np.max(np.abs(Yb.float().cpu().numpy() - Yref)) / max(np.max(np.abs(Yref)), 1e-30)
+    assert err <= 2e-2
