@@ -510,9 +510,29 @@ def achievable_peaks(torch, steps: int = 10):
             "device_copy_GBps": round(2 * COPY_BYTES / (cms * 1e-3) / 1e9, 1)}
 
 
+def host_cpus():
+    """What the host offers: the CPU model, the cores this process may run on
+    (sched affinity, as nproc reports) and the logical CPUs of the machine."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count() or 0
+    return {"cpu_model": cpu_model(), "nproc": nproc, "logical_cpus": os.cpu_count(),
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
-    """fp64 oracle on a seeded token sample, scaled to effective TFLOP/s."""
+    """fp64 oracle on a seeded token sample, scaled to effective TFLOP/s.
+
+    The oracle is rebuilt here with gcc -O3 -march=native (same arithmetic)
+    so the baseline uses this host's vector units."""
     import numpy as np
+    build = "gcc -O2 (prebuilt)"
+    try:
+        oracle.use_library(oracle.build_native(os.path.join(ROOT, "gpurun_out", "oracle_native")))
+        build = "gcc -O3 -march=native -fopenmp, built on this host"
+    except Exception as e:  # noqa: BLE001 - report, keep the -O2 build
+        log(f"native oracle build failed ({e}); timing the -O2 build")
     rng = np.random.default_rng(w.seed + 99)
     m = inp["mask"].numpy()
     x, wg, wu, wd = (inp[k].float().numpy() for k in ("X", "Wg", "Wu", "Wd"))
@@ -529,10 +549,12 @@ def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
     t = run(rows)
     active = int(m[rows].sum())
     flops = 6.0 * w.d * w.G * active
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": f"{n} of {w.T} tokens (seeded), fp64, {t:.1f} s; effective flops of the "
-                      f"sampled tokens' active groups"}
+    out = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "build": build,
+           "sample": f"{n} of {w.T} tokens (seeded), fp64, {t:.1f} s; effective flops of the "
+                     f"sampled tokens' active groups"}
+    out.update(host_cpus())
+    return out
 
 
 def decode_setup(torch, wide, dg, w, copies: int):

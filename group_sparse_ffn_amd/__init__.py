@@ -43,8 +43,10 @@ def decode_max_t() -> int:
     return int(_lib.load().wide_decode_max_t())
 
 
-def workspace_size(T: int, d: int, d_ff: int, G: int, dtype: torch.dtype) -> int:
-    return int(_lib.load().wide_ffn_workspace_size(T, d, d_ff, G, _DTYPES[dtype]))
+def workspace_size(T: int, d: int, d_ff: int, G: int, dtype: torch.dtype,
+                   h_out_given: bool = False) -> int:
+    return int(_lib.load().wide_ffn_workspace_size_for(T, d, d_ff, G, _DTYPES[dtype],
+                                                       1 if h_out_given else 0))
 
 
 def reorder_masks(mask: torch.Tensor, tile: int = WIDE_TOKEN_TILE):
@@ -95,7 +97,7 @@ class FfnCall:
                                           if return_h else None)
         if self.H is not None:
             _need_cuda("H", self.H)
-        nbytes = workspace_size(T, d, d_ff, G, X.dtype)
+        nbytes = workspace_size(T, d, d_ff, G, X.dtype, h_out_given=self.H is not None)
         if workspace is None:
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         self.workspace = workspace

@@ -50,6 +50,7 @@ _GEMM_ARGS = [_p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p, _sz, _p]
 SIGNATURES = {
     "wide_reorder_masks": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _p, _p, _p]),
     "wide_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int]),
+    "wide_ffn_workspace_size_for": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int, _i32]),
     "wide_ffn_forward": (ctypes.c_int, _FFN_ARGS),
     "wide_ffn_stage": (ctypes.c_int, [ctypes.c_int] + _FFN_ARGS),
     "wide_decode_weights_size": (_sz, [_i32, _i32]),

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void attention_vt_kernel(const uint16_t* __res
 
 }  // namespace
 
-int attention_tpad(int T) { return (T + kAtBK - 1) / kAtBK * kAtBK; }
+int64_t attention_tpad(int64_t T) { return (T + kAtBK - 1) / kAtBK * kAtBK; }
 
 hipError_t launch_attention_prefill_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                          const int32_t* perm, const int32_t* counts, int T, int Hq,
@@ -334,7 +334,7 @@ hipError_t launch_attention_prefill_bf16(const uint16_t* Q, const uint16_t* K, c
                                          uint16_t* Vt, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (dh != kAtDh || Hk <= 0 || Hq % Hk != 0) return hipErrorInvalidValue;
-  const int Tpad = attention_tpad(T);
+  const int Tpad = (int)attention_tpad(T);  // T * Hq * dh < 2^31 is checked by the caller
   hipLaunchKernelGGL(attention_vt_kernel, dim3(Tpad / 64, Hk), dim3(256), 0, stream, V, T, Tpad, Hk,
                      Vt);
   hipError_t e = hipGetLastError();

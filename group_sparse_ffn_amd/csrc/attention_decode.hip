@@ -221,9 +221,9 @@ __global__ __launch_bounds__(kDcSlices * kDcDh) void attention_decode_merge_kern
 
 }  // namespace
 
-int attention_decode_splits(int T) { return (T + kDcKeys - 1) / kDcKeys; }
-size_t attention_decode_part_floats(int T, int Hq) {
-  return (size_t)attention_decode_splits(T) * Hq * kDcRec;
+int64_t attention_decode_splits(int64_t T) { return (T + kDcKeys - 1) / kDcKeys; }
+size_t attention_decode_part_floats(int64_t T, int64_t Hq) {
+  return (size_t)(attention_decode_splits(T) * Hq * kDcRec);
 }
 
 hipError_t launch_attention_decode_bf16(const uint16_t* q, const uint16_t* K, const uint16_t* V,
@@ -232,7 +232,7 @@ hipError_t launch_attention_decode_bf16(const uint16_t* q, const uint16_t* K, co
                                         hipStream_t stream) {
   if (dh != kDcDh || Hk <= 0 || Hq % Hk != 0) return hipErrorInvalidValue;
   const int hpg = Hq / Hk;
-  const int nsplit = attention_decode_splits(T);
+  const int nsplit = (int)attention_decode_splits(T);
   if (T > 0) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
     const dim3 grid(nsplit, Hk), block(kDcThreads);

@@ -72,8 +72,9 @@ hipError_t launch_reorder_from_bits(const uint32_t* maskbits, int T, int ng, int
 hipError_t launch_pack_mask_bits(const uint8_t* mask, int T, int ng, uint32_t* maskbits,
                                  hipStream_t stream);
 
-// Keys of the transposed V copy per KV head (T rounded up to the key tile).
-int attention_tpad(int T);
+// Keys of the transposed V copy per KV head (T rounded up to the key tile;
+// 64-bit so that a size query with any int32 T cannot overflow).
+int64_t attention_tpad(int64_t T);
 
 // Head-group-pruned causal attention, prefill (dh = 128): V is transposed into
 // Vt [Hk, dh, attention_tpad(T)], then one workgroup per (query tile of the
@@ -87,8 +88,8 @@ hipError_t launch_attention_prefill_bf16(const uint16_t* Q, const uint16_t* K, c
 // One decoding step of the head-group-pruned attention (dh = 128, Hq/Hk in
 // {1, 2, 4, 8}): per (128-key split, kept KV group) fp32 partials into `part`
 // (attention_decode_part_floats(T, Hq) floats), then a per-head merge.
-int attention_decode_splits(int T);
-size_t attention_decode_part_floats(int T, int Hq);
+int64_t attention_decode_splits(int64_t T);
+size_t attention_decode_part_floats(int64_t T, int64_t Hq);
 hipError_t launch_attention_decode_bf16(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                                         const uint8_t* mask, int T, int Hq, int Hk, int dh,
                                         uint16_t* O, bool zero_inactive, float* part,

@@ -40,23 +40,36 @@ wide_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// An enum argument as the int the C caller passed. C lets a caller pass any
+// int for an enum parameter; reading a value outside the enumerators as a C++
+// enum is undefined, so every entry point reads its enum arguments through
+// this and validates the int.
+template <class E>
+int32_t raw(const E& e) {  // by reference: no enum-typed load
+  static_assert(sizeof(E) == sizeof(int32_t), "C enums are int-sized on this ABI");
+  int32_t v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t elt_size(wide_dtype_t dt) { return dt == WIDE_BF16 ? 2 : 4; }
+size_t elt_size(int32_t dt) { return dt == WIDE_BF16 ? 2 : 4; }
 
 // Workspace layout (each region 256-byte aligned):
 //   perm     int32  [ngroups, T]
 //   counts   int32  [ngroups]
 //   padded   int32  [ngroups]
 //   maskbits uint32 [ngroups, ceil(T/32)]
-//   H        dtype  [T, d_ff]   (used when the caller passes no H_out)
 //   part     fp32   [kDecodeDownSplit, T, d]   (T <= WIDE_DECODE_T_LIMIT only:
 //                   the decode down GEMV's partial sums)
+//   H        dtype  [T, d_ff]   (only when the caller passes no H_out; last, so
+//                   the other offsets do not depend on it)
 struct Layout {
   size_t perm, counts, padded, maskbits, h, part, total;
 };
 
-Layout layout(int64_t T, int64_t d, int64_t d_ff, int64_t G, wide_dtype_t dt) {
+Layout layout(int64_t T, int64_t d, int64_t d_ff, int64_t G, int32_t dt, bool with_h) {
   const int64_t ng = d_ff / G;
   const int64_t words = (T + 31) / 32;
   Layout L{};
@@ -69,10 +82,10 @@ Layout layout(int64_t T, int64_t d, int64_t d_ff, int64_t G, wide_dtype_t dt) {
   off = round_up(off + (size_t)ng * 4, 256);
   L.maskbits = off;
   off = round_up(off + (size_t)(ng * words) * 4, 256);
-  L.h = off;
-  off = round_up(off + (size_t)(T * d_ff) * elt_size(dt), 256);
   L.part = off;
   if (T <= WIDE_DECODE_T_LIMIT) off = round_up(off + (size_t)(wide::kDecodeDownSplit * T * d) * 4, 256);
+  L.h = off;
+  if (with_h) off = round_up(off + (size_t)(T * d_ff) * elt_size(dt), 256);
   L.total = off;
   return L;
 }
@@ -96,7 +109,7 @@ struct Args {
   const void* Wd;
   const uint8_t* mask;
   int32_t T, d, d_ff, G;
-  wide_dtype_t dt;
+  int32_t dt;  // wide_dtype_t value as passed (validated before use)
   void* Y;
   void* H_out;
   void* ws;
@@ -117,7 +130,7 @@ wide_status_t validate(const Args& a, bool* decode) {
   // X, mask and Y have T rows: with T == 0 they may be NULL (nothing is read or written).
   if (a.T != 0 && (!a.X || !a.mask || !a.Y))
     return fail(WIDE_ERR_NULL, "X, mask and Y must be non-NULL when T > 0");
-  if (a.dt != WIDE_F32 && a.dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)a.dt);
+  if (a.dt != WIDE_F32 && a.dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", a.dt);
   if (a.T < 0 || a.d <= 0 || a.d_ff <= 0 || a.G <= 0)
     return fail(WIDE_ERR_SHAPE, "need T >= 0 and d, d_ff, G >= 1 (T=%d d=%d d_ff=%d G=%d)", a.T, a.d,
                 a.d_ff, a.G);
@@ -145,7 +158,7 @@ wide_status_t validate(const Args& a, bool* decode) {
       return fail(WIDE_ERR_UNSUPPORTED, "the decode path needs bf16 and T <= %d", WIDE_DECODE_T_LIMIT);
     dec = true;
   }
-  const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt);
+  const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt, a.H_out == nullptr);
   if (!a.ws) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if ((reinterpret_cast<uintptr_t>(a.ws) & 255u) != 0)
     return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -155,8 +168,8 @@ wide_status_t validate(const Args& a, bool* decode) {
   return WIDE_OK;
 }
 
-wide_status_t run_stage(wide_stage_t stage, const Args& a) {
-  const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt);
+wide_status_t run_stage(int32_t stage, const Args& a) {
+  const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt, a.H_out == nullptr);
   char* ws = static_cast<char*>(a.ws);
   int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -236,11 +249,22 @@ WIDE_API wide_status_t wide_reorder_masks(const uint8_t* mask, int32_t T, int32_
   return ok();
 }
 
+namespace {
+size_t ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G, int32_t dt, bool with_h) {
+  if (T < 0 || d <= 0 || d_ff <= 0 || G <= 0 || d_ff % G != 0) return 0;
+  if (dt != WIDE_F32 && dt != WIDE_BF16) return 0;
+  return layout(T, d, d_ff, G, dt, with_h).total;
+}
+}  // namespace
+
+WIDE_API size_t wide_ffn_workspace_size_for(int32_t T, int32_t d, int32_t d_ff, int32_t G,
+                                            wide_dtype_t dtype, int32_t h_out_given) {
+  return ffn_workspace_size(T, d, d_ff, G, raw(dtype), h_out_given == 0);
+}
+
 WIDE_API size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G,
                                         wide_dtype_t dtype) {
-  if (T < 0 || d <= 0 || d_ff <= 0 || G <= 0 || d_ff % G != 0) return 0;
-  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return 0;
-  return layout(T, d, d_ff, G, dtype).total;
+  return ffn_workspace_size(T, d, d_ff, G, raw(dtype), true);
 }
 
 WIDE_API wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup,
@@ -248,15 +272,15 @@ WIDE_API wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const 
                                         int32_t d, int32_t d_ff, int32_t G, wide_dtype_t dtype,
                                         void* Y, void* H_out, void* workspace,
                                         size_t workspace_bytes, uint32_t flags, void* stream) {
-  const Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, dtype, Y, H_out, workspace,
+  const Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, raw(dtype), Y, H_out, workspace,
                workspace_bytes, flags, static_cast<hipStream_t>(stream)};
   bool dec = false;
   wide_status_t st = validate(a, &dec);
   if (st != WIDE_OK) return st;
   if (T == 0) return ok();
-  const wide_stage_t prefill[] = {WIDE_STAGE_REORDER, WIDE_STAGE_GATE_UP, WIDE_STAGE_DOWN};
-  const wide_stage_t decode[] = {WIDE_STAGE_DECODE_GATE_UP, WIDE_STAGE_DECODE_DOWN};
-  const wide_stage_t* stages = dec ? decode : prefill;
+  const int32_t prefill[] = {WIDE_STAGE_REORDER, WIDE_STAGE_GATE_UP, WIDE_STAGE_DOWN};
+  const int32_t decode[] = {WIDE_STAGE_DECODE_GATE_UP, WIDE_STAGE_DECODE_DOWN};
+  const int32_t* stages = dec ? decode : prefill;
   const int n = dec ? 2 : 3;
   for (int i = 0; i < n; ++i) {
     st = run_stage(stages[i], a);
@@ -270,19 +294,20 @@ WIDE_API wide_status_t wide_ffn_stage(wide_stage_t stage, const void* X, const v
                                       int32_t T, int32_t d, int32_t d_ff, int32_t G,
                                       wide_dtype_t dtype, void* Y, void* H_out, void* workspace,
                                       size_t workspace_bytes, uint32_t flags, void* stream) {
-  const Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, dtype, Y, H_out, workspace,
+  const Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, raw(dtype), Y, H_out, workspace,
                workspace_bytes, flags, static_cast<hipStream_t>(stream)};
+  const int32_t sg = raw(stage);
   bool dec = false;
   wide_status_t st = validate(a, &dec);
   if (st != WIDE_OK) return st;
-  const bool is_dec_stage = stage == WIDE_STAGE_DECODE_GATE_UP || stage == WIDE_STAGE_DECODE_DOWN;
-  if (stage < WIDE_STAGE_REORDER || stage > WIDE_STAGE_DECODE_DOWN)
-    return fail(WIDE_ERR_SHAPE, "unknown stage %d", (int)stage);
+  const bool is_dec_stage = sg == WIDE_STAGE_DECODE_GATE_UP || sg == WIDE_STAGE_DECODE_DOWN;
+  if (sg < WIDE_STAGE_REORDER || sg > WIDE_STAGE_DECODE_DOWN)
+    return fail(WIDE_ERR_SHAPE, "unknown stage %d", sg);
   if (is_dec_stage != dec)
-    return fail(WIDE_ERR_UNSUPPORTED, "stage %d is not on the %s path these arguments take",
-                (int)stage, dec ? "decode" : "prefill");
+    return fail(WIDE_ERR_UNSUPPORTED, "stage %d is not on the %s path these arguments take", sg,
+                dec ? "decode" : "prefill");
   if (T == 0) return ok();
-  st = run_stage(stage, a);
+  st = run_stage(sg, a);
   if (st != WIDE_OK) return st;
   return ok();
 }
@@ -378,12 +403,12 @@ GemmLayout gemm_layout(int64_t M, int64_t ng) {
 
 // routed = N (N axis) or K (K axis).
 wide_status_t validate_gemm(const void* A, const void* B, const uint8_t* mask, int32_t M, int32_t N,
-                            int32_t K, int32_t G, int32_t routed, wide_dtype_t dt, const void* C,
+                            int32_t K, int32_t G, int32_t routed, int32_t dt, const void* C,
                             const void* ws, size_t ws_bytes) {
   if (!B) return fail(WIDE_ERR_NULL, "B must be non-NULL");
   if (M != 0 && (!A || !mask || !C))
     return fail(WIDE_ERR_NULL, "A, mask and C must be non-NULL when M > 0");
-  if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", dt);
   if (M < 0 || N <= 0 || K <= 0 || G <= 0)
     return fail(WIDE_ERR_SHAPE, "need M >= 0 and N, K, G >= 1 (M=%d N=%d K=%d G=%d)", M, N, K, G);
   if (routed % G != 0)
@@ -417,7 +442,7 @@ WIDE_API wide_status_t wide_gemm_mn(const void* A, const void* B, const uint8_t*
                                     int32_t N, int32_t K, int32_t G, wide_dtype_t dtype, void* C,
                                     void* workspace, size_t workspace_bytes, void* stream) {
   wide_status_t st =
-      validate_gemm(A, B, mask, M, N, K, G, N, dtype, C, workspace, workspace_bytes);
+      validate_gemm(A, B, mask, M, N, K, G, N, raw(dtype), C, workspace, workspace_bytes);
   if (st != WIDE_OK) return st;
   if (M == 0) return ok();
   const int ng = N / G;
@@ -442,7 +467,7 @@ WIDE_API wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* 
                                    int32_t N, int32_t K, int32_t G, wide_dtype_t dtype, void* C,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   wide_status_t st =
-      validate_gemm(A, B, mask, M, N, K, G, K, dtype, C, workspace, workspace_bytes);
+      validate_gemm(A, B, mask, M, N, K, G, K, raw(dtype), C, workspace, workspace_bytes);
   if (st != WIDE_OK) return st;
   if (M == 0) return ok();
   const int ng = K / G;
@@ -472,7 +497,7 @@ AttnLayout attn_layout(int64_t T, int64_t Hk, int64_t dh) {
   AttnLayout L{};
   L.g = gemm_layout(T, Hk);
   L.vt = L.g.total;
-  L.total = round_up(L.vt + (size_t)(Hk * dh) * (size_t)wide::attention_tpad((int)T) * 2, 256);
+  L.total = round_up(L.vt + (size_t)(Hk * dh) * (size_t)wide::attention_tpad(T) * 2, 256);
   return L;
 }
 
@@ -488,14 +513,15 @@ WIDE_API wide_status_t wide_attention_prefill(const void* Q, const void* K, cons
                                               int32_t Hk, int32_t dh, wide_dtype_t dtype, void* O,
                                               uint32_t flags, void* workspace,
                                               size_t workspace_bytes, void* stream) {
+  const int32_t dt = raw(dtype);
   if (T != 0 && (!Q || !K || !V || !mask || !O))
     return fail(WIDE_ERR_NULL, "Q, K, V, mask and O must be non-NULL when T > 0");
-  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", dt);
   if (T < 0 || Hq < 1 || Hk < 1 || dh < 1 || Hq % Hk != 0)
     return fail(WIDE_ERR_SHAPE, "need T >= 0, Hq, Hk, dh >= 1 and Hk dividing Hq (T=%d Hq=%d Hk=%d dh=%d)",
                 T, Hq, Hk, dh);
   if ((flags & ~WIDE_ATTN_ZERO_INACTIVE) != 0) return fail(WIDE_ERR_SHAPE, "unknown flags 0x%x", flags);
-  if (dtype != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel runs bf16 only");
+  if (dt != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel runs bf16 only");
   if (dh != 128) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel needs dh == 128 (dh=%d)", dh);
   if ((int64_t)T * Hq * dh >= (1ll << 31))
     return fail(WIDE_ERR_UNSUPPORTED, "T*Hq*dh must stay below 2^31");
@@ -536,13 +562,14 @@ WIDE_API wide_status_t wide_attention_decode(const void* q, const void* K, const
                                              int32_t Hk, int32_t dh, wide_dtype_t dtype, void* O,
                                              uint32_t flags, void* workspace,
                                              size_t workspace_bytes, void* stream) {
+  const int32_t dt = raw(dtype);
   if (!q || !K || !V || !mask || !O) return fail(WIDE_ERR_NULL, "q, K, V, mask and O must be non-NULL");
-  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", dt);
   if (T < 1 || Hq < 1 || Hk < 1 || dh < 1 || Hq % Hk != 0)
     return fail(WIDE_ERR_SHAPE, "need T >= 1, Hq, Hk, dh >= 1 and Hk dividing Hq (T=%d Hq=%d Hk=%d dh=%d)",
                 T, Hq, Hk, dh);
   if ((flags & ~WIDE_ATTN_ZERO_INACTIVE) != 0) return fail(WIDE_ERR_SHAPE, "unknown flags 0x%x", flags);
-  if (dtype != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel runs bf16 only");
+  if (dt != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the attention kernel runs bf16 only");
   const int hpg = Hq / Hk;
   if (dh != 128 || (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8))
     return fail(WIDE_ERR_UNSUPPORTED, "the decode kernel needs dh == 128 and Hq/Hk in {1, 2, 4, 8} (dh=%d Hq/Hk=%d)",
@@ -568,15 +595,17 @@ WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const 
                                            int32_t T, int32_t D, int32_t r, int32_t ngroups,
                                            wide_act_t act, wide_dtype_t dtype, uint8_t* mask,
                                            float* logits, void* stream) {
+  const int32_t dt = raw(dtype);
+  const int32_t ac = raw(act);
   if (!W1 || !W2) return fail(WIDE_ERR_NULL, "W1 and W2 must be non-NULL");
   if (T != 0 && (!X || !mask)) return fail(WIDE_ERR_NULL, "X and mask must be non-NULL when T > 0");
-  if (dtype != WIDE_F32 && dtype != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", dt);
   if (T < 0 || D <= 0 || r <= 0 || ngroups <= 0)
     return fail(WIDE_ERR_SHAPE, "need T >= 0 and D, r, ngroups >= 1 (T=%d D=%d r=%d ngroups=%d)", T, D,
                 r, ngroups);
-  if (act != WIDE_ACT_IDENTITY && act != WIDE_ACT_RELU && act != WIDE_ACT_SILU)
-    return fail(WIDE_ERR_SHAPE, "unknown activation %d", (int)act);
-  if (dtype != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the router kernel runs bf16 only");
+  if (ac != WIDE_ACT_IDENTITY && ac != WIDE_ACT_RELU && ac != WIDE_ACT_SILU)
+    return fail(WIDE_ERR_SHAPE, "unknown activation %d", ac);
+  if (dt != WIDE_BF16) return fail(WIDE_ERR_UNSUPPORTED, "the router kernel runs bf16 only");
   if (D % 32 != 0 || (r != 16 && r != 32 && r != 64))
     return fail(WIDE_ERR_UNSUPPORTED, "the router kernel needs D %% 32 == 0 and r in {16, 32, 64} (D=%d r=%d)",
                 D, r);
@@ -587,14 +616,14 @@ WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const 
     return fail(WIDE_ERR_ALIGN, "X, W1 and W2 must be 16-byte aligned, logits 8-byte aligned");
   if (T == 0) return ok();
   const hipError_t e = wide::launch_router_bf16((const uint16_t*)X, (const uint16_t*)W1,
-                                                (const uint16_t*)W2, T, D, r, ngroups, (int)act,
+                                                (const uint16_t*)W2, T, D, r, ngroups, ac,
                                                 mask, logits, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "router launch");
   return ok();
 }
 
-WIDE_API const char* wide_status_string(wide_status_t s) {
-  switch (s) {
+WIDE_API const char* wide_status_string(wide_status_t status) {
+  switch (raw(status)) {
     case WIDE_OK: return "ok";
     case WIDE_ERR_NULL: return "null pointer argument";
     case WIDE_ERR_SHAPE: return "invalid size or argument";

@@ -92,11 +92,20 @@ wide_status_t wide_reorder_masks(const uint8_t* mask, int32_t T, int32_t ngroups
                                  int32_t* perm, int32_t* counts, int32_t* padded, void* stream);
 
 /*
- * wide_ffn_workspace_size - bytes of device workspace wide_ffn_forward needs.
- * Holds the per-group permutations, counts, packed mask bits and, when the
- * caller passes no H_out, the intermediate H. Returns 0 for invalid sizes.
+ * wide_ffn_workspace_size - bytes of device workspace wide_ffn_forward needs
+ * for a call without H_out: the per-group permutations, counts, packed mask
+ * bits, the decode path's partial sums (T <= WIDE_DECODE_T_LIMIT) and the
+ * intermediate H [T, d_ff]. Returns 0 for invalid sizes.
+ *
+ * wide_ffn_workspace_size_for - the same for a call that passes H_out
+ * (h_out_given != 0) or not (h_out_given == 0). With H_out the workspace
+ * holds no H (at T = 16384, d_ff = 14336 in bf16 that is 470 MB less).
+ * wide_ffn_forward, wide_ffn_stage and wide_ffn_decode_prepared check the
+ * workspace against the size that matches the H_out they receive.
  */
 size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G, wide_dtype_t dtype);
+size_t wide_ffn_workspace_size_for(int32_t T, int32_t d, int32_t d_ff, int32_t G,
+                                   wide_dtype_t dtype, int32_t h_out_given);
 
 /*
  * wide_ffn_forward - the masked SwiGLU FFN defined at the top of this file.
@@ -111,8 +120,8 @@ size_t wide_ffn_workspace_size(int32_t T, int32_t d, int32_t d_ff, int32_t G, wi
  *   H_out  [T, d_ff]   device, dtype, optional (NULL = keep H in the workspace).
  *                      When given, it receives H with exact +0.0 at every
  *                      masked channel.
- *   workspace          device, >= wide_ffn_workspace_size(...) bytes, 256-byte
- *                      aligned; contents on entry are ignored.
+ *   workspace          device, >= wide_ffn_workspace_size_for(..., H_out != NULL)
+ *                      bytes, 256-byte aligned; contents on entry are ignored.
  *   flags              WIDE_FLAG_* (0 = choose the path from T).
  *
  * Prefill path (T > wide_decode_max_t(), or WIDE_FLAG_FORCE_PREFILL): mask

@@ -28,6 +28,31 @@ def build_oracle(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_native(out_dir: str) -> str:
+    """A copy of the oracle for timing on the host that runs it: gcc -O3
+    -march=native -fopenmp, built there (the build container's CPU may differ).
+
+    The arithmetic is unchanged: ISO C mode (-std=c11) keeps floating-point
+    contraction off and there is no fast-math, so every product and sum is
+    the same double operation in the same order as in the -O2 build (the
+    pins compare the two bit for bit)."""
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "liboracle_native.so")
+    tmp = path + ".tmp"
+    subprocess.check_call(["gcc", "-O3", "-march=native", "-std=c11", "-fopenmp", "-fPIC",
+                           "-shared", _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, path)
+    return path
+
+
+def use_library(path: str) -> None:
+    """Load the oracle from `path` (a build of wide_oracle.c) from now on."""
+    global _LIB_PATH, _lib
+    _LIB_PATH = path
+    _lib = None
+    _load()
+
+
 def _load():
     global _lib
     if _lib is None:

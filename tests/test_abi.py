@@ -119,6 +119,29 @@ def test_workspace_size(lib):
     assert need <= ws <= need + 5 * 256
     assert lib.wide_ffn_workspace_size(16, 4096, 14336, 100, _lib.WIDE_BF16) == 0
     assert lib.wide_ffn_workspace_size(16, 4096, 14336, 128, 5) == 0
+    # with H_out given the workspace holds no H
+    assert lib.wide_ffn_workspace_size_for(16384, 4096, 14336, 128, _lib.WIDE_BF16, 0) == ws
+    small = lib.wide_ffn_workspace_size_for(16384, 4096, 14336, 128, _lib.WIDE_BF16, 1)
+    assert need - T * 14336 * 2 <= small <= need - T * 14336 * 2 + 5 * 256
+    # decode sizes hold the split partial sums either way
+    dec = lib.wide_ffn_workspace_size_for(16, 4096, 14336, 128, _lib.WIDE_BF16, 1)
+    assert dec >= 4 * 16 * 4096 * 4
+    assert lib.wide_ffn_workspace_size_for(16, 4096, 14336, 128, _lib.WIDE_BF16, 0) >= \
+        dec + 16 * 14336 * 2
+
+
+def test_workspace_check_follows_h_out(lib):
+    # a workspace sized for a call with H_out is accepted with H_out and
+    # refused without it (T = 0 would skip the check, so T stays positive;
+    # the check runs before anything is enqueued)
+    small = lib.wide_ffn_workspace_size_for(64, 256, 1024, 64, _lib.WIDE_BF16, 1)
+    full = lib.wide_ffn_workspace_size_for(64, 256, 1024, 64, _lib.WIDE_BF16, 0)
+    assert full == small + 64 * 1024 * 2
+    assert ffn_call(lib, ws_bytes=small, d=96) == _lib.WIDE_ERR_UNSUPPORTED  # checks run in order
+    assert ffn_call(lib, ws_bytes=small) == _lib.WIDE_ERR_WORKSPACE
+    assert "needs %d" % full in lib.wide_last_error().decode()
+    assert ffn_call(lib, ws_bytes=small - 1, H=FAKE) == _lib.WIDE_ERR_WORKSPACE
+    assert "needs %d" % small in lib.wide_last_error().decode()
 
 
 def test_decode_threshold_default(lib):

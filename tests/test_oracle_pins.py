@@ -771,3 +771,25 @@ def test_attention_pins_catch_planted_mistake(bug):
         except (ValueError, IndexError):
             results[pin.__name__] = False
     assert not all(results.values()), f"no pin caught '{bug}': {results}"
+
+
+def test_native_build_is_bit_identical(tmp_path):
+    """The CPU baseline times a gcc -O3 -march=native build of the oracle; it
+    must compute the same doubles as the -O2 build the tests use."""
+    import ctypes
+    path = oracle.build_native(str(tmp_path))
+    native = ctypes.CDLL(path)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    native.oracle_ffn.argtypes = [p, p, p, p, p, i64, i64, i64, i64, p, i64, p, p]
+    native.oracle_ffn.restype = ctypes.c_int
+    inp = dg.random_small(4242, 9, 64, 256, 32, "bf16", 0.5, wscale=0.05)
+    X, Wg, Wu, Wd = (np.ascontiguousarray(inp[k].float().numpy()) for k in ("X", "Wg", "Wu", "Wd"))
+    m = np.ascontiguousarray(inp["mask"].numpy())
+
+    H, Y = np.empty((9, 256)), np.empty((9, 64))
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    assert native.oracle_ffn(ptr(X), ptr(Wg), ptr(Wu), ptr(Wd), ptr(m), 9, 64, 256, 32, None, 9,
+                             ptr(H), ptr(Y)) == 0
+    H0, Y0 = oracle.ffn(X, Wg, Wu, Wd, m, 32)
+    assert np.array_equal(H.view(np.int64), H0.view(np.int64))
+    assert np.array_equal(Y.view(np.int64), Y0.view(np.int64))
