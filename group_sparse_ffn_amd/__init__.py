@@ -23,7 +23,7 @@ __all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decod
            "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
            "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
            "WIDE_STAGE_DECODE_DOWN", "decode_weights_size", "decode_prepare_weights",
-           "ffn_decode_prepared"]
+           "ffn_decode_prepared", "ffn_forward_noalloc"]
 
 _DTYPES = {torch.bfloat16: WIDE_BF16, torch.float32: WIDE_F32}
 
@@ -141,6 +141,31 @@ def ffn_forward(X, Wg, Wu, Wd, mask, G: int, return_h: bool = False, flags: int 
     call = FfnCall(X, Wg, Wu, Wd, mask, G, return_h=return_h, flags=flags)
     Y = call.run()
     return (Y, call.H) if return_h else Y
+
+
+def ffn_forward_noalloc(X, Wg, Wu, Wd, mask, G: int, flags: int = 0,
+                        Y: Optional[torch.Tensor] = None, H: Optional[torch.Tensor] = None):
+    """ffn_forward through wide_ffn_forward_noalloc (the library's own scratch
+    array instead of a workspace) -> (Y, H). Y and H are allocated here unless
+    given; the library call itself allocates nothing."""
+    for name, t in (("X", X), ("Wgate", Wg), ("Wup", Wu), ("Wdown", Wd), ("mask", mask)):
+        _need_cuda(name, t)
+    if X.dtype not in _DTYPES or any(w.dtype != X.dtype for w in (Wg, Wu, Wd)):
+        raise ValueError("X and the weights must share one dtype, bfloat16 or float32")
+    T, d = X.shape
+    d_ff = Wg.shape[0]
+    if Wg.shape != (d_ff, d) or Wu.shape != (d_ff, d) or Wd.shape != (d, d_ff):
+        raise ValueError("expected Wgate, Wup [d_ff, d] and Wdown [d, d_ff]")
+    if mask.dtype != torch.uint8 or d_ff % G != 0 or mask.shape != (T, d_ff // G):
+        raise ValueError("mask must be uint8 [T, d_ff // G] with G dividing d_ff")
+    Y = Y if Y is not None else torch.empty((T, d), dtype=X.dtype, device=X.device)
+    H = H if H is not None else torch.empty((T, d_ff), dtype=X.dtype, device=X.device)
+    _need_cuda("Y", Y)
+    _need_cuda("H", H)
+    _lib.check(_lib.load().wide_ffn_forward_noalloc(
+        X.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), mask.data_ptr(), T, d, d_ff, G,
+        _DTYPES[X.dtype], Y.data_ptr(), H.data_ptr(), flags, _stream_ptr(X.device)))
+    return Y, H
 
 
 def ffn_stage(stage: int, call: FfnCall) -> None:

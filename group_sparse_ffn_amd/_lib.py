@@ -28,6 +28,7 @@ WIDE_TOKEN_TILE = 256
 WIDE_DECODE_T_LIMIT = 16
 WIDE_FLAG_FORCE_PREFILL = 0x1
 WIDE_FLAG_FORCE_DECODE = 0x2
+WIDE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 WIDE_ACT_IDENTITY = 0
 WIDE_ACT_RELU = 1
@@ -53,6 +54,8 @@ SIGNATURES = {
     "wide_ffn_workspace_size_for": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int, _i32]),
     "wide_ffn_forward": (ctypes.c_int, _FFN_ARGS),
     "wide_ffn_stage": (ctypes.c_int, [ctypes.c_int] + _FFN_ARGS),
+    "wide_ffn_forward_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                                ctypes.c_int, _p, _p, _u32, _p]),
     "wide_decode_weights_size": (_sz, [_i32, _i32]),
     "wide_decode_prepare_weights": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _sz, _p]),
     "wide_ffn_decode_prepared": (ctypes.c_int, [_p, _p, _p, _p, _p, _sz, _p, _i32, _i32, _i32,

@@ -147,6 +147,12 @@ hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint1
                               int D, int r, int ng, int act, uint8_t* mask, float* logits,
                               hipStream_t stream);
 
+// Device address of the no-allocation entry point's scratch array
+// (WIDE_NOALLOC_SCRATCH_BYTES, 256-byte aligned) on the device that runs
+// `stream` (the current device for the null stream); looked up on the first
+// call per device and kept. Allocates nothing.
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 // fp32 prefill kernels (VALU, same structure as the bf16 ones).
 hipError_t launch_gate_up_f32(const float* X, const float* Wg, const float* Wu,
                               const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,

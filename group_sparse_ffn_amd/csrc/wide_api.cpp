@@ -123,9 +123,10 @@ struct Args {
 // regions of d * d_ff bf16 each, 256-byte aligned.
 size_t prep_region(int64_t d, int64_t d_ff) { return round_up((size_t)(d * d_ff) * 2, 256); }
 
-// Host-side checks shared by wide_ffn_forward and wide_ffn_stage. Sets
-// *decode to the path the call takes.
-wide_status_t validate(const Args& a, bool* decode) {
+// Host-side checks of the arguments (all but the workspace) shared by
+// wide_ffn_forward, wide_ffn_stage, wide_ffn_decode_prepared and
+// wide_ffn_forward_noalloc. Sets *decode to the path the call takes.
+wide_status_t validate_args(const Args& a, bool* decode) {
   if (!a.Wg || !a.Wu || !a.Wd) return fail(WIDE_ERR_NULL, "Wgate, Wup and Wdown must be non-NULL");
   // X, mask and Y have T rows: with T == 0 they may be NULL (nothing is read or written).
   if (a.T != 0 && (!a.X || !a.mask || !a.Y))
@@ -158,14 +159,24 @@ wide_status_t validate(const Args& a, bool* decode) {
       return fail(WIDE_ERR_UNSUPPORTED, "the decode path needs bf16 and T <= %d", WIDE_DECODE_T_LIMIT);
     dec = true;
   }
+  *decode = dec;
+  return WIDE_OK;
+}
+
+// The workspace argument against the layout of a validated call.
+wide_status_t check_workspace(const Args& a) {
   const Layout L = layout(a.T, a.d, a.d_ff, a.G, a.dt, a.H_out == nullptr);
   if (!a.ws) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if ((reinterpret_cast<uintptr_t>(a.ws) & 255u) != 0)
     return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (a.ws_bytes < L.total)
     return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", a.ws_bytes, L.total);
-  *decode = dec;
   return WIDE_OK;
+}
+
+wide_status_t validate(const Args& a, bool* decode) {
+  const wide_status_t st = validate_args(a, decode);
+  return st != WIDE_OK ? st : check_workspace(a);
 }
 
 wide_status_t run_stage(int32_t stage, const Args& a) {
@@ -370,6 +381,40 @@ WIDE_API wide_status_t wide_ffn_decode_prepared(const void* X, const void* Wgate
   if (st != WIDE_OK) return st;
   st = run_stage(WIDE_STAGE_DECODE_DOWN, a);
   if (st != WIDE_OK) return st;
+  return ok();
+}
+
+// ---------------------------------------------------------------- no-allocation entry point
+
+WIDE_API wide_status_t wide_ffn_forward_noalloc(const void* X, const void* Wgate, const void* Wup,
+                                                const void* Wdown, const uint8_t* mask, int32_t T,
+                                                int32_t d, int32_t d_ff, int32_t G,
+                                                wide_dtype_t dtype, void* Y, void* H_out,
+                                                uint32_t flags, void* stream) {
+  Args a{X, Wgate, Wup, Wdown, mask, T, d, d_ff, G, raw(dtype), Y, H_out, nullptr,
+         (size_t)WIDE_NOALLOC_SCRATCH_BYTES, flags, static_cast<hipStream_t>(stream)};
+  bool dec = false;
+  wide_status_t st = validate_args(a, &dec);
+  if (st != WIDE_OK) return st;
+  if (T != 0 && H_out == nullptr)
+    return fail(WIDE_ERR_NULL, "H_out is required: the scratch array holds no H");
+  const size_t need = layout(T, d, d_ff, G, a.dt, false).total;
+  if (need > (size_t)WIDE_NOALLOC_SCRATCH_BYTES)
+    return fail(WIDE_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu "
+                "(WIDE_NOALLOC_SCRATCH_BYTES)", need, (size_t)WIDE_NOALLOC_SCRATCH_BYTES);
+  if (T == 0) return ok();
+  const hipError_t e = wide::noalloc_scratch(a.stream, &a.ws);
+  if (e != hipSuccess) return hip_status(e, "scratch array of the stream's device");
+  st = check_workspace(a);
+  if (st != WIDE_OK) return st;
+  const int32_t prefill[] = {WIDE_STAGE_REORDER, WIDE_STAGE_GATE_UP, WIDE_STAGE_DOWN};
+  const int32_t decode[] = {WIDE_STAGE_DECODE_GATE_UP, WIDE_STAGE_DECODE_DOWN};
+  const int32_t* stages = dec ? decode : prefill;
+  for (int i = 0; i < (dec ? 2 : 3); ++i) {
+    st = run_stage(stages[i], a);
+    if (st != WIDE_OK) return st;
+  }
   return ok();
 }
 

@@ -152,6 +152,33 @@ wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup
                                wide_dtype_t dtype, void* Y, void* H_out, void* workspace,
                                size_t workspace_bytes, uint32_t flags, void* stream);
 
+/*
+ * wide_ffn_forward_noalloc - wide_ffn_forward for callers that cannot
+ * allocate device memory: code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, kernels and results (bit
+ * for bit) as wide_ffn_forward, without the workspace: the library keeps its
+ * workspace in a static device array of WIDE_NOALLOC_SCRATCH_BYTES on each GPU
+ * (placed when the library is loaded on that GPU, held until the process
+ * ends). The call allocates and frees nothing.
+ *   H_out  required (non-NULL when T > 0): the array does not hold H.
+ *   Limit: wide_ffn_workspace_size_for(T, d, d_ff, G, dtype, 1) must not
+ *          exceed WIDE_NOALLOC_SCRATCH_BYTES (e.g. T * ngroups up to about
+ *          7.9 million at d <= 16384), else WIDE_ERR_WORKSPACE and nothing is
+ *          enqueued.
+ *   The array is shared by every call on one GPU and keeps the last call's
+ *   contents (nothing in it needs to start at zero: every call writes what it
+ *   reads). Calls that overlap on one GPU (different streams, or host
+ *   threads racing) race on it: serialise them.
+ * The first call on a GPU looks up the array's device address
+ * (hipGetSymbolAddress) and keeps it. Errors: as wide_ffn_forward, plus
+ * WIDE_ERR_HIP when the device or the address cannot be obtained.
+ */
+#define WIDE_NOALLOC_SCRATCH_BYTES (32u << 20)
+wide_status_t wide_ffn_forward_noalloc(const void* X, const void* Wgate, const void* Wup,
+                                       const void* Wdown, const uint8_t* mask, int32_t T,
+                                       int32_t d, int32_t d_ff, int32_t G, wide_dtype_t dtype,
+                                       void* Y, void* H_out, uint32_t flags, void* stream);
+
 /* Stages of wide_ffn_forward, for callers that time or interleave them. */
 typedef enum {
   WIDE_STAGE_REORDER = 0,   /* prefill: mask reorder into the workspace */

@@ -167,6 +167,12 @@ hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint1
   if (logits) wr(logits, (size_t)T * ng * 2 * 4);
   return hipSuccess;
 }
+// the scratch array of wide_ffn_forward_noalloc: an exact-size host buffer
+hipError_t noalloc_scratch(hipStream_t, void** out) {
+  static void* p = aligned_alloc(256, WIDE_NOALLOC_SCRATCH_BYTES);
+  *out = p;
+  return hipSuccess;
+}
 hipError_t launch_gate_up_f32(const float* X, const float* Wg, const float* Wu, const int32_t* perm,
                               const int32_t* counts, int T, int d, int d_ff, int G, float* H, bool,
                               hipStream_t) {
@@ -244,6 +250,16 @@ void ffn_case(int T, int d, int d_ff, int G, wide_dtype_t dt, bool with_h, uint3
       EXPECT(wide_ffn_stage((wide_stage_t)s, X.p, Wg.p, Wu.p, Wd.p, (const uint8_t*)mask.p, T, d,
                             d_ff, G, dt, Y.p, with_h ? H.p : nullptr, ws.p, need, flags,
                             nullptr) == WIDE_OK);
+  if (with_h) {
+    const size_t small = wide_ffn_workspace_size_for(T, d, d_ff, G, dt, 1);
+    EXPECT(wide_ffn_forward_noalloc(X.p, Wg.p, Wu.p, Wd.p, (const uint8_t*)mask.p, T, d, d_ff, G,
+                                    dt, Y.p, H.p, flags, nullptr) ==
+           (small <= WIDE_NOALLOC_SCRATCH_BYTES ? WIDE_OK : WIDE_ERR_WORKSPACE));
+  } else {
+    EXPECT(wide_ffn_forward_noalloc(X.p, Wg.p, Wu.p, Wd.p, (const uint8_t*)mask.p, T, d, d_ff, G,
+                                    dt, Y.p, nullptr, flags, nullptr) ==
+           (T == 0 ? WIDE_OK : WIDE_ERR_NULL));
+  }
   if (dt == WIDE_BF16 && T <= WIDE_DECODE_T_LIMIT && d_ff % 64 == 0) {
     const size_t pn = wide_decode_weights_size(d, d_ff);
     Buf prep(pn);
@@ -316,6 +332,10 @@ int main() {
     ffn_case(3, 64, 320, 64, f32, with_h, 0);              // fp32 never takes the decode path
     ffn_case(0, 64, 128, 64, bf, with_h, 0);
   }
+  // prefill whose workspace (without H) nearly fills the scratch array
+  // (32.4 of its 33.6 MB)
+  EXPECT(wide_ffn_workspace_size_for(122880, 64, 1024, 16, bf, 1) > (30u << 20));
+  ffn_case(122880, 64, 1024, 16, bf, true, 0);
   gemm_case(300, 1024, 256, 256, false);
   gemm_case(300, 256, 1024, 256, true);
   gemm_case(77, 64, 128, 64, false);  // one group: dynamic depth

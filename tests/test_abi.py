@@ -354,3 +354,30 @@ def test_decode_prepared_validation(lib, kw, status):
                                         a["prep_bytes"], a["mask"], a["T"], a["d"], a["d_ff"],
                                         a["G"], a["Y"], a["H"], a["ws"], a["ws_bytes"],
                                         None) == status
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    # validation and the size limit come before the scratch lookup, so these
+    # return without touching a device
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 1024, 64, _lib.WIDE_BF16, FAKE, FAKE, 0, None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[{"T": 5, "d": 6, "d_ff": 7, "G": 8, "dtype": 9, "Y": 10, "H": 11, "flags": 12}[k]] = v
+        return lib.wide_ffn_forward_noalloc(*a)
+
+    assert call(H=None) == _lib.WIDE_ERR_NULL
+    assert call(d=96) == _lib.WIDE_ERR_UNSUPPORTED
+    assert call(dtype=9) == _lib.WIDE_ERR_DTYPE
+    assert call(H=FAKE + 4) == _lib.WIDE_ERR_ALIGN
+    # T * ngroups too large for the array: 2^19 tokens x 64 groups needs 128 MiB of row lists
+    assert call(T=1 << 19, d_ff=1024, G=16) == _lib.WIDE_ERR_WORKSPACE
+    assert "WIDE_NOALLOC_SCRATCH_BYTES" in lib.wide_last_error().decode()
+    assert lib.wide_ffn_workspace_size_for(1 << 19, 256, 1024, 16, _lib.WIDE_BF16, 1) > \
+        _lib.WIDE_NOALLOC_SCRATCH_BYTES
+    # the largest workload of the bench fits
+    assert lib.wide_ffn_workspace_size_for(16384, 4096, 14336, 128, _lib.WIDE_BF16, 1) <= \
+        _lib.WIDE_NOALLOC_SCRATCH_BYTES
+    # T == 0 with H_out NULL is a valid no-op
+    assert call(T=0, H=None) == _lib.WIDE_OK
