@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 CSRC = "group_sparse_ffn_amd/csrc"
 # sources that define each kernel (a change to any of them invalidates its counters)
 KERNEL_SOURCES = {
@@ -613,7 +614,14 @@ def bench_decode(torch, wide, dg, steps: int, copies: int = 8):
         gms = graph_step_ms(torch, all_copies, max(steps, 4)) / copies
         gu_bytes = 2 * w.d * w.G * union * 2
         dn_bytes = w.d * w.G * union * 2
+        # torch's dense GEMVs on the same rotated weight copies
+        X0 = calls[0].args[0]
+        dfns = [dense_ffn_fn(torch, X0, c["Wg"], c["Wu"], c["Wd"]) for c in ws]
+        for f in dfns:
+            f()
+        dms = time_events(torch, rotating(dfns), n)
         res[f"T{w.T}"] = {"us_per_step": ms * 1e3, "active_weight_GBps": act_bytes / ms / 1e6,
+                          "dense_us": dms * 1e3, "speedup_vs_dense": dms / ms,
                           "hbm_frac": act_bytes / ms / 1e6 / PEAK_HBM_GBS,
                           "graph_us_per_step": gms * 1e3,
                           "graph_hbm_frac": act_bytes / gms / 1e6 / PEAK_HBM_GBS,
@@ -648,6 +656,162 @@ def bench_decode(torch, wide, dg, steps: int, copies: int = 8):
         del calls, ws
         torch.cuda.empty_cache()
     return res
+
+
+def dense_ffn_fn(torch, X, Wg, Wu, Wd):
+    """The unpruned FFN with torch's matmuls (hipBLASLt GEMMs / GEMVs)."""
+    def f():
+        a = X @ Wg.t()
+        b = X @ Wu.t()
+        return (torch.nn.functional.silu(a) * b) @ Wd.t()
+    return f
+
+
+def rotating(fns):
+    """A callable that runs fns[0], fns[1], ... in turn (one per call)."""
+    idx = [0]
+
+    def f():
+        fns[idx[0] % len(fns)]()
+        idx[0] += 1
+    return f
+
+
+def bench_prefill_cell(torch, wide, w, inp, steps: int, dense: bool = True):
+    """One prefill-sized workload: the library call (eager, events) next to the
+    dense torch FFN on the same operands; effective TFLOP/s of the active
+    pairs, roofline fraction against the bf16 (fp32) peak, speedups."""
+    dev = "cuda:0"
+    d = {k: v.to(dev) for k, v in inp.items()}
+    A = int(inp["mask"].sum())
+    ng = w.ngroups
+    call = wide.FfnCall(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], w.G)
+    for _ in range(2):
+        call.run()
+    ms = time_events(torch, call.run, steps)
+    flops = 6.0 * w.d * w.G * A
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    out = {"T": w.T, "G": w.G, "groups": ng, "active_pairs": A,
+           "sparsity": round(1 - A / max(w.T * ng, 1), 4), "ms": round(ms, 4),
+           "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "roofline_frac": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
+           "ideal_speedup": round(w.T * ng / A, 3) if A else None}
+    if dense:
+        f = dense_ffn_fn(torch, d["X"], d["Wg"], d["Wu"], d["Wd"])
+        for _ in range(2):
+            f()
+        dms = time_events(torch, f, steps)
+        out["dense_ms"] = round(dms, 4)
+        out["speedup_vs_dense"] = round(dms / ms, 3)
+    del call, d
+    return out
+
+
+def bench_decode_cell(torch, wide, w, inp, steps: int, copies: int = 8, dense: bool = True):
+    """One decode workload (T <= 16): calls rotate over `copies` device copies of
+    the weights so every call reads HBM; active-weight GB/s against the HBM
+    peak; torch's dense GEMVs on the same rotated copies."""
+    dev = "cuda:0"
+    X = inp["X"].to(dev)
+    mask = inp["mask"].to(dev)
+    ws = [{k: inp[k].to(dev) for k in ("Wg", "Wu", "Wd")}]
+    for _ in range(copies - 1):
+        ws.append({k: v.clone() for k, v in ws[0].items()})
+    calls = [wide.FfnCall(X, c["Wg"], c["Wu"], c["Wd"], mask, w.G) for c in ws]
+    union = int(inp["mask"].numpy().any(axis=0).sum())
+    act_bytes = 3 * w.d * w.G * union * 2
+    for c in calls:
+        c.run()
+    n = max(steps, 4) * copies
+    ms = time_events(torch, rotating([c.run for c in calls]), n)
+    out = {"T": w.T, "G": w.G, "active_groups": union, "groups": w.ngroups,
+           "us": round(ms * 1e3, 2), "active_weight_MB": round(act_bytes / 1e6, 2),
+           "active_weight_GBps": round(act_bytes / ms / 1e6, 1),
+           "hbm_frac": round(act_bytes / ms / 1e6 / PEAK_HBM_GBS, 4), "weight_copies": copies}
+    if dense:
+        fns = [dense_ffn_fn(torch, X, c["Wg"], c["Wu"], c["Wd"]) for c in ws]
+        for f in fns:
+            f()
+        dms = time_events(torch, rotating(fns), n)
+        out["dense_us"] = round(dms * 1e3, 2)
+        out["speedup_vs_dense"] = round(dms / ms, 3)
+    del calls, ws, X, mask
+    return out
+
+
+def bench_configs(torch, wide, dg, steps: int):
+    """Every workload of the measured set beside the headline: the tiny fp32
+    SwiGLU, the Llama3.2-3B-shaped G x sparsity sweep (every G at 50% for
+    T = 8192 and T = 1, every sparsity level at G = 128), and the
+    Qwen3-14B-shaped skewed masks with the all-ones and all-zero limits."""
+    import dataclasses
+    out = {}
+    # tiny fp32 SwiGLU: launch-bound; timed eagerly and by graph replay
+    w = dg.TINY
+    log(f"config {w.name}")
+    inp = dg.make_inputs(w)
+    cell = bench_prefill_cell(torch, wide, w, inp, max(steps, 50))
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    call = wide.FfnCall(d["X"], d["Wg"], d["Wu"], d["Wd"], d["mask"], w.G)
+    cell["graph_us"] = round(graph_step_ms(torch, call.run, max(steps, 50)) * 1e3, 2)
+    cell["note"] = "fp32 VALU path; launch-bound at this size"
+    out[w.name] = cell
+    del call, d
+    # Llama3.2-3B sweep
+    cells = {(c.G, round((1 - c.density) * 100), c.T): c for c in dg.llama3b_sweep_cells()}
+    want = [(G, 50, T) for T in (8192, 1) for G in (16, 32, 64, 128, 256, 512)]
+    want += [(128, s, 8192) for s in (10, 25, 70)]
+    base = cells[(128, 50, 8192)]
+    wts = dg.make_inputs(base, T=1)  # weights depend only on the workload id
+    xs = {T: dg.make_inputs(base, T=T, weights=False)["X"] for T in (8192, 1)}
+    sweep = []
+    for key in want:
+        c = cells[key]
+        log(f"config {c.name}")
+        inp = {"X": xs[c.T], "Wg": wts["Wg"], "Wu": wts["Wu"], "Wd": wts["Wd"],
+               "mask": torch.from_numpy(dg.make_mask(c))}
+        r = (bench_prefill_cell(torch, wide, c, inp, steps) if c.T > 16
+             else bench_decode_cell(torch, wide, c, inp, steps))
+        r["target_sparsity"] = key[1] / 100
+        sweep.append(r)
+        torch.cuda.empty_cache()
+    out["llama3.2-3b-sweep"] = sweep
+    del wts, xs
+    # Qwen3-14B skewed masks and the two limits
+    w = dg.QWEN14B_SKEW
+    inp = dg.make_inputs(w)
+    q = {}
+    for kind in ("zipf", "ones", "zeros"):
+        log(f"config {w.name} mask={kind}")
+        inp["mask"] = torch.from_numpy(dg.make_mask(w, kind))
+        q[kind] = bench_prefill_cell(torch, wide, w, inp, steps)
+        torch.cuda.empty_cache()
+    out[w.name] = q
+    del inp
+    torch.cuda.empty_cache()
+    # where decode hands over to prefill: both paths at small T (Llama3.1-8B shape)
+    thr = {}
+    w = dg.LLAMA8B_DECODE_T16
+    full = dg.make_inputs(w)
+    for T in (1, 2, 4, 8, 16):
+        wt = dataclasses.replace(w, T=T, name=f"{w.name[:-3]}t{T}")
+        inp = dict(full, X=full["X"][:T].contiguous(), mask=full["mask"][:T].contiguous())
+        dv = {k: v.to("cuda:0") for k, v in inp.items()}
+        row = {}
+        for path, flags in (("decode", wide.WIDE_FLAG_FORCE_DECODE),
+                            ("prefill", wide.WIDE_FLAG_FORCE_PREFILL)):
+            c = wide.FfnCall(dv["X"], dv["Wg"], dv["Wu"], dv["Wd"], dv["mask"], wt.G, flags=flags)
+            c.run()
+            row[f"{path}_us"] = round(time_events(torch, c.run, max(steps, 10)) * 1e3, 2)
+            del c
+        thr[f"T{T}"] = row
+        del dv
+    thr["decode_max_t"] = wide.decode_max_t()
+    thr["note"] = ("same weights every call (MALL-warm for both paths); the library takes the "
+                   "decode path for T <= decode_max_t")
+    out["decode_vs_prefill_small_t"] = thr
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_profile(steps: int):
@@ -1130,6 +1294,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--profile-baselines", action="store_true")
@@ -1213,6 +1378,8 @@ def main():
         line["masked_gemms"] = bench_masked_gemms(torch, wide, dg, args.steps)
         line["router"] = bench_router(torch, wide, dg, args.steps)
         line["attention"] = bench_attention(torch, wide, dg, args.steps)
+    if not args.no_configs:
+        line["configs"] = bench_configs(torch, wide, dg, max(5, args.steps // 2))
     if not args.no_baselines:
         line["gemm_baselines"] = bench_baselines(torch, wide, dg)
     if not args.no_cpu:
