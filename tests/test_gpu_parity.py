@@ -457,3 +457,36 @@ def test_sweep_cells_cover_every_g_and_sparsity():
     assert {G for G, _ in pre} == {16, 32, 64, 128, 256, 512}
     assert {s for _, s in pre} == {10, 25, 50, 70}
     assert len({G for G, _, T in SWEEP_CELLS if T == 1}) >= 2
+
+
+# ----------------------------------------------------------------------------- down projection
+
+# The down kernel on ragged shapes: T not a multiple of the 256-token tile, d
+# not a multiple of the 256-column tile, G from 64 to 512 (one to eight
+# 64-channel K-blocks per group), densities from nearly empty to full, a
+# 128-token run that executes no group and a token that executes every group;
+# workspace (where H lives) filled with NaN bits, two calls bit-identical.
+@pytest.mark.parametrize("T,d,d_ff,G,density", [
+    (700, 512, 2048, 128, 0.5), (1000, 320, 1536, 64, 0.3), (129, 256, 1024, 256, 0.7),
+    (300, 576, 3072, 192, 0.5), (257, 256, 4096, 512, 0.5), (128, 256, 1024, 64, 1.0),
+    (333, 256, 1024, 64, 0.05), (4096, 512, 2048, 128, 0.5), (300, 256, 257 * 64, 64, 0.5),
+])
+def test_down_ragged_tiles_and_idle_runs(T, d, d_ff, G, density):
+    inp = dg.random_small(31 * T + G, T, d, d_ff, G, "bf16", density, wscale=0.05)
+    m = inp["mask"].clone()
+    if T >= 400:
+        m[128:256, :] = 0   # a run of 128 tokens with no live group
+        m[300, :] = 1       # a token executing every group
+    inp["mask"] = m
+    x = to_dev(inp)
+    a = wide.FfnCall(x["X"], x["Wg"], x["Wu"], x["Wd"], x["mask"], G)
+    a.workspace.fill_(0xFF)
+    Ya = a.run().clone()
+    Ya2 = a.run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(Ya.view(torch.int16), Ya2.view(torch.int16)), "not deterministic"
+    _, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], m, G)
+    assert rel_err(Ya, Yref) <= TOL["bf16"]
+    idle = (m.sum(dim=1) == 0).nonzero().flatten().tolist()
+    for t in idle[:64]:
+        assert bool((Ya[t] == 0).all()) and not bool(torch.signbit(Ya[t].float()).any())
