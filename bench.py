@@ -472,11 +472,34 @@ def bench_router(torch, wide, dg, steps: int):
                 wide.router_forward(xs[i % len(xs)], W1, W2, "silu", mask=mask)
         ms = graph_step_ms(torch, calls16, max(steps, 10)) / 16
         nbytes = T * D * 2 + T * ng + r * D * 2 + 2 * ng * r * 2
+        # router fused with the reorder (wide_router_reorder: X -> packed bits
+        # -> row lists) against the unfused chain (router -> mask bytes -> the
+        # FFN's pack + partition stage) on the same rotated copies of X
+        fused = [wide.RouterReorderCall(X, W1, W2, "silu", wide.WIDE_TOKEN_TILE) for X in xs]
+        Z = torch.zeros((T, 64), dtype=torch.bfloat16, device=dev)
+        Wz = torch.zeros((ng * 64, 64), dtype=torch.bfloat16, device=dev)
+        Wdz = torch.zeros((64, ng * 64), dtype=torch.bfloat16, device=dev)
+        reo = wide.FfnCall(Z, Wz, Wz, Wdz, mask, 64, flags=wide.WIDE_FLAG_FORCE_PREFILL)
+
+        def chain16():
+            for i in range(16):
+                wide.router_forward(xs[i % len(xs)], W1, W2, "silu", mask=mask)
+                reo.stage(wide.WIDE_STAGE_REORDER)
+
+        def fused16():
+            for i in range(16):
+                fused[i % len(fused)].run()
+        for f in (chain16, fused16):
+            f()
+        cms = graph_step_ms(torch, chain16, max(steps, 10)) / 16
+        fms = graph_step_ms(torch, fused16, max(steps, 10)) / 16
         out[f"T{T}"] = {"us": round(ms * 1e3, 2), "bytes": nbytes,
                         "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                        "execute_fraction": round(float(mask.float().mean()), 4)}
-        del xs, X0, mask
+                        "execute_fraction": round(float(mask.float().mean()), 4),
+                        "router_then_reorder_us": round(cms * 1e3, 2),
+                        "router_reorder_fused_us": round(fms * 1e3, 2)}
+        del xs, X0, mask, fused, reo, Z, Wz, Wdz
     return out
 
 

@@ -18,7 +18,8 @@ from ._lib import (WIDE_BF16, WIDE_DECODE_T_LIMIT, WIDE_F32, WIDE_FLAG_FORCE_DEC
                    WideError)
 
 __all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decode_max_t",
-           "gemm_mn", "gemm_k", "gemm_workspace_size", "router_forward",
+           "gemm_mn", "gemm_k", "gemm_workspace_size", "router_forward", "router_reorder",
+           "RouterReorderCall", "router_reorder_workspace_size",
            "FfnCall", "WideError", "WIDE_TOKEN_TILE", "WIDE_DECODE_T_LIMIT",
            "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
            "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
@@ -274,6 +275,57 @@ def router_forward(X, W1, W2, act: str = "silu", return_logits: bool = False, ma
         X.data_ptr(), W1.data_ptr(), W2.data_ptr(), T, D, r, ng, _ACTS[act], WIDE_BF16,
         mask.data_ptr(), None if logits is None else logits.data_ptr(), _stream_ptr(dev)))
     return (mask, logits) if return_logits else mask
+
+
+def router_reorder_workspace_size(T: int, ngroups: int) -> int:
+    return int(_lib.load().wide_router_reorder_workspace_size(T, ngroups))
+
+
+class RouterReorderCall:
+    """Arguments of wide_router_reorder with outputs and workspace allocated once:
+    run() enqueues router -> packed bits -> per-group partition."""
+
+    def __init__(self, X, W1, W2, act: str = "silu", tile: int = WIDE_TOKEN_TILE,
+                 return_mask: bool = False, return_logits: bool = False):
+        for name, t in (("X", X), ("W1", W1), ("W2", W2)):
+            _need_cuda(name, t)
+        if any(t.dtype != torch.bfloat16 for t in (X, W1, W2)):
+            raise ValueError("X, W1 and W2 must be bfloat16")
+        T, D = X.shape
+        r = W1.shape[0]
+        if W1.shape != (r, D) or W2.dim() != 2 or W2.shape[1] != r or W2.shape[0] % 2:
+            raise ValueError("expected W1 [r, D] and W2 [2 * ngroups, r]")
+        ng = W2.shape[0] // 2
+        dev = X.device
+        self.args = (X, W1, W2)
+        self.T, self.D, self.r, self.ng, self.act, self.tile = T, D, r, ng, _ACTS[act], tile
+        self.mask = torch.empty((T, ng), dtype=torch.uint8, device=dev) if return_mask else None
+        self.logits = (torch.empty((T, ng, 2), dtype=torch.float32, device=dev)
+                       if return_logits else None)
+        self.perm = torch.empty((ng, T), dtype=torch.int32, device=dev)
+        self.counts = torch.empty(ng, dtype=torch.int32, device=dev)
+        self.padded = torch.empty(ng, dtype=torch.int32, device=dev)
+        n = router_reorder_workspace_size(T, ng)
+        self.workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+
+    def run(self):
+        X, W1, W2 = self.args
+        _lib.check(_lib.load().wide_router_reorder(
+            X.data_ptr(), W1.data_ptr(), W2.data_ptr(), self.T, self.D, self.r, self.ng, self.act,
+            WIDE_BF16, self.tile, None if self.mask is None else self.mask.data_ptr(),
+            None if self.logits is None else self.logits.data_ptr(), self.perm.data_ptr(),
+            self.counts.data_ptr(), self.padded.data_ptr(), self.workspace.data_ptr(),
+            self.workspace.numel(), _stream_ptr(X.device)))
+        return self.perm, self.counts, self.padded
+
+
+def router_reorder(X, W1, W2, act: str = "silu", tile: int = WIDE_TOKEN_TILE,
+                   return_mask: bool = False):
+    """Router fused with the mask reorder -> (perm [ng, T], counts [ng], padded [ng]) int32,
+    plus the mask [T, ng] uint8 if return_mask."""
+    call = RouterReorderCall(X, W1, W2, act, tile, return_mask=return_mask)
+    out = call.run()
+    return (*out, call.mask) if return_mask else out
 
 
 # ---------------------------------------------------------------- attention

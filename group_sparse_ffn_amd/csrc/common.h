@@ -46,6 +46,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
 
+// Workgroup barrier for LDS hand-offs only: orders this workgroup's LDS
+// accesses across the barrier (fences scoped to LDS) without the release
+// fence of __syncthreads, which also waits for every outstanding global
+// store to complete.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // LDS tiles hold rows of 64 bf16 (128 bytes = 8 chunks of 16 bytes). Chunk c
 // of row r is stored at chunk position c ^ (r & 7): eight consecutive rows
 // reading the same logical chunk then hit eight different 16-byte bank groups.
@@ -63,7 +73,8 @@ hipError_t launch_reorder(const uint8_t* mask, int T, int ng, int tile, int32_t*
                           int32_t* counts, int32_t* padded, uint32_t* maskbits,
                           hipStream_t stream);
 
-// The same reorder from packed mask bits (made by launch_pack_mask_bits).
+// The same reorder from packed mask bits (made by launch_pack_mask_bits or by
+// the router kernel).
 hipError_t launch_reorder_from_bits(const uint32_t* maskbits, int T, int ng, int tile,
                                     int32_t* perm, int32_t* counts, int32_t* padded,
                                     hipStream_t stream);
@@ -142,10 +153,12 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                                    float* part, hipStream_t stream);
 
 // Bottleneck router: mask[t, g] = argmax over the two logits of group g is
-// class 0 (act 0 identity, 1 relu, 2 silu); logits [T, ng, 2] optional.
+// class 0 (act 0 identity, 1 relu, 2 silu). Each output is optional (NULL =
+// not written): mask bytes [T, ng], logits [T, ng, 2], and the decisions packed
+// as maskbits [ng, ceil(T/32)] (the layout of launch_pack_mask_bits).
 hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
                               int D, int r, int ng, int act, uint8_t* mask, float* logits,
-                              hipStream_t stream);
+                              uint32_t* maskbits, hipStream_t stream);
 
 // Device address of the no-allocation entry point's scratch array
 // (WIDE_NOALLOC_SCRATCH_BYTES, 256-byte aligned) on the device that runs

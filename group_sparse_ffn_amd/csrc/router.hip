@@ -47,6 +47,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
                                             const uint16_t* __restrict__ W2, int T, int D, int ng,
                                             int act, uint8_t* __restrict__ mask,
                                             float* __restrict__ logits,
+                                            uint32_t* __restrict__ maskbits, int words,
                                             float (*s_part)[16 * kRtRB][R],
                                             float (*s_z)[R + 1], uint8_t (*s_mask)[kRtGC]) {
   constexpr int kRtTok = 16 * kRtRB;
@@ -146,7 +147,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         s_part[wave][16 * b + 4 * (lane >> 4) + e][16 * f + (lane & 15)] = acc[b][f][e];
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < kRtTok * R; e += kRtThreads) {
     const int t = e / R, j = e % R;
     float a = 0.0f;
@@ -165,7 +166,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   constexpr int KQ = R / 4;
   const int ntok = min(kRtTok, T - t0);
   const int q = lane >> 4, c16 = lane & 15;
-  __syncthreads();  // s_z complete
+  lds_barrier();  // s_z complete
   for (int g0 = 0; g0 < ng; g0 += kRtGC) {
     const int gc = min(kRtGC, ng - g0);
     const int nob = (gc + 7) / 8;  // 16-column blocks of the chunk
@@ -196,12 +197,36 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
         if (logits && colok && t < ntok) logits[((size_t)(t0 + t) * ng + g0) * 2 + col] = acc[e];
       }
     }
-    __syncthreads();
-    for (int e = tid; e < ntok * gc; e += kRtThreads) {
-      const int t = e / gc, gl = e % gc;
-      mask[(size_t)(t0 + t) * ng + g0 + gl] = s_mask[t][gl];
+    lds_barrier();
+    if (mask != nullptr) {
+      for (int e = tid; e < ntok * gc; e += kRtThreads) {
+        const int t = e / gc, gl = e % gc;
+        mask[(size_t)(t0 + t) * ng + g0 + gl] = s_mask[t][gl];
+      }
     }
-    __syncthreads();  // s_mask is refilled by the next chunk
+    if (maskbits != nullptr) {
+      // packed bits straight from the decisions in LDS: thread (j, h) reads
+      // the 4-group words of tokens 32 h .. 32 h + 31 (consecutive threads,
+      // consecutive words: no bank conflict) and builds the bit words of
+      // groups 4 j .. 4 j + 3; tokens past T give 0 bits.
+      // maskbits[g, w] bit b = decision of token 32 w + b.
+      constexpr int kHalves = (kRtTok + 31) / 32;
+      const int nj = (gc + 3) / 4;
+      const int j = tid / kHalves, h = tid % kHalves;
+      const int nt = min(32, ntok - 32 * h);  // <= 0: the word lies past T (none stored)
+      if (tid < nj * kHalves && nt > 0) {
+        uint32_t b[4] = {0u, 0u, 0u, 0u};
+        for (int t = 0; t < nt; ++t) {
+          const uint32_t w = *(const uint32_t*)&s_mask[32 * h + t][4 * j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) b[q] |= ((w >> (8 * q)) & 0xFFu) != 0 ? (1u << t) : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * j + q < gc) maskbits[(size_t)(g0 + 4 * j + q) * words + (t0 >> 5) + h] = b[q];
+      }
+    }
+    lds_barrier();  // s_mask is refilled by the next chunk
   }
 }
 
@@ -209,11 +234,13 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   __global__ __launch_bounds__(64 * NW) void NAME(                                             \
       const uint16_t* __restrict__ X, const uint16_t* __restrict__ W1,                         \
       const uint16_t* __restrict__ W2, int T, int D, int ng, int act,                          \
-      uint8_t* __restrict__ mask, float* __restrict__ logits) {                                \
+      uint8_t* __restrict__ mask, float* __restrict__ logits, uint32_t* __restrict__ maskbits, \
+      int words) {                                                                             \
     __shared__ float s_part[NW][16 * RB][R];                                                   \
     __shared__ float s_z[16 * RB][R + 1];                                                      \
     __shared__ uint8_t s_mask[16 * RB][kRtGC];                                                 \
-    router_body<R, RB, NW>(X, W1, W2, T, D, ng, act, mask, logits, s_part, s_z, s_mask);       \
+    router_body<R, RB, NW>(X, W1, W2, T, D, ng, act, mask, logits, maskbits, words, s_part,    \
+                           s_z, s_mask);                                                       \
   }
 WIDE_ROUTER_KERNEL(router_kernel_16, 16, 4, 8)
 WIDE_ROUTER_KERNEL(router_kernel_32, 32, 4, 8)
@@ -227,31 +254,18 @@ WIDE_ROUTER_KERNEL(router_small_kernel_64, 64, 1, 16)
 
 hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
                               int D, int r, int ng, int act, uint8_t* mask, float* logits,
-                              hipStream_t stream) {
+                              uint32_t* maskbits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (T <= 16) {
-    const dim3 grid(1), block(1024);
-    if (r == 16)
-      hipLaunchKernelGGL(router_small_kernel_16, grid, block, 0, stream, X, W1, W2, T, D, ng, act,
-                         mask, logits);
-    else if (r == 32)
-      hipLaunchKernelGGL(router_small_kernel_32, grid, block, 0, stream, X, W1, W2, T, D, ng, act,
-                         mask, logits);
-    else
-      hipLaunchKernelGGL(router_small_kernel_64, grid, block, 0, stream, X, W1, W2, T, D, ng, act,
-                         mask, logits);
-    return hipGetLastError();
-  }
-  const dim3 grid((T + 63) / 64), block(512);
-  if (r == 16)
-    hipLaunchKernelGGL(router_kernel_16, grid, block, 0, stream, X, W1, W2, T, D, ng, act, mask,
-                       logits);
-  else if (r == 32)
-    hipLaunchKernelGGL(router_kernel_32, grid, block, 0, stream, X, W1, W2, T, D, ng, act, mask,
-                       logits);
-  else
-    hipLaunchKernelGGL(router_kernel_64, grid, block, 0, stream, X, W1, W2, T, D, ng, act, mask,
-                       logits);
+  const int words = (T + 31) / 32;
+  typedef void (*K)(const uint16_t*, const uint16_t*, const uint16_t*, int, int, int, int, uint8_t*,
+                    float*, uint32_t*, int);
+  const bool small = T <= 16;
+  const K k = small ? (r == 16 ? router_small_kernel_16 : r == 32 ? router_small_kernel_32
+                                                                  : router_small_kernel_64)
+                    : (r == 16 ? router_kernel_16 : r == 32 ? router_kernel_32 : router_kernel_64);
+  const dim3 grid(small ? 1 : (T + 63) / 64), block(small ? 1024 : 512);
+  hipLaunchKernelGGL(k, grid, block, 0, stream, X, W1, W2, T, D, ng, act, mask, logits, maskbits,
+                     words);
   return hipGetLastError();
 }
 

@@ -636,14 +636,13 @@ WIDE_API wide_status_t wide_attention_decode(const void* q, const void* K, const
   return ok();
 }
 
-WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
-                                           int32_t T, int32_t D, int32_t r, int32_t ngroups,
-                                           wide_act_t act, wide_dtype_t dtype, uint8_t* mask,
-                                           float* logits, void* stream) {
-  const int32_t dt = raw(dtype);
-  const int32_t ac = raw(act);
+namespace {
+
+// Host checks shared by the router entry points (everything but the outputs).
+wide_status_t validate_router(const void* X, const void* W1, const void* W2, int32_t T, int32_t D,
+                              int32_t r, int32_t ngroups, int32_t ac, int32_t dt) {
   if (!W1 || !W2) return fail(WIDE_ERR_NULL, "W1 and W2 must be non-NULL");
-  if (T != 0 && (!X || !mask)) return fail(WIDE_ERR_NULL, "X and mask must be non-NULL when T > 0");
+  if (T != 0 && !X) return fail(WIDE_ERR_NULL, "X must be non-NULL when T > 0");
   if (dt != WIDE_F32 && dt != WIDE_BF16) return fail(WIDE_ERR_DTYPE, "unknown dtype %d", dt);
   if (T < 0 || D <= 0 || r <= 0 || ngroups <= 0)
     return fail(WIDE_ERR_SHAPE, "need T >= 0 and D, r, ngroups >= 1 (T=%d D=%d r=%d ngroups=%d)", T, D,
@@ -656,14 +655,72 @@ WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const 
                 D, r);
   if ((int64_t)T * D >= (1ll << 31) || (int64_t)T * ngroups >= (1ll << 31))
     return fail(WIDE_ERR_UNSUPPORTED, "T*D and T*ngroups must stay below 2^31");
-  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) ||
-      (reinterpret_cast<uintptr_t>(logits) & 7u) != 0)
-    return fail(WIDE_ERR_ALIGN, "X, W1 and W2 must be 16-byte aligned, logits 8-byte aligned");
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2))
+    return fail(WIDE_ERR_ALIGN, "X, W1 and W2 must be 16-byte aligned");
+  return WIDE_OK;
+}
+
+size_t router_bits_bytes(int64_t T, int64_t ngroups) {
+  return round_up((size_t)(ngroups * ((T + 31) / 32)) * 4, 256);
+}
+
+}  // namespace
+
+WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
+                                           int32_t T, int32_t D, int32_t r, int32_t ngroups,
+                                           wide_act_t act, wide_dtype_t dtype, uint8_t* mask,
+                                           float* logits, void* stream) {
+  const int32_t ac = raw(act);
+  wide_status_t st = validate_router(X, W1, W2, T, D, r, ngroups, ac, raw(dtype));
+  if (st != WIDE_OK) return st;
+  if (T != 0 && !mask) return fail(WIDE_ERR_NULL, "mask must be non-NULL when T > 0");
+  if ((reinterpret_cast<uintptr_t>(logits) & 7u) != 0)
+    return fail(WIDE_ERR_ALIGN, "logits must be 8-byte aligned");
   if (T == 0) return ok();
   const hipError_t e = wide::launch_router_bf16((const uint16_t*)X, (const uint16_t*)W1,
                                                 (const uint16_t*)W2, T, D, r, ngroups, ac,
-                                                mask, logits, static_cast<hipStream_t>(stream));
+                                                mask, logits, nullptr,
+                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "router launch");
+  return ok();
+}
+
+WIDE_API size_t wide_router_reorder_workspace_size(int32_t T, int32_t ngroups) {
+  if (T < 0 || ngroups < 1) return 0;
+  return router_bits_bytes(T, ngroups);
+}
+
+WIDE_API wide_status_t wide_router_reorder(const void* X, const void* W1, const void* W2,
+                                           int32_t T, int32_t D, int32_t r, int32_t ngroups,
+                                           wide_act_t act, wide_dtype_t dtype, int32_t tile,
+                                           uint8_t* mask, float* logits, int32_t* perm,
+                                           int32_t* counts, int32_t* padded, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  const int32_t ac = raw(act);
+  wide_status_t st = validate_router(X, W1, W2, T, D, r, ngroups, ac, raw(dtype));
+  if (st != WIDE_OK) return st;
+  if (!counts || !padded) return fail(WIDE_ERR_NULL, "counts and padded must be non-NULL");
+  if (T != 0 && !perm) return fail(WIDE_ERR_NULL, "perm must be non-NULL when T > 0");
+  if (tile < 1) return fail(WIDE_ERR_SHAPE, "need tile >= 1 (tile=%d)", tile);
+  if ((reinterpret_cast<uintptr_t>(logits) & 7u) != 0)
+    return fail(WIDE_ERR_ALIGN, "logits must be 8-byte aligned");
+  const size_t need = router_bits_bytes(T, ngroups);
+  if (!workspace) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* maskbits = static_cast<uint32_t*>(workspace);
+  hipError_t e = hipSuccess;
+  if (T > 0) {
+    e = wide::launch_router_bf16((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)W2, T, D,
+                                 r, ngroups, ac, mask, logits, maskbits, s);
+    if (e != hipSuccess) return hip_status(e, "router launch");
+  }
+  // T == 0: the partition still writes counts = padded = 0
+  e = wide::launch_reorder_from_bits(maskbits, T, ngroups, tile, perm, counts, padded, s);
+  if (e != hipSuccess) return hip_status(e, "mask reorder launch");
   return ok();
 }
 

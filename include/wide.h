@@ -331,6 +331,36 @@ wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
                                   wide_dtype_t dtype, uint8_t* mask, float* logits, void* stream);
 
 /*
+ * wide_router_reorder - the router of wide_router_forward fused with the mask
+ * reorder of wide_reorder_masks: from the activations straight to the per-group
+ * row lists, with no mask round trip (the pages count router execution and
+ * mask reordering in the work that pruning does not accelerate: WIDE paper
+ * Sec. 4.2, the layer-time breakdown; ai.info summary, "How decisions are
+ * made"). The router kernel packs its decisions into bits [ngroups,
+ * ceil(T/32)] in the workspace as it makes them (one ballot per group over
+ * each block of 64 tokens), and a partition kernel turns the bits into the
+ * stable per-group partition.
+ *
+ *   X, W1, W2, T, D, r, ngroups, act, dtype: as wide_router_forward.
+ *   tile            >= 1: padded[g] = ceil(counts[g] / tile) * tile.
+ *   mask            [T, ngroups] uint8, optional (NULL = not written): the
+ *                   decisions, as wide_router_forward writes them.
+ *   logits          [T, ngroups, 2] fp32, optional, 8-byte aligned.
+ *   perm, counts, padded: as wide_reorder_masks (perm may be NULL when T == 0):
+ *                   exactly wide_reorder_masks applied to the mask above.
+ *   workspace       device, 256-byte aligned, at least
+ *                   wide_router_reorder_workspace_size(T, ngroups) bytes.
+ * Errors: as wide_router_forward, plus WIDE_ERR_SHAPE (tile < 1),
+ * WIDE_ERR_WORKSPACE.
+ */
+size_t wide_router_reorder_workspace_size(int32_t T, int32_t ngroups);
+wide_status_t wide_router_reorder(const void* X, const void* W1, const void* W2, int32_t T,
+                                  int32_t D, int32_t r, int32_t ngroups, wide_act_t act,
+                                  wide_dtype_t dtype, int32_t tile, uint8_t* mask, float* logits,
+                                  int32_t* perm, int32_t* counts, int32_t* padded,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * wide_attention_prefill - head-group-pruned causal attention for one sequence
  * (ai.info summary, "What gets pruned": the attention unit is a GQA-aligned
  * group of H_q/H_k query heads, and each token keeps or skips each group;

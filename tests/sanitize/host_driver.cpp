@@ -158,13 +158,15 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
   return hipSuccess;
 }
 hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
-                              int D, int r, int ng, int, uint8_t* mask, float* logits, hipStream_t) {
+                              int D, int r, int ng, int, uint8_t* mask, float* logits,
+                              uint32_t* maskbits, hipStream_t) {
   ++g_launches;
   rd(X, (size_t)T * D * 2);
   rd(W1, (size_t)r * D * 2);
   rd(W2, (size_t)2 * ng * r * 2);
-  wr(mask, (size_t)T * ng);
+  if (mask) wr(mask, (size_t)T * ng);
   if (logits) wr(logits, (size_t)T * ng * 2 * 4);
+  if (maskbits) wr(maskbits, (size_t)ng * words(T) * 4);
   return hipSuccess;
 }
 // the scratch array of wide_ffn_forward_noalloc: an exact-size host buffer
@@ -307,6 +309,21 @@ void attention_case(int T, int Hq, int Hk) {
                                0, wd.p, nd - 1, nullptr) == WIDE_ERR_WORKSPACE);
 }
 
+void router_reorder_case(int T, int D, int r, int ng, bool mask_out) {
+  Buf X((size_t)T * D * 2), W1((size_t)r * D * 2), W2((size_t)2 * ng * r * 2), mask((size_t)T * ng),
+      perm((size_t)ng * T * 4), counts((size_t)ng * 4), padded((size_t)ng * 4);
+  const size_t need = wide_router_reorder_workspace_size(T, ng);
+  Buf ws(need);
+  EXPECT(wide_router_reorder(X.p, W1.p, W2.p, T, D, r, ng, WIDE_ACT_SILU, WIDE_BF16, 7,
+                             mask_out ? (uint8_t*)mask.p : nullptr, nullptr, (int32_t*)perm.p,
+                             (int32_t*)counts.p, (int32_t*)padded.p, ws.p, need,
+                             nullptr) == WIDE_OK);
+  if (need > 0)
+    EXPECT(wide_router_reorder(X.p, W1.p, W2.p, T, D, r, ng, WIDE_ACT_SILU, WIDE_BF16, 7, nullptr,
+                               nullptr, (int32_t*)perm.p, (int32_t*)counts.p, (int32_t*)padded.p,
+                               ws.p, need - 1, nullptr) == WIDE_ERR_WORKSPACE);
+}
+
 void router_case(int T, int D, int r, int ng, bool logits) {
   Buf X((size_t)T * D * 2), W1((size_t)r * D * 2), W2((size_t)2 * ng * r * 2), mask((size_t)T * ng),
       lg((size_t)T * ng * 2 * 4);
@@ -346,6 +363,9 @@ int main() {
   router_case(100, 256, 32, 7, true);
   router_case(1, 512, 16, 40, false);
   router_case(0, 64, 64, 3, false);
+  router_reorder_case(1000, 256, 32, 37, true);
+  router_reorder_case(33, 64, 16, 1, false);
+  router_reorder_case(0, 64, 16, 5, false);
   // rejected arguments: nothing launched, a message set
   const int before = g_launches;
   std::vector<uint8_t> small(4096);

@@ -381,3 +381,28 @@ def test_noalloc_rejects_before_any_hip_call(lib):
         _lib.WIDE_NOALLOC_SCRATCH_BYTES
     # T == 0 with H_out NULL is a valid no-op
     assert call(T=0, H=None) == _lib.WIDE_OK
+
+
+def test_router_reorder_validation(lib):
+    ws = lib.wide_router_reorder_workspace_size(1000, 112)
+    assert ws == (112 * 32 * 4 + 255) // 256 * 256
+    assert lib.wide_router_reorder_workspace_size(-1, 4) == 0
+    base = [FAKE, FAKE, FAKE, 64, 256, 32, 8, _lib.WIDE_ACT_SILU, _lib.WIDE_BF16, 256, None, None,
+            FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return lib.wide_router_reorder(*a)
+
+    assert call(0, None) == _lib.WIDE_ERR_NULL          # X
+    assert call(12, None) == _lib.WIDE_ERR_NULL         # perm
+    assert call(13, None) == _lib.WIDE_ERR_NULL         # counts
+    assert call(9, 0) == _lib.WIDE_ERR_SHAPE            # tile
+    assert call(5, 24) == _lib.WIDE_ERR_UNSUPPORTED     # r
+    assert call(7, 5) == _lib.WIDE_ERR_SHAPE            # activation
+    assert call(8, _lib.WIDE_F32) == _lib.WIDE_ERR_UNSUPPORTED
+    assert call(15, None) == _lib.WIDE_ERR_WORKSPACE
+    assert call(16, 16) == _lib.WIDE_ERR_WORKSPACE
+    assert call(15, FAKE + 16) == _lib.WIDE_ERR_ALIGN
+    assert call(11, FAKE + 4) == _lib.WIDE_ERR_ALIGN    # logits

@@ -124,3 +124,75 @@ def test_router_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(mask, eager), f"replay {i} differs from eager"
+
+
+# ----------------------------------------------------------------------------- router fused with the reorder
+
+# wide_router_reorder: the row lists equal the oracle's stable partition of the
+# router's own mask, bit for bit (the decision is the kernel's, so the
+# reference partition is taken of the GPU mask that the same call returns,
+# and that mask is also checked against wide_router_forward's, bit for bit);
+# T from 1 to the Llama prefill length, words split over 64-token blocks
+# (odd word counts included), tiles of 1, 7 and 256.
+@pytest.mark.parametrize("T,D,r,ng,tile", [
+    (1, 256, 16, 5, 256), (16, 512, 32, 112, 256), (17, 256, 64, 3, 7), (100, 1024, 32, 37, 1),
+    (1000, 4096, 32, 112, 256), (16384, 4096, 32, 112, 256), (4096, 5120, 32, 136, 256),
+    (33, 96, 16, 1, 256), (2049, 3072, 16, 512, 128),
+])
+def test_router_reorder_equals_reorder_of_router_mask(T, D, r, ng, tile):
+    X, W1, W2 = inputs(7 * T + ng, T, D, r, ng)
+    Xd, W1d, W2d = X.to(DEV), W1.to(DEV), W2.to(DEV)
+    call = wide.RouterReorderCall(Xd, W1d, W2d, "silu", tile, return_mask=True)
+    call.workspace.fill_(0xA5)
+    call.perm.fill_(-7)
+    perm, counts, padded = call.run()
+    mask_ref = wide.router_forward(Xd, W1d, W2d, "silu")
+    torch.cuda.synchronize()
+    m = call.mask.cpu().numpy()
+    assert np.array_equal(m, mask_ref.cpu().numpy())
+    rp, rc, rpad = oracle.reorder(m, tile)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(padded.cpu().numpy(), rpad)
+    # and the decisions are the router's (checked against the oracle's logits)
+    if T <= 1000:
+        check(X, W1, W2, "silu")
+
+
+def test_router_reorder_without_mask_output_and_t0():
+    T, D, r, ng = 300, 512, 32, 24
+    X, W1, W2 = inputs(99, T, D, r, ng)
+    Xd, W1d, W2d = X.to(DEV), W1.to(DEV), W2.to(DEV)
+    perm, counts, padded = wide.router_reorder(Xd, W1d, W2d, "relu", 64)
+    mask = wide.router_forward(Xd, W1d, W2d, "relu")
+    p2, c2, pad2 = wide.reorder_masks(mask, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(perm, p2) and torch.equal(counts, c2) and torch.equal(padded, pad2)
+    # T == 0: counts and padded are zero
+    X0 = torch.empty((0, D), dtype=torch.bfloat16, device=DEV)
+    p0, c0, pad0 = wide.router_reorder(X0, W1d, W2d, "relu", 64)
+    torch.cuda.synchronize()
+    assert p0.numel() == 0 and bool((c0 == 0).all()) and bool((pad0 == 0).all())
+
+
+def test_router_reorder_graph_replay_matches_eager():
+    T, D, r, ng = 1000, 1024, 32, 56
+    X, W1, W2 = inputs(5, T, D, r, ng)
+    Xd, W1d, W2d = X.to(DEV), W1.to(DEV), W2.to(DEV)
+    call = wide.RouterReorderCall(Xd, W1d, W2d, "silu", 256)
+    eager = [t.clone() for t in call.run()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call.run()
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        call.perm.fill_(-1)
+        call.counts.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip((call.perm, call.counts, call.padded), eager)), i
