@@ -8,7 +8,8 @@
 // per L2 channel), and that design issues one atomic per (active token, group,
 // output column): about 15 GB at the Llama3.1-8B prefill shape, over 10 ms.
 // So this kernel keeps the pages' group-level skipping but owns its outputs:
-//   * a workgroup owns Y[256 tokens (natural order), 256 output columns] and
+//   * a workgroup owns Y[256 tokens (natural order), 256 output columns] (or
+//     128 x 128 when 256-tiles would leave CUs idle) and
 //     accumulates over the K axis in registers; every output has one writer,
 //     no atomics, no zero-initialised buffer and a fixed summation order;
 //   * 64-channel K-blocks whose groups are inactive for every token of the
@@ -34,22 +35,34 @@ namespace wide {
 
 namespace {
 
-constexpr int kTile = 256;
 constexpr int kMaxSteps = 1024;  // d_ff / 64 limit (d_ff <= 65536)
-using DS = core::Shape<kTile, kTile, 2, 4>;
 constexpr int kCopyWaves = 4;
-constexpr int kCB = DS::PBLOCKS / kCopyWaves;  // blocks per operand per copying wave
-static_assert(DS::PBLOCKS == DS::QBLOCKS && 8 * kCopyWaves == 32, "mask word i covers block i");
 
-__global__ __launch_bounds__(512, 1) void down_bf16_kernel(
+// Tile shapes: kTile tokens x kTile output columns. 256 for large problems;
+// 128 when 256-tiles would leave CUs idle (four times the workgroups).
+template <int kTile>
+struct DownShape {
+  using DS = core::Shape<kTile, kTile, 2, 4>;
+  static constexpr int kCB = DS::PBLOCKS / kCopyWaves;  // blocks per operand per copying wave
+  static constexpr int kWords = kTile / 32;            // mask words per token tile
+  static_assert(DS::PBLOCKS == DS::QBLOCKS && 8 * kCopyWaves == 32, "mask word i covers block i");
+  static_assert(kCB == kWords, "block i of a copying wave holds mask word i");
+  // epilogue staging rows of [kTile tokens][kTile columns] bf16 per LDS stage
+  static constexpr int kRowB = kTile * 2;
+  static constexpr int kStgRows = DS::STAGE / kRowB;
+  static_assert(2 * kStgRows >= kTile, "epilogue staging fits the two stages");
+};
+
+template <int kTile>
+__device__ __forceinline__ void down_body(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint32_t* __restrict__ maskbits, int T, int d, int d_ff, int G, uint16_t* __restrict__ Y,
-    int ntt, int nnt, int words) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[DS::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB[DS::STAGE];
-  __shared__ uint16_t s_steps[kMaxSteps];
-  __shared__ __attribute__((aligned(16))) uint32_t s_mw[kDownMaxGroups * 8];  // [group][8 words]: the tile's mask bits
-  __shared__ int s_wave_cnt[8];
+    int ntt, int nnt, int words, uint8_t* sA, uint8_t* sB, uint16_t* s_steps, uint32_t* s_mw,
+    int* s_wave_cnt) {
+  using SH = DownShape<kTile>;
+  using DS = typename SH::DS;
+  constexpr int kCB = SH::kCB;
+  constexpr int kW = SH::kWords;
 
   const int total = ntt * nnt;
   const int per_xcd = (total + 7) / 8;
@@ -69,20 +82,20 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
   // into the bit rows and words past the last one are masked to zero, so no
   // load sits in a divergent branch.
   if (table) {
-    constexpr int kTab = kDownMaxGroups * 8 / 512;
+    constexpr int kTab = kDownMaxGroups * kW / 512;
     uint32_t v[kTab];
 #pragma unroll
     for (int i = 0; i < kTab; ++i) {
-      if (512 * i >= ng * 8) break;
-      const int e = min(tid + 512 * i, ng * 8 - 1);
-      const int g = e >> 3, wi = e & 7;
+      if (512 * i >= ng * kW) break;
+      const int e = min(tid + 512 * i, ng * kW - 1);
+      const int g = e / kW, wi = e % kW;
       v[i] = maskbits[(size_t)g * words + min(w0 + wi, words - 1)] &
              (w0 + wi < words ? 0xFFFFFFFFu : 0u);
     }
 #pragma unroll
     for (int i = 0; i < kTab; ++i) {
-      if (512 * i >= ng * 8) break;
-      if (tid + 512 * i < ng * 8) s_mw[tid + 512 * i] = v[i];
+      if (512 * i >= ng * kW) break;
+      if (tid + 512 * i < ng * kW) s_mw[tid + 512 * i] = v[i];
     }
     __syncthreads();
   }
@@ -100,11 +113,11 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
       for (int g = glo; g <= ghi; ++g) {
         if (table) {
 #pragma unroll
-          for (int wi = 0; wi < 8; ++wi) acc |= s_mw[g * 8 + wi];
+          for (int wi = 0; wi < kW; ++wi) acc |= s_mw[g * kW + wi];
         } else {
           const uint32_t* mw = maskbits + (size_t)g * words;
 #pragma unroll
-          for (int wi = 0; wi < 8; ++wi)
+          for (int wi = 0; wi < kW; ++wi)
             acc |= mw[min(w0 + wi, words - 1)] & (w0 + wi < words ? 0xFFFFFFFFu : 0u);
         }
       }
@@ -166,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
     const uint32_t sh = rw & 31;
     if (table) {
       const int k0 = (int)s_steps[s] * 64;
-      const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * 8;  // this lane's group
+      const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * kW;  // this lane's group
 #pragma unroll
       for (int i = 0; i < kCB; ++i)
         vq_next[i] = ((mw[i] >> sh) & 1u) ? voff_q[i] : 0x80000000u;
@@ -200,13 +213,18 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
   core::mainloop<DS>(f, sA, sB, nst, wp, wq, lane, DS::FQ, issue, prepare);
   __syncthreads();  // every wave is done with the stages: reuse them for the epilogue
 
-  // Epilogue: staged as [256 tokens][256 columns] bf16 (512-byte rows, chunk
-  // c of row r at c ^ (r & 31)); token rows 0..127 in sA, 128..255 in sB.
+  // Epilogue: staged as [kTile tokens][kTile columns] bf16 (kTile * 2-byte
+  // rows, chunk c of row r at c ^ (r % chunks-per-row)); the first kStgRows
+  // token rows in sA, the rest in sB.
+  constexpr int kRowB = SH::kRowB;
+  constexpr int kCpr = kTile / 8;  // 16-byte chunks per staged row
+  constexpr int kStg = SH::kStgRows;
+  auto srow = [&](int r) -> uint8_t* { return r < kStg ? sA + r * kRowB : sB + (r - kStg) * kRowB; };
   const int lrow = lane & 31, lhalf = lane >> 5;
 #pragma unroll
   for (int j = 0; j < DS::FQ; ++j) {
     const int r = wq * DS::QW + j * 32 + lrow;
-    uint8_t* row = (r < 128 ? sA : sB) + (r & 127) * 512;
+    uint8_t* row = srow(r);
 #pragma unroll
     for (int i = 0; i < DS::FP; ++i) {
 #pragma unroll
@@ -215,34 +233,64 @@ __global__ __launch_bounds__(512, 1) void down_bf16_kernel(
         const int c = nl >> 3, hh = (nl >> 2) & 1;
         const u32x2 v = {pack_bf16x2(f.acc[i][j][4 * q], f.acc[i][j][4 * q + 1]),
                          pack_bf16x2(f.acc[i][j][4 * q + 2], f.acc[i][j][4 * q + 3])};
-        *(u32x2*)(row + ((c ^ (r & 31)) << 4) + hh * 8) = v;
+        *(u32x2*)(row + ((c ^ (r % kCpr)) << 4) + hh * 8) = v;
       }
     }
   }
   __syncthreads();
   const int nrows = min(kTile, T - t0);
   const int ncch = min(kTile, d - n0) / 8;  // 16-byte column chunks that exist
-  for (int e = tid; e < nrows * 32; e += 512) {
-    const int r = e >> 5, c = e & 31;
+  for (int e = tid; e < nrows * kCpr; e += 512) {
+    const int r = e / kCpr, c = e % kCpr;
     if (c >= ncch) continue;
-    const uint8_t* row = (r < 128 ? sA : sB) + (r & 127) * 512;
-    const u32x4 v = *(const u32x4*)(row + ((c ^ (r & 31)) << 4));
+    const u32x4 v = *(const u32x4*)(srow(r) + ((c ^ (r % kCpr)) << 4));
     *(u32x4*)(Y + (size_t)(t0 + r) * d + n0 + c * 8) = v;
   }
 }
 
+// One plain kernel per tile size (a kernel template that passes a local lambda
+// to the mainloop loses its host launch stub with this toolchain).
+#define WIDE_DOWN_KERNEL(NAME, TILE)                                                          \
+  __global__ __launch_bounds__(512, 1) void NAME(                                             \
+      const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,                        \
+      const uint32_t* __restrict__ maskbits, int T, int d, int d_ff, int G,                   \
+      uint16_t* __restrict__ Y, int ntt, int nnt, int words) {                                \
+    using DSx = DownShape<TILE>::DS;                                                          \
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[DSx::STAGE];                         \
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[DSx::STAGE];                         \
+    __shared__ uint16_t s_steps[kMaxSteps];                                                   \
+    __shared__ __attribute__((aligned(16))) uint32_t s_mw[kDownMaxGroups * (TILE / 32)];     \
+    __shared__ int s_wave_cnt[8];                                                             \
+    down_body<TILE>(H, Wd, maskbits, T, d, d_ff, G, Y, ntt, nnt, words, sA, sB, s_steps,      \
+                    s_mw, s_wave_cnt);                                                        \
+  }
+WIDE_DOWN_KERNEL(down_bf16_kernel, 256)
+WIDE_DOWN_KERNEL(down_bf16_kernel_t128, 128)
+#undef WIDE_DOWN_KERNEL
+
 }  // namespace
+
+int down_tile(int T, int d) {
+  // 256 x 256 tiles unless fewer than 128 of them would leave most of the 256
+  // CUs idle; then 128 x 128 tiles run four times as many workgroups. Measured
+  // at 50% masks: 2048^3 60 -> 41 us with 128-tiles (64 large tiles), but
+  // 4096^3 127 -> 183 us (256 large tiles) and 384 / 320 large tiles
+  // (Llama3.2-3B T = 8192, Qwen3-14B T = 4096) slower by 0.1 ms
+  const long long t256 = (long long)((T + 255) / 256) * ((d + 255) / 256);
+  return t256 < 128 ? 128 : 256;
+}
 
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
                             int d, int d_ff, int G, uint16_t* Y, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int ntt = (T + kTile - 1) / kTile;
-  const int nnt = (d + kTile - 1) / kTile;
+  const int tile = down_tile(T, d);
+  const int ntt = (T + tile - 1) / tile;
+  const int nnt = (d + tile - 1) / tile;
   const int words = (T + 31) / 32;
   const int total = ntt * nnt;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(down_bf16_kernel, dim3(per_xcd * 8), dim3(512), 0, stream, H, Wd, maskbits, T,
-                     d, d_ff, G, Y, ntt, nnt, words);
+  hipLaunchKernelGGL(tile == 256 ? down_bf16_kernel : down_bf16_kernel_t128, dim3(per_xcd * 8),
+                     dim3(512), 0, stream, H, Wd, maskbits, T, d, d_ff, G, Y, ntt, nnt, words);
   return hipGetLastError();
 }
 

@@ -30,16 +30,18 @@ namespace wide {
 
 namespace {
 
-constexpr int kTokTile = 256;
 constexpr int kCopyWaves = 4;
 
-template <int CW, bool SWIGLU>
+// TT: positions of the reordered row list per tile, 256 for large problems or
+// 128 (with channel blocks of 64 or more) when 256-tiles would leave CUs idle.
+template <int CW, bool SWIGLU, int TT = 256>
 struct MnShape {
   // a 16-channel plain block is padded to one 32-row fragment (zero rows)
   static constexpr int TP = SWIGLU ? 2 * CW : (CW < 32 ? 32 : CW);
-  static constexpr int WP = (TP >= 256) ? 2 : 1;
+  static constexpr int WP = (TP >= 256 || TT == 128) ? 2 : 1;
   static constexpr int WQ = 8 / WP;
-  using S = core::Shape<TP, kTokTile, WP, WQ>;
+  static constexpr int kTokTile = TT;
+  using S = core::Shape<TP, TT, WP, WQ>;
   static constexpr int PBLK = S::PBLOCKS, QBLK = S::QBLOCKS;
   static constexpr int NBLK = PBLK + QBLK;
   // Only waves 0..kCopyWaves-1 issue copies: each SIMD then runs one copying
@@ -50,7 +52,7 @@ struct MnShape {
   // epilogue staging: [256 positions][CW] bf16, split over the two stages
   static constexpr int ROWB = CW * 2;
   static constexpr int STG_ROWS = S::STAGE / ROWB;  // staged rows per LDS stage
-  static_assert(2 * STG_ROWS >= kTokTile, "epilogue staging fits the two stages");
+  static_assert(2 * STG_ROWS >= TT, "epilogue staging fits the two stages");
 };
 
 // The body is a device function template called from one plain kernel per
@@ -58,15 +60,16 @@ struct MnShape {
 // the mainloop loses its host launch stub with this toolchain.
 //   A [M, K] rows, gathered through perm; B and (SwiGLU) B2 [N, K]; C [M, N].
 //   Group g's row list is perm[g*M .. g*M + M), its active prefix counts[g].
-template <int CW, bool SWIGLU>
+template <int CW, bool SWIGLU, int TT>
 __device__ __forceinline__ void mn_body(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, int M, int K, int N, int G, uint16_t* __restrict__ C,
     int zero_inactive, int ntok_tiles, int nct, int total, uint8_t* sA, uint8_t* sB,
     int* s_tok) {
-  using SH = MnShape<CW, SWIGLU>;
+  using SH = MnShape<CW, SWIGLU, TT>;
   using S = typename SH::S;
+  constexpr int kTokTile = TT;
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so give
   // each XCD a contiguous range of (channel block, token tile) pairs; the
@@ -236,38 +239,58 @@ __device__ __forceinline__ void mn_body(
   }
 }
 
-#define WIDE_MN_KERNEL(NAME, CW, SWIGLU)                                                      \
+#define WIDE_MN_KERNEL(NAME, CW, SWIGLU, TT)                                                  \
   __global__ __launch_bounds__(512, 1) void NAME(                                             \
       const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,                         \
       const uint16_t* __restrict__ B2, const int32_t* __restrict__ perm,                      \
       const int32_t* __restrict__ counts, int M, int K, int N, int G,                         \
       uint16_t* __restrict__ C, int zero_inactive, int ntok_tiles, int nct, int total) {      \
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[MnShape<CW, SWIGLU>::S::STAGE];      \
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[MnShape<CW, SWIGLU>::S::STAGE];      \
-    __shared__ int s_tok[kTokTile];                                                           \
-    mn_body<CW, SWIGLU>(A, B, B2, perm, counts, M, K, N, G, C, zero_inactive, ntok_tiles,     \
-                        nct, total, sA, sB, s_tok);                                           \
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[MnShape<CW, SWIGLU, TT>::S::STAGE];  \
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[MnShape<CW, SWIGLU, TT>::S::STAGE];  \
+    __shared__ int s_tok[TT];                                                                 \
+    mn_body<CW, SWIGLU, TT>(A, B, B2, perm, counts, M, K, N, G, C, zero_inactive, ntok_tiles, \
+                            nct, total, sA, sB, s_tok);                                       \
   }
-WIDE_MN_KERNEL(gate_up_bf16_kernel_128, 128, true)
-WIDE_MN_KERNEL(gate_up_bf16_kernel_64, 64, true)
-WIDE_MN_KERNEL(gate_up_bf16_kernel_32, 32, true)
-WIDE_MN_KERNEL(gate_up_bf16_kernel_16, 16, true)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_256, 256, false)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_128, 128, false)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_64, 64, false)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_32, 32, false)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_16, 16, false)
+WIDE_MN_KERNEL(gate_up_bf16_kernel_128, 128, true, 256)
+WIDE_MN_KERNEL(gate_up_bf16_kernel_64, 64, true, 256)
+WIDE_MN_KERNEL(gate_up_bf16_kernel_32, 32, true, 256)
+WIDE_MN_KERNEL(gate_up_bf16_kernel_16, 16, true, 256)
+WIDE_MN_KERNEL(gate_up_bf16_kernel_128_t128, 128, true, 128)
+WIDE_MN_KERNEL(gate_up_bf16_kernel_64_t128, 64, true, 128)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_256, 256, false, 256)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_128, 128, false, 256)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_64, 64, false, 256)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_32, 32, false, 256)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_16, 16, false, 256)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_256_t128, 256, false, 128)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_128_t128, 128, false, 128)
+WIDE_MN_KERNEL(gemm_mn_bf16_kernel_64_t128, 64, false, 128)
 #undef WIDE_MN_KERNEL
 
 typedef void (*MnKernel)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*,
                          const int32_t*, int, int, int, int, uint16_t*, int, int, int, int);
 
-hipError_t launch_mn(MnKernel kernel, int CW, const uint16_t* A, const uint16_t* B,
+// 128-position tiles when the 256-position grid (before level-0 exits) would
+// leave CUs idle: fewer than 1024 workgroups (about two active per CU at 50%
+// masks) for an A side of up to 128 rows, fewer than 256 for a 256-row A side
+// (SwiGLU with 128 channels, plain with 256), whose 128-position tile reads
+// four A fragments per B fragment from LDS. They need channel blocks of at
+// least 64. Measured at 50% masks: N axis (128 channels) 2048^3 46 -> 39 us,
+// 4096^3 128 -> 119 us; dynamic depth (256 channels) 2048^3 54 -> 43 us, but
+// 4096^3 100 -> 127 us.
+int mn_token_tile(int M, int N, int G, int CW, bool swiglu) {
+  const long long t256 = (long long)(N / G) * (G / CW) * ((M + 255) / 256);
+  const int tp = swiglu ? 2 * CW : CW;
+  if (CW < 64) return 256;
+  return t256 < (tp >= 256 ? 256 : 1024) ? 128 : 256;
+}
+
+hipError_t launch_mn(MnKernel kernel, int CW, int TT, const uint16_t* A, const uint16_t* B,
                      const uint16_t* B2, const int32_t* perm, const int32_t* counts, int M, int K,
                      int N, int G, uint16_t* C, bool zero_inactive, hipStream_t stream) {
   const int ng = N / G;
   const int nct = G / CW;
-  const int ntok_tiles = (M + kTokTile - 1) / kTokTile;
+  const int ntok_tiles = (M + TT - 1) / TT;
   const long long total = (long long)ng * nct * ntok_tiles;
   const int per_xcd = (int)((total + 7) / 8);
   hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(512), 0, stream, A, B, B2, perm, counts, M, K,
@@ -281,25 +304,31 @@ hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint
                                const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
                                int G, uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  MnKernel k = G % 128 == 0  ? gate_up_bf16_kernel_128
-               : G % 64 == 0 ? gate_up_bf16_kernel_64
-               : G % 32 == 0 ? gate_up_bf16_kernel_32
-                             : gate_up_bf16_kernel_16;
   const int cw = G % 128 == 0 ? 128 : G % 64 == 0 ? 64 : G % 32 == 0 ? 32 : 16;
-  return launch_mn(k, cw, X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
+  const int tt = mn_token_tile(T, d_ff, G, cw, true);
+  MnKernel k = tt == 128 ? (cw == 128 ? gate_up_bf16_kernel_128_t128 : gate_up_bf16_kernel_64_t128)
+               : cw == 128 ? gate_up_bf16_kernel_128
+               : cw == 64  ? gate_up_bf16_kernel_64
+               : cw == 32  ? gate_up_bf16_kernel_32
+                           : gate_up_bf16_kernel_16;
+  return launch_mn(k, cw, tt, X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
 }
 
 hipError_t launch_gemm_mn_bf16(const uint16_t* A, const uint16_t* B, const int32_t* perm,
                                const int32_t* counts, int M, int K, int N, int G, uint16_t* C,
                                hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  MnKernel k = G % 256 == 0  ? gemm_mn_bf16_kernel_256
-               : G % 128 == 0 ? gemm_mn_bf16_kernel_128
-               : G % 64 == 0  ? gemm_mn_bf16_kernel_64
-               : G % 32 == 0  ? gemm_mn_bf16_kernel_32
-                              : gemm_mn_bf16_kernel_16;
   const int cw = G % 256 == 0 ? 256 : G % 128 == 0 ? 128 : G % 64 == 0 ? 64 : G % 32 == 0 ? 32 : 16;
-  return launch_mn(k, cw, A, B, nullptr, perm, counts, M, K, N, G, C, true, stream);
+  const int tt = mn_token_tile(M, N, G, cw, false);
+  MnKernel k = tt == 128 ? (cw == 256   ? gemm_mn_bf16_kernel_256_t128
+                            : cw == 128 ? gemm_mn_bf16_kernel_128_t128
+                                        : gemm_mn_bf16_kernel_64_t128)
+               : cw == 256 ? gemm_mn_bf16_kernel_256
+               : cw == 128 ? gemm_mn_bf16_kernel_128
+               : cw == 64  ? gemm_mn_bf16_kernel_64
+               : cw == 32  ? gemm_mn_bf16_kernel_32
+                           : gemm_mn_bf16_kernel_16;
+  return launch_mn(k, cw, tt, A, B, nullptr, perm, counts, M, K, N, G, C, true, stream);
 }
 
 }  // namespace wide
