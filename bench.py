@@ -845,6 +845,15 @@ def run_profile(steps: int):
     r = bench_prefill(torch, wide, dg, steps, 1, graph=False)
     del r["call"], r["dev_inputs"]
     torch.cuda.empty_cache()
+    # the Qwen3-14B-shaped prefill on its Zipf-skewed mask
+    qw = dg.QWEN14B_SKEW
+    qd = {k: v.to("cuda:0") for k, v in dg.make_inputs(qw).items()}
+    qc = wide.FfnCall(qd["X"], qd["Wg"], qd["Wu"], qd["Wd"], qd["mask"], qw.G)
+    for _ in range(PROFILE_QWEN_CALLS):
+        qc.run()
+    torch.cuda.synchronize()
+    del qc, qd
+    torch.cuda.empty_cache()
     for w in (dg.LLAMA8B_DECODE_T1, dg.LLAMA8B_DECODE_T16):
         calls, ws, _ = decode_setup(torch, wide, dg, w, 8)
         for _ in range(2):
@@ -900,6 +909,7 @@ def run_profile(steps: int):
 
 PROFILE_GEMM_CALLS = 3
 PROFILE_DECODE_CALLS = 16
+PROFILE_QWEN_CALLS = 5
 T16_PREPARED = "llama3.1-8b-ffn-decode-t16-operand-order-weights"
 PROFILE_ROUTER_T = (16384, 1)
 ROUTER_WORKLOADS = {16384: "llama3.1-8b-router-prefill", 1: "llama3.1-8b-router-decode-t1"}
@@ -917,6 +927,9 @@ def profile_plan(dg, steps: int):
     # the reorder stage is the mask-bit packing and the per-group partition
     plan = [(pre, "pack_mask_bits", n), (pre, "reorder_bits", n), (pre, "gate_up", n),
             (pre, "down", n)]
+    qw = dg.QWEN14B_SKEW.name
+    plan += [(qw, "pack_mask_bits", PROFILE_QWEN_CALLS), (qw, "reorder_bits", PROFILE_QWEN_CALLS),
+             (qw, "gate_up", PROFILE_QWEN_CALLS), (qw, "down", PROFILE_QWEN_CALLS)]
     # T = 1 takes the whole-row VALU GEMVs; T = 16 the MFMA gate/up and the
     # split-K down with its reduce
     t1, t16 = dg.LLAMA8B_DECODE_T1.name, dg.LLAMA8B_DECODE_T16.name
@@ -978,6 +991,10 @@ def work_closed_forms(dg):
     A = pre.T * (pre.ngroups // 2)  # top-50% masks: exactly ng/2 groups per token
     out = {(pre.name, "gate_up"): (4.0 * pre.d * pre.G * A, 4.0 * pre.d * pre.G * A),
            (pre.name, "down"): (2.0 * pre.d * pre.G * A, 2.0 * pre.T * pre.d * pre.d_ff)}
+    qw = dg.QWEN14B_SKEW
+    qa = int(dg.make_mask(qw).sum())
+    out[(qw.name, "gate_up")] = (4.0 * qw.d * qw.G * qa, 4.0 * qw.d * qw.G * qa)
+    out[(qw.name, "down")] = (2.0 * qw.d * qw.G * qa, 2.0 * qw.T * qw.d * qw.d_ff)
     for w in (dg.LLAMA8B_ATTN_Q, dg.LLAMA8B_ATTN_O, dg.LLAMA8B_DEPTH):
         a = int(dg.make_gemm_mask(w).sum())
         if w.axis == "mn":
@@ -1037,7 +1054,10 @@ def mfma_summary(directory, command, plan, split_fn):
              "each kernel's dispatches for the workload, times the flops of the kernel's MFMA",
              "instruction (32x32x16 bf16 = 32768, 16x16x32 bf16 = 16384). `algorithmic` is the",
              "method's work (active pairs only); `designed` is what the kernel is built to",
-             "execute (the down kernel runs the dense product; decode pads tokens to 16).", "",
+             "execute (the down kernel runs the dense product; decode pads tokens to 16).",
+             "The router's ratio is not 1: its second map runs v_mfma_f32_16x16x4_f32",
+             "(2048 flops), which the counter counts beside the 16x16x32 bf16 instructions of",
+             "the first map and this table prices at 16384.", "",
              "```", command.replace("PMC", "SQ_INSTS_MFMA"), "```", "",
              "| kernel | workload | counted TFLOP | algorithmic TFLOP | designed TFLOP | counted / designed |",
              "|---|---|---|---|---|---|"]

@@ -470,6 +470,8 @@ def test_sweep_cells_cover_every_g_and_sparsity():
     (700, 512, 2048, 128, 0.5), (1000, 320, 1536, 64, 0.3), (129, 256, 1024, 256, 0.7),
     (300, 576, 3072, 192, 0.5), (257, 256, 4096, 512, 0.5), (128, 256, 1024, 64, 1.0),
     (333, 256, 1024, 64, 0.05), (4096, 512, 2048, 128, 0.5), (300, 256, 257 * 64, 64, 0.5),
+    # partial 256 x 256 tiles in both dimensions
+    (2000, 4032, 1024, 128, 0.5),
 ])
 def test_down_ragged_tiles_and_idle_runs(T, d, d_ff, G, density):
     inp = dg.random_small(31 * T + G, T, d, d_ff, G, "bf16", density, wscale=0.05)
