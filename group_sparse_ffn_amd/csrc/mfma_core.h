@@ -13,7 +13,11 @@
 //     the 16 lanes that read one MFMA fragment row-group on distinct banks;
 //   * fragments are read one MFMA k-step ahead of their use, and the barrier
 //     sits before the last k-step of a stage so the fragments of the next
-//     stage are read while the last MFMAs of this one run;
+//     stage are read while the last MFMAs of this one run. The P fragments of
+//     the next k-step are read in one burst at the start of a k-step (two
+//     register sets); each Q fragment is read again right after its last
+//     MFMA of the current k-step (one set), which spreads the LDS reads over
+//     the k-step (dense probe: 2-5% faster than reading both in one burst);
 //   * v_mfma_f32_32x32x16_bf16, fp32 accumulation in registers.
 //
 // Output fragment layout (per wave, fragment (i, j)): lane l holds Q row
@@ -60,7 +64,7 @@ template <class S>
 struct Frags {
   f32x16 acc[S::FP][S::FQ];
   bf16x8 fa[2][S::FP];
-  bf16x8 fb[2][S::FQ];
+  bf16x8 fb[S::FQ];
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -71,27 +75,34 @@ struct Frags {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   }
 
-  // Fragments of MFMA k-step kk (0..3) of the stage held at `stage`.
-  __device__ __forceinline__ void load(const uint8_t* stage, int kk, int set, int pbase, int qbase,
-                                       int sw, int lhalf) {
+  // P fragments of MFMA k-step kk (0..3) of the stage held at `stage`, into `set`.
+  __device__ __forceinline__ void load_p(const uint8_t* stage, int kk, int set, int pbase, int sw,
+                                         int lhalf) {
     const int off = ((kk * 2 + lhalf) ^ sw) << 4;
 #pragma unroll
     for (int i = 0; i < S::FP; ++i)
       fa[set][i] = *(const bf16x8*)(stage + pbase + i * 32 * kRowBytes + off);
-#pragma unroll
-    for (int j = 0; j < S::FQ; ++j)
-      fb[set][j] = *(const bf16x8*)(stage + S::PBYTES + qbase + j * 32 * kRowBytes + off);
   }
 
-  // MFMAs of one k-step; Q fragments j >= nq are skipped (their rows are inactive).
-  __device__ __forceinline__ void mma(int set, int nq) {
+  // Q fragment j of MFMA k-step kk of the stage held at `stage`.
+  __device__ __forceinline__ void load_q(const uint8_t* stage, int kk, int j, int qbase, int sw,
+                                         int lhalf) {
+    const int off = ((kk * 2 + lhalf) ^ sw) << 4;
+    fb[j] = *(const bf16x8*)(stage + S::PBYTES + qbase + j * 32 * kRowBytes + off);
+  }
+
+  // MFMAs of one k-step with P set `set`; Q fragments j >= nq are skipped
+  // (their rows are inactive). When `next` is set, Q fragment j of k-step nkk
+  // of the stage at `next` is read right after its last MFMA here.
+  __device__ __forceinline__ void step(int set, int nq, const uint8_t* next, int nkk, int qbase,
+                                       int sw, int lhalf) {
 #pragma unroll
     for (int j = 0; j < S::FQ; ++j) {
       if (j < nq) {
 #pragma unroll
         for (int i = 0; i < S::FP; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0,
-                                                              0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[j], acc[i][j], 0, 0, 0);
+        if (next != nullptr) load_q(next, nkk, j, qbase, sw, lhalf);
       }
     }
   }
@@ -123,7 +134,10 @@ __device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, 
   }
   __builtin_amdgcn_s_waitcnt(WIDE_VMCNT(0));
   __syncthreads();
-  f.load(sA, 0, 0, pbase, qbase, sw, lhalf);
+  f.load_p(sA, 0, 0, pbase, sw, lhalf);
+#pragma unroll
+  for (int j = 0; j < S::FQ; ++j)
+    if (j < nq) f.load_q(sA, 0, j, qbase, sw, lhalf);
   for (int s = 0; s < nst; ++s) {
     uint8_t* cur = (s & 1) ? sB : sA;
     uint8_t* nxt = (s & 1) ? sA : sB;
@@ -131,9 +145,9 @@ __device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, 
     for (int kk = 0; kk < 4; ++kk) {
       const int set = kk & 1;
       if (kk < 3) {
-        f.load(cur, kk + 1, set ^ 1, pbase, qbase, sw, lhalf);
+        f.load_p(cur, kk + 1, set ^ 1, pbase, sw, lhalf);
         if (kk == 0 && s + 2 < nst) prepare(s + 2);
-        f.mma(set, nq);
+        f.step(set, nq, cur, kk + 1, qbase, sw, lhalf);
       } else {
         // stage s+1 must have landed (each wave waits for its own copies)
         // and be visible to all waves; after the barrier every wave has read
@@ -143,8 +157,9 @@ __device__ __forceinline__ void mainloop(Frags<S>& f, uint8_t* sA, uint8_t* sB, 
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         if (s + 2 < nst) issue(s + 2, cur);
-        if (s + 1 < nst) f.load(nxt, 0, set ^ 1, pbase, qbase, sw, lhalf);
-        f.mma(set, nq);
+        const bool more = s + 1 < nst;
+        if (more) f.load_p(nxt, 0, set ^ 1, pbase, sw, lhalf);
+        f.step(set, nq, more ? nxt : nullptr, 0, qbase, sw, lhalf);
       }
     }
   }
