@@ -93,32 +93,17 @@ __device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
 
-// Lists the groups (or 32-channel chunks) executed by some token into s_list
-// (ascending) and returns their number. Every thread of the block must call
-// it. `nitems` items; item i covers groups [glo(i), ghi(i)]; 1 <= T <= kMaxT.
-template <int kThreads, int kMaxT, class Range>
-__device__ __forceinline__ int list_active(const uint8_t* __restrict__ mask, int T, int ng,
-                                           int nitems, Range range, uint16_t* s_list,
-                                           int* s_wave_cnt) {
+// Lists the items i < nitems with pred(i) into s_list (ascending) and returns
+// their number. Every thread of the block must call it.
+template <int kThreads, class Pred>
+__device__ __forceinline__ int list_where(int nitems, Pred pred, uint16_t* s_list,
+                                          int* s_wave_cnt) {
   constexpr int kWaves = kThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n = 0;
   for (int b0 = 0; b0 < nitems; b0 += kThreads) {
     const int it = b0 + tid;
-    bool any = false;
-    if (it < nitems) {
-      int glo, ghi;
-      range(it, glo, ghi);
-      // all mask bytes are requested before any is tested: token rows past
-      // T - 1 are clamped to T - 1 (T >= 1), which leaves the OR unchanged and
-      // keeps the loads out of branches
-      for (int g = glo; g <= ghi; ++g) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int t = 0; t < kMaxT; ++t) m |= mask[(size_t)min(t, T - 1) * ng + g];
-        any |= m != 0;
-      }
-    }
+    const bool any = it < nitems && pred(it);
     const uint64_t bal = __ballot(any);
     if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
     __syncthreads();
@@ -133,6 +118,44 @@ __device__ __forceinline__ int list_active(const uint8_t* __restrict__ mask, int
     __syncthreads();
   }
   return n;
+}
+
+// Whether some token executes group g. All mask bytes are requested before
+// any is tested: token rows past T - 1 are clamped to T - 1 (T >= 1), which
+// leaves the OR unchanged and keeps the loads out of branches.
+template <int kMaxT>
+__device__ __forceinline__ bool group_live(const uint8_t* __restrict__ mask, int T, int ng, int g) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t) m |= mask[(size_t)min(t, T - 1) * ng + g];
+  return m != 0;
+}
+
+// Lists the groups executed by some token (1 <= T <= kMaxT) into s_list.
+template <int kThreads, int kMaxT>
+__device__ __forceinline__ int list_active(const uint8_t* __restrict__ mask, int T, int ng,
+                                           uint16_t* s_list, int* s_wave_cnt) {
+  return list_where<kThreads>(
+      ng, [&](int g) { return group_live<kMaxT>(mask, T, ng, g); }, s_list, s_wave_cnt);
+}
+
+// Flags the groups executed by some token into s_gact[0, ng) and lists the
+// 32-channel chunks that hold at least one of them into s_list (one pass
+// over the mask; the chunk test reads the flags in LDS).
+template <int kThreads, int kMaxT>
+__device__ __forceinline__ int list_active_chunks(const uint8_t* __restrict__ mask, int T, int ng,
+                                                  int G, int nchunks, uint8_t* s_gact,
+                                                  uint16_t* s_list, int* s_wave_cnt) {
+  for (int g = threadIdx.x; g < ng; g += kThreads) s_gact[g] = group_live<kMaxT>(mask, T, ng, g);
+  __syncthreads();
+  return list_where<kThreads>(
+      nchunks,
+      [&](int c) {
+        bool any = false;
+        for (int g = (c * 32) / G; g <= (c * 32 + 31) / G; ++g) any |= s_gact[g] != 0;
+        return any;
+      },
+      s_list, s_wave_cnt);
 }
 
 constexpr int kGuThreads = 256;
@@ -164,8 +187,7 @@ __device__ __forceinline__ void gate_up_unit(const uint16_t* __restrict__ X,
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int nact = list_active<kGuThreads, 16>(
-      mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
+  const int nact = list_active<kGuThreads, 16>(mask, T, ng, s_groups, s_wave_cnt);
   const int u = blockIdx.x;
   if (u >= nact * upg) {
     // Past the active units: when H must hold exact zeros, the units of the
@@ -364,8 +386,7 @@ __global__ __launch_bounds__(kXThreads) void decode_gate_up_xlds_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int nact = list_active<kXThreads, 16>(
-      mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
+  const int nact = list_active<kXThreads, 16>(mask, T, ng, s_groups, s_wave_cnt);
   const int u = 2 * (int)blockIdx.x + (wave >> 2);  // this wave's unit
   const int quarter = wave & 3;
   const bool active = u < nact * upg;
@@ -559,23 +580,9 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // 32-channel chunks whose group some token executes
-  const int nch = list_active<kSkThreads, 16>(
-      mask, T, ng, d_ff / 32,
-      [G](int c, int& lo, int& hi) {
-        lo = (c * 32) / G;
-        hi = (c * 32 + 31) / G;
-      },
-      s_chunks, s_wave_cnt);
-  if (PIECES) {
-    for (int g = tid; g < ng; g += kSkThreads) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) m |= mask[(size_t)min(t, T - 1) * ng + g];
-      s_gact[g] = m != 0;
-    }
-    __syncthreads();
-  }
+  // groups some token executes (s_gact) and the 32-channel chunks that hold one
+  const int nch =
+      list_active_chunks<kSkThreads, 16>(mask, T, ng, G, d_ff / 32, s_gact, s_chunks, s_wave_cnt);
   const int lo = (split * nch) / kDecodeDownSplit;
   const int hi = ((split + 1) * nch) / kDecodeDownSplit;
 
@@ -710,8 +717,7 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
   constexpr int kJ = 8;  // 1 KB loads per row and k-block (4096 channels)
   const int ng = d_ff / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nact = list_active<kValuThreads, NT>(
-      mask, T, ng, ng, [](int i, int& lo, int& hi) { lo = hi = i; }, s_groups, s_wave_cnt);
+  const int nact = list_active<kValuThreads, NT>(mask, T, ng, s_groups, s_wave_cnt);
   const int nj = d / 512;
   const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
   const int nitems = nact * G;
@@ -802,17 +808,12 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
                                           const uint16_t* __restrict__ Wd,
                                           const uint8_t* __restrict__ mask, int T, int d, int d_ff,
                                           int G, uint16_t* __restrict__ Y, uint16_t* s_chunks,
-                                          int* s_wave_cnt, uint16_t* s_h) {
+                                          uint8_t* s_gact, int* s_wave_cnt, uint16_t* s_h) {
   constexpr int kBatch = 16;  // loads in flight per lane (a whole row of 256 live chunks)
   const int ng = d_ff / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = list_active<kValuThreads, NT>(
-      mask, T, ng, d_ff / 32,
-      [G](int c, int& lo, int& hi) {
-        lo = (c * 32) / G;
-        hi = (c * 32 + 31) / G;
-      },
-      s_chunks, s_wave_cnt);
+  const int nch = list_active_chunks<kValuThreads, NT>(mask, T, ng, G, d_ff / 32, s_gact, s_chunks,
+                                                      s_wave_cnt);
   const int stride = nch * 32;  // compacted channels per token
   const int ninstr = (nch + 15) / 16;
   const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
@@ -836,10 +837,7 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
     const int t = e / (nch * 4), r = e % (nch * 4);
     const int j = r >> 2, q = r & 3;
     const int ch = (int)s_chunks[j] * 32 + 8 * q;
-    const int g = ch / G;
-    bool live = false;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) live |= mask[(size_t)min(tt, T - 1) * ng + g] != 0;
+    const bool live = s_gact[ch / G] != 0;
     const u32x4 z = {0u, 0u, 0u, 0u};
     // an H fragment of a group no token executes may be unwritten: it is
     // loaded (in bounds) and replaced by zeros, never summed
@@ -889,9 +887,10 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
       const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G,                          \
       uint16_t* __restrict__ Y) {                                                               \
     __shared__ uint16_t s_chunks[valu_cap(NT) / 32];                                            \
+    __shared__ uint8_t s_gact[valu_cap(NT) / 16];                                               \
     __shared__ int s_wave_cnt[kValuWaves];                                                      \
     __shared__ __attribute__((aligned(16))) uint16_t s_h[NT * valu_cap(NT)];                    \
-    down_valu<NT>(H, Wd, mask, T, d, d_ff, G, Y, s_chunks, s_wave_cnt, s_h);                   \
+    down_valu<NT>(H, Wd, mask, T, d, d_ff, G, Y, s_chunks, s_gact, s_wave_cnt, s_h);           \
   }
 WIDE_DECODE_VALU_KERNELS(1)
 WIDE_DECODE_VALU_KERNELS(2)

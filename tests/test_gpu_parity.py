@@ -193,6 +193,9 @@ def test_decode_path_vs_oracle(T, G):
     # G = 48: a 32-channel chunk can hold an executed and a skipped group at any
     # offset, not only at its halves (matrix-core GEMVs at both T)
     (5, 512, 1536, 48), (1, 576, 1536, 48), (16, 512, 1536, 48), (3, 256, 960, 80),
+    # past the reach of the gate/up with the activations in LDS, the
+    # global-fragment kernel: T * d above the LDS capacity, d not a multiple of 128
+    (16, 4224, 1024, 64), (8, 576, 1024, 64),
 ])
 def test_decode_never_reads_unwritten_h(T, d, d_ff, G):
     inp = dg.random_small(500 + T + G, T, d, d_ff, G, "bf16", 0.3, wscale=0.05)
