@@ -19,6 +19,16 @@
 //            touching memory;
 //   level 2: 32-row MFMA fragments that lie wholly past the count are not
 //            multiplied.
+// Tile order. A tile is (channel block, token tile); a group's tiles are
+// full (TT active positions), at most one boundary tile (fewer), and tiles
+// past its count (only zeros to write, and only with zero_inactive). Every
+// workgroup scans the active counts and takes, on its XCD (workgroup ids go
+// to the XCDs in turn), first an eighth of all full tiles in group-major
+// order (the tiles that run at the same time on one XCD share their weight
+// rows in its L2), then an eighth of the boundary tiles, then an eighth of
+// the tiles past the counts. The last round of the grid is then filled by
+// the short boundary tiles, workgroups with no work are dispatched after all
+// of the real ones, and skewed counts spread evenly over the XCDs.
 // The epilogue rounds once to bf16 (RNE), stages the tile through LDS and
 // scatters 16-byte row segments to C[row, channels]. With zero_inactive,
 // every (row, channel) of the group that the row skips is also written as
@@ -55,6 +65,86 @@ struct MnShape {
   static_assert(2 * STG_ROWS >= TT, "epilogue staging fits the two stages");
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
+// each 16-lane row, then the row totals carried by row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// This workgroup's tile in the order above (blk, tile index and the group's
+// active count), or false when it has none. Every wave computes it on its
+// own, with no barrier: lane l scans a contiguous run of blocks, the run that
+// holds the wanted index is found by a ballot, and its lane's answer is read
+// by every lane.
+template <int TT>
+__device__ __forceinline__ bool ordered_tile(const int32_t* __restrict__ counts, int nblk, int nct,
+                                             int ntok_tiles, bool with_zero, int& blk, int& tile,
+                                             int& count) {
+  const int lane = (int)(threadIdx.x & 63);
+  const int per = (nblk + 63) / 64;
+  const int b0 = lane * per;
+  int sf = 0, sb = 0, sz = 0;
+  for (int k = 0; k < per && b0 + k < nblk; ++k) {
+    const int c = counts[(b0 + k) / nct];
+    const int f = c / TT, b = c % TT != 0;
+    sf += f;
+    sb += b;
+    sz += ntok_tiles - f - b;
+  }
+  const int pf = wave_incl_scan(sf), pb = wave_incl_scan(sb), pz = wave_incl_scan(sz);
+  const int F = __builtin_amdgcn_readlane(pf, 63);
+  const int B = __builtin_amdgcn_readlane(pb, 63);
+  const int Z = __builtin_amdgcn_readlane(pz, 63);
+  const int x = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+  const int fx = (F + 7) / 8, bx = (B + 7) / 8, zx = (Z + 7) / 8;
+  const int nf = min(max(F - x * fx, 0), fx);
+  const int nb = min(max(B - x * bx, 0), bx);
+  const int nz = with_zero ? min(max(Z - x * zx, 0), zx) : 0;
+  int cls, i;
+  if (j < nf) {
+    cls = 0;
+    i = x * fx + j;
+  } else if (j < nf + nb) {
+    cls = 1;
+    i = x * bx + (j - nf);
+  } else if (j < nf + nb + nz) {
+    cls = 2;
+    i = x * zx + (j - nf - nb);
+  } else {
+    return false;
+  }
+  const int mine = cls == 0 ? sf : cls == 1 ? sb : sz;
+  int acc = (cls == 0 ? pf : cls == 1 ? pb : pz) - mine;  // tiles of the class before this run
+  const uint64_t own = __ballot(i >= acc && i < acc + mine);
+  if (own == 0) return false;  // (never: the runs cover the class)
+  const int owner = (int)__builtin_ctzll(own);
+  int rb = 0, rt = 0, rc = 0;
+  if (lane == owner) {
+    for (int k = 0; k < per && b0 + k < nblk; ++k) {
+      const int c = counts[(b0 + k) / nct];
+      const int f = c / TT, b = c % TT != 0;
+      const int n = cls == 0 ? f : cls == 1 ? b : ntok_tiles - f - b;
+      if (i < acc + n) {
+        rb = b0 + k;
+        rt = cls == 0 ? i - acc : cls == 1 ? f : f + b + (i - acc);
+        rc = c;
+        break;
+      }
+      acc += n;
+    }
+  }
+  blk = __builtin_amdgcn_readlane(rb, owner);
+  tile = __builtin_amdgcn_readlane(rt, owner);
+  count = __builtin_amdgcn_readlane(rc, owner);
+  return true;
+}
+
 // The body is a device function template called from one plain kernel per
 // (channel width, epilogue): a kernel template that passes a local lambda to
 // the mainloop loses its host launch stub with this toolchain.
@@ -71,17 +161,13 @@ __device__ __forceinline__ void mn_body(
   using S = typename SH::S;
   constexpr int kTokTile = TT;
 
-  // XCD-aware order: consecutive workgroup ids go to different XCDs, so give
-  // each XCD a contiguous range of (channel block, token tile) pairs; the
-  // tiles of one channel block then share their weight rows in one L2.
-  const int per_xcd = (total + 7) / 8;
-  const int L = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (L >= total) return;
-  const int blk = L / ntok_tiles;
-  const int tile0 = (L % ntok_tiles) * kTokTile;
+  int blk, tile, count;
+  if (!ordered_tile<TT>(counts, total / ntok_tiles, nct, ntok_tiles, zero_inactive != 0, blk, tile,
+                        count))
+    return;
+  const int tile0 = tile * kTokTile;
   const int g = blk / nct;
   const int ct = blk % nct;
-  const int count = counts[g];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -292,7 +378,8 @@ hipError_t launch_mn(MnKernel kernel, int CW, int TT, const uint16_t* A, const u
   const int nct = G / CW;
   const int ntok_tiles = (M + TT - 1) / TT;
   const long long total = (long long)ng * nct * ntok_tiles;
-  const int per_xcd = (int)((total + 7) / 8);
+  // per XCD at most an eighth (rounded up) of each of the three tile classes
+  const int per_xcd = (int)((total + 7) / 8) + 2;
   hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(512), 0, stream, A, B, B2, perm, counts, M, K,
                      N, G, C, zero_inactive ? 1 : 0, ntok_tiles, nct, (int)total);
   return hipGetLastError();
