@@ -123,11 +123,54 @@ hipError_t launch_gemm_mn_bf16(const uint16_t* A, const uint16_t* B, const int32
                                const int32_t* counts, int M, int K, int N, int G, uint16_t* C,
                                hipStream_t stream);
 
+// Tile edge of the prefill down projection: 256 x 256 tiles unless fewer
+// than 128 of them would leave most of the 256 CUs idle; then 128 x 128
+// tiles run four times as many workgroups. Measured at 50% masks: 2048^3
+// 60 -> 41 us with 128-tiles (64 large tiles), but 4096^3 127 -> 183 us (256
+// large tiles) and 384 / 320 large tiles (Llama3.2-3B T = 8192, Qwen3-14B
+// T = 4096) slower by 0.1 ms.
+inline int down_tile(int T, int d) {
+  const long long t256 = (((long long)T + 255) / 256) * (((long long)d + 255) / 256);
+  return t256 < 128 ? 128 : 256;
+}
+
+// The last round of 256 x 256 down tiles: with nt tiles on kDownRoundCUs CUs
+// the nrem = nt % kDownRoundCUs tiles of the last round are split nsplit
+// ways along their live K-blocks (nsplit = 1: no split). A function of the
+// shape only (the CU count of MI355X is a constant here), so the workspace
+// size and the launch always agree.
+constexpr int kDownRoundCUs = 256;
+constexpr int kDownMaxSplit = 8;
+struct DownSplit {
+  int nrem, nsplit;
+};
+inline DownSplit down_split(int T, int d, int d_ff) {
+  DownSplit ds{0, 1};
+  if (T <= 0 || down_tile(T, d) != 256) return ds;
+  const long long nt = (((long long)T + 255) / 256) * (((long long)d + 255) / 256);
+  const int rem = (int)(nt % kDownRoundCUs);
+  if (rem == 0) return ds;
+  int s = kDownRoundCUs / rem;
+  if (s > kDownMaxSplit) s = kDownMaxSplit;
+  if (s > (d_ff / 64) / 8) s = (d_ff / 64) / 8;  // at least 8 K-blocks of 64 channels per part
+  if (s < 2) return ds;
+  ds.nrem = rem;
+  ds.nsplit = s;
+  return ds;
+}
+// bytes of the fp32 partial sums of the split tiles (0 without a split)
+inline size_t down_split_bytes(int T, int d, int d_ff) {
+  const DownSplit ds = down_split(T, d, d_ff);
+  return ds.nsplit > 1 ? (size_t)ds.nrem * ds.nsplit * 256 * 256 * 4 : 0;
+}
+
 // bf16 prefill down projection, also the K-axis masked GEMM (output-stationary;
 // K-blocks inactive for a whole token tile are skipped and the H copies of
 // inactive (token, group) pairs read zeros, so H's values there never matter).
+// part: down_split_bytes(T, d, d_ff) bytes of workspace for the split
+// last-round tiles, or NULL (no split).
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
-                            int d, int d_ff, int G, uint16_t* Y, hipStream_t stream);
+                            int d, int d_ff, int G, uint16_t* Y, float* part, hipStream_t stream);
 
 // Operand-order copy of a bf16 [rows, cols] matrix (rows % 16 == 0, cols % 32
 // == 0): each 16-row x 32-column MFMA operand becomes one contiguous 1 KB

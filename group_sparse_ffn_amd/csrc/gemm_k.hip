@@ -23,6 +23,13 @@
 //     workgroup; with more than kDownMaxGroups groups the table does not fit
 //     and each lane reads its mask words from global memory instead, one
 //     stage ahead, so the stage's own wait covers those loads too.
+// Last round. With 256 x 256 tiles the grid is whole rounds of one tile per
+// CU plus a remainder of r tiles (Qwen3-14B T = 4096: 320 tiles = 256 + 64);
+// given a partial-sum buffer, the r remainder tiles are each split into
+// s = 256 / r parts along their list of live K-blocks, so the last round has
+// a CU for every part, each a 1/s of a tile. The parts write fp32 partial
+// sums in their accumulator layout (1 KB coalesced stores) and a second
+// kernel adds the s parts in order and rounds once to bf16.
 // The same kernel is the K-axis masked GEMM C = (mask-expanded A) . B^T.
 // Operands: MFMA A side = Wdown rows (output columns), B side = H rows
 // (tokens); the shared 8-wave mainloop streams both through LDS with
@@ -57,17 +64,28 @@ template <int kTile>
 __device__ __forceinline__ void down_body(
     const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,
     const uint32_t* __restrict__ maskbits, int T, int d, int d_ff, int G, uint16_t* __restrict__ Y,
-    int ntt, int nnt, int words, uint8_t* sA, uint8_t* sB, uint16_t* s_steps, uint32_t* s_mw,
-    int* s_wave_cnt) {
+    int ntt, int nnt, int words, float* __restrict__ part, int nrem, int nsplit, uint8_t* sA,
+    uint8_t* sB, uint16_t* s_steps, uint32_t* s_mw, int* s_wave_cnt) {
   using SH = DownShape<kTile>;
   using DS = typename SH::DS;
   constexpr int kCB = SH::kCB;
   constexpr int kW = SH::kWords;
 
-  const int total = ntt * nnt;
-  const int per_xcd = (total + 7) / 8;
-  const int L = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (L >= total) return;
+  // whole tiles first (XCD-aware: each XCD a contiguous range), then the
+  // nsplit parts of each of the last nrem tiles
+  const int nfull = ntt * nnt - nrem;
+  const int per_xcd = (nfull + 7) / 8;
+  int L, spart = 0;
+  if ((int)blockIdx.x < 8 * per_xcd) {
+    L = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (L >= nfull) return;
+  } else {
+    const int u = (int)blockIdx.x - 8 * per_xcd;
+    if (u >= nrem * nsplit) return;
+    L = nfull + u / nsplit;
+    spart = u % nsplit;
+  }
+  const bool split = L >= nfull;
   const int t0 = (L / nnt) * kTile;
   const int n0 = (L % nnt) * kTile;
   const int tid = threadIdx.x;
@@ -137,6 +155,11 @@ __device__ __forceinline__ void down_body(
     __syncthreads();
   }
 
+  // a part of a split tile runs its share of the live K-blocks
+  const int kb0 = split ? (spart * nst) / nsplit : 0;
+  if (split) nst = ((spart + 1) * nst) / nsplit - kb0;
+  const uint16_t* steps = s_steps + kb0;
+
   // Copies: only waves 0..kCopyWaves-1 issue them, so each SIMD runs one
   // copying and one MFMA-only wave, and the MFMA-only wave keeps the matrix
   // core busy while the other waits to issue its copies. Copying wave w
@@ -168,7 +191,7 @@ __device__ __forceinline__ void down_body(
   // index is clamped, so no load sits in a branch).
   uint32_t mwv[kCB];
   auto fetch = [&](int s) {
-    const int k0 = (int)s_steps[s] * 64;
+    const int k0 = (int)steps[s] * 64;
     const uint32_t* mw = maskbits + (size_t)((k0 + chunk * 8) / G) * words;
 #pragma unroll
     for (int i = 0; i < kCB; ++i)
@@ -178,7 +201,7 @@ __device__ __forceinline__ void down_body(
     if (!copier) return;
     const uint32_t sh = rw & 31;
     if (table) {
-      const int k0 = (int)s_steps[s] * 64;
+      const int k0 = (int)steps[s] * 64;
       const uint32_t* mw = s_mw + ((k0 + chunk * 8) / G) * kW;  // this lane's group
 #pragma unroll
       for (int i = 0; i < kCB; ++i)
@@ -193,7 +216,7 @@ __device__ __forceinline__ void down_body(
   if (copier && !table && nst > 0) fetch(0);
   auto issue = [&](int s, uint8_t* stage) {
     if (!copier) return;
-    const int k0 = (int)s_steps[s] * 64;
+    const int k0 = (int)steps[s] * 64;
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Wd + k0), 0, (int)(w_bytes - 2u * k0), 0x00020000);
     const __amdgpu_buffer_rsrc_t hr =
@@ -211,6 +234,21 @@ __device__ __forceinline__ void down_body(
   const int wq = wave % DS::WQ;
   core::Frags<DS> f;
   core::mainloop<DS>(f, sA, sB, nst, wp, wq, lane, DS::FQ, issue, prepare);
+  if (split) {
+    // fp32 partial sums in accumulator order: [wave][i][j][q][lane] f32x4
+    float* out = part + ((size_t)(L - nfull) * nsplit + spart) * (kTile * kTile);
+#pragma unroll
+    for (int i = 0; i < DS::FP; ++i)
+#pragma unroll
+      for (int j = 0; j < DS::FQ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {f.acc[i][j][4 * q], f.acc[i][j][4 * q + 1], f.acc[i][j][4 * q + 2],
+                           f.acc[i][j][4 * q + 3]};
+          *(f32x4*)(out + ((((size_t)wave * DS::FP + i) * DS::FQ + j) * 4 + q) * 256 + 4 * lane) = v;
+        }
+    return;
+  }
   __syncthreads();  // every wave is done with the stages: reuse them for the epilogue
 
   // Epilogue: staged as [kTile tokens][kTile columns] bf16 (kTile * 2-byte
@@ -254,43 +292,67 @@ __device__ __forceinline__ void down_body(
   __global__ __launch_bounds__(512, 1) void NAME(                                             \
       const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,                        \
       const uint32_t* __restrict__ maskbits, int T, int d, int d_ff, int G,                   \
-      uint16_t* __restrict__ Y, int ntt, int nnt, int words) {                                \
+      uint16_t* __restrict__ Y, int ntt, int nnt, int words, float* __restrict__ part,        \
+      int nrem, int nsplit) {                                                                 \
     using DSx = DownShape<TILE>::DS;                                                          \
     __shared__ __attribute__((aligned(1024))) uint8_t sA[DSx::STAGE];                         \
     __shared__ __attribute__((aligned(1024))) uint8_t sB[DSx::STAGE];                         \
     __shared__ uint16_t s_steps[kMaxSteps];                                                   \
     __shared__ __attribute__((aligned(16))) uint32_t s_mw[kDownMaxGroups * (TILE / 32)];     \
     __shared__ int s_wave_cnt[8];                                                             \
-    down_body<TILE>(H, Wd, maskbits, T, d, d_ff, G, Y, ntt, nnt, words, sA, sB, s_steps,      \
-                    s_mw, s_wave_cnt);                                                        \
+    down_body<TILE>(H, Wd, maskbits, T, d, d_ff, G, Y, ntt, nnt, words, part, nrem, nsplit,   \
+                    sA, sB, s_steps, s_mw, s_wave_cnt);                                       \
   }
 WIDE_DOWN_KERNEL(down_bf16_kernel, 256)
 WIDE_DOWN_KERNEL(down_bf16_kernel_t128, 128)
 #undef WIDE_DOWN_KERNEL
 
-}  // namespace
-
-int down_tile(int T, int d) {
-  // 256 x 256 tiles unless fewer than 128 of them would leave most of the 256
-  // CUs idle; then 128 x 128 tiles run four times as many workgroups. Measured
-  // at 50% masks: 2048^3 60 -> 41 us with 128-tiles (64 large tiles), but
-  // 4096^3 127 -> 183 us (256 large tiles) and 384 / 320 large tiles
-  // (Llama3.2-3B T = 8192, Qwen3-14B T = 4096) slower by 0.1 ms
-  const long long t256 = (long long)((T + 255) / 256) * ((d + 255) / 256);
-  return t256 < 128 ? 128 : 256;
+// Y of the split tiles: the nsplit parts' partial sums added in order, one
+// rounding to bf16. Thread e handles f32x4 e of the accumulator layout of
+// 256 x 256 tiles (8 waves x 4 x 2 fragments x 4 quads x 64 lanes).
+__global__ __launch_bounds__(256) void down_split_reduce_kernel(
+    const float* __restrict__ part, int nfull, int nrem, int nsplit, int nnt, int T, int d,
+    uint16_t* __restrict__ Y) {
+  using DS = DownShape<256>::DS;
+  constexpr int kPer = 256 * 256 / 4;  // f32x4 per tile
+  const int e = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (e >= nrem * kPer) return;
+  const int q = e / kPer, w = e % kPer;
+  const int lane = w & 63, qd = (w >> 6) & 3, j = (w >> 8) % DS::FQ,
+            i = (w >> 8) / DS::FQ % DS::FP, wave = (w >> 8) / (DS::FQ * DS::FP);
+  const int wp = wave / DS::WQ, wq = wave % DS::WQ;
+  const int r = wq * DS::QW + j * 32 + (lane & 31);                   // token in the tile
+  const int n = wp * DS::PW + i * 32 + 8 * qd + 4 * (lane >> 5);      // first of 4 columns
+  const int L = nfull + q;
+  const int t = (L / nnt) * 256 + r, c = (L % nnt) * 256 + n;
+  if (t >= T || c >= d) return;
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) y += *(const f32x4*)(part + ((size_t)q * nsplit + sp) * (4 * kPer) + 4 * w);
+  const u32x2 v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  *(u32x2*)(Y + (size_t)t * d + c) = v;
 }
 
+}  // namespace
+
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
-                            int d, int d_ff, int G, uint16_t* Y, hipStream_t stream) {
+                            int d, int d_ff, int G, uint16_t* Y, float* part, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int tile = down_tile(T, d);
   const int ntt = (T + tile - 1) / tile;
   const int nnt = (d + tile - 1) / tile;
   const int words = (T + 31) / 32;
-  const int total = ntt * nnt;
-  const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(tile == 256 ? down_bf16_kernel : down_bf16_kernel_t128, dim3(per_xcd * 8),
-                     dim3(512), 0, stream, H, Wd, maskbits, T, d, d_ff, G, Y, ntt, nnt, words);
+  const DownSplit ds = part != nullptr ? down_split(T, d, d_ff) : DownSplit{0, 1};
+  const int nrem = ds.nsplit > 1 ? ds.nrem : 0;
+  const int nfull = ntt * nnt - nrem;
+  const int grid = (nfull + 7) / 8 * 8 + nrem * ds.nsplit;
+  hipLaunchKernelGGL(tile == 256 ? down_bf16_kernel : down_bf16_kernel_t128, dim3(grid), dim3(512),
+                     0, stream, H, Wd, maskbits, T, d, d_ff, G, Y, ntt, nnt, words, part, nrem,
+                     ds.nsplit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nrem == 0) return e;
+  const int n4 = nrem * (256 * 256 / 4);
+  hipLaunchKernelGGL(down_split_reduce_kernel, dim3((n4 + 255) / 256), dim3(256), 0, stream, part,
+                     nfull, nrem, ds.nsplit, nnt, T, d, Y);
   return hipGetLastError();
 }
 

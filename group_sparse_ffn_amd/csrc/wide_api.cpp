@@ -63,10 +63,12 @@ size_t elt_size(int32_t dt) { return dt == WIDE_BF16 ? 2 : 4; }
 //   maskbits uint32 [ngroups, ceil(T/32)]
 //   part     fp32   [kDecodeDownSplit, T, d]   (T <= WIDE_DECODE_T_LIMIT only:
 //                   the decode down GEMV's partial sums)
+//   dpart    fp32   down_split_bytes(T, d, d_ff) (the prefill down
+//                   projection's split last-round tiles; often empty)
 //   H        dtype  [T, d_ff]   (only when the caller passes no H_out; last, so
 //                   the other offsets do not depend on it)
 struct Layout {
-  size_t perm, counts, padded, maskbits, h, part, total;
+  size_t perm, counts, padded, maskbits, h, part, dpart, total;
 };
 
 Layout layout(int64_t T, int64_t d, int64_t d_ff, int64_t G, int32_t dt, bool with_h) {
@@ -84,6 +86,8 @@ Layout layout(int64_t T, int64_t d, int64_t d_ff, int64_t G, int32_t dt, bool wi
   off = round_up(off + (size_t)(ng * words) * 4, 256);
   L.part = off;
   if (T <= WIDE_DECODE_T_LIMIT) off = round_up(off + (size_t)(wide::kDecodeDownSplit * T * d) * 4, 256);
+  L.dpart = off;
+  off = round_up(off + wide::down_split_bytes((int)T, (int)d, (int)d_ff), 256);
   L.h = off;
   if (with_h) off = round_up(off + (size_t)(T * d_ff) * elt_size(dt), 256);
   L.total = off;
@@ -215,7 +219,8 @@ wide_status_t run_stage(int32_t stage, const Args& a) {
     case WIDE_STAGE_DOWN:
       if (a.dt == WIDE_BF16)
         e = wide::launch_down_bf16((const uint16_t*)H, (const uint16_t*)a.Wd, maskbits, a.T, a.d,
-                                   a.d_ff, a.G, (uint16_t*)a.Y, a.stream);
+                                   a.d_ff, a.G, (uint16_t*)a.Y,
+                                   reinterpret_cast<float*>(ws + L.dpart), a.stream);
       else
         e = wide::launch_down_f32((const float*)H, (const float*)a.Wd, maskbits, a.T, a.d, a.d_ff,
                                   a.G, (float*)a.Y, a.stream);
@@ -521,8 +526,9 @@ WIDE_API wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = wide::launch_pack_mask_bits(mask, M, ng, maskbits, s);
   if (e != hipSuccess) return hip_status(e, "mask pack launch");
+  // (no partial-sum space in this workspace: no split last round)
   e = wide::launch_down_bf16((const uint16_t*)A, (const uint16_t*)B, maskbits, M, N, K, G,
-                             (uint16_t*)C, s);
+                             (uint16_t*)C, nullptr, s);
   if (e != hipSuccess) return hip_status(e, "GEMM-K launch");
   return ok();
 }

@@ -117,11 +117,12 @@ hipError_t launch_gemm_mn_bf16(const uint16_t* A, const uint16_t* B, const int32
   return hipSuccess;
 }
 hipError_t launch_down_bf16(const uint16_t* H, const uint16_t* Wd, const uint32_t* maskbits, int T,
-                            int d, int d_ff, int G, uint16_t* Y, hipStream_t) {
+                            int d, int d_ff, int G, uint16_t* Y, float* part, hipStream_t) {
   ++g_launches;
   rd(H, (size_t)T * d_ff * 2);
   rd(Wd, (size_t)d * d_ff * 2);
   rd(maskbits, (size_t)(d_ff / G) * words(T) * 4);
+  if (part) wr(part, down_split_bytes(T, d, d_ff));
   wr(Y, (size_t)T * d * 2);
   return hipSuccess;
 }
