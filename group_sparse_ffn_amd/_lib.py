@@ -28,7 +28,7 @@ WIDE_TOKEN_TILE = 256
 WIDE_DECODE_T_LIMIT = 16
 WIDE_FLAG_FORCE_PREFILL = 0x1
 WIDE_FLAG_FORCE_DECODE = 0x2
-WIDE_NOALLOC_SCRATCH_BYTES = 32 << 20
+WIDE_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 WIDE_ACT_IDENTITY = 0
 WIDE_ACT_RELU = 1

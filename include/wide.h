@@ -162,9 +162,10 @@ wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup
  * ends). The call allocates and frees nothing.
  *   H_out  required (non-NULL when T > 0): the array does not hold H.
  *   Limit: wide_ffn_workspace_size_for(T, d, d_ff, G, dtype, 1) must not
- *          exceed WIDE_NOALLOC_SCRATCH_BYTES (e.g. T * ngroups up to about
- *          7.9 million at d <= 16384), else WIDE_ERR_WORKSPACE and nothing is
- *          enqueued.
+ *          exceed WIDE_NOALLOC_SCRATCH_BYTES, else WIDE_ERR_WORKSPACE and
+ *          nothing is enqueued. 64 MiB of the array cover the largest
+ *          partial sums of the prefill down projection's split last round;
+ *          the rest holds T * ngroups up to about 7.9 million at d <= 16384.
  *   The array is shared by every call on one GPU and keeps the last call's
  *   contents (nothing in it needs to start at zero: every call writes what it
  *   reads). Calls that overlap on one GPU (different streams, or host
@@ -173,7 +174,7 @@ wide_status_t wide_ffn_forward(const void* X, const void* Wgate, const void* Wup
  * (hipGetSymbolAddress) and keeps it. Errors: as wide_ffn_forward, plus
  * WIDE_ERR_HIP when the device or the address cannot be obtained.
  */
-#define WIDE_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define WIDE_NOALLOC_SCRATCH_BYTES (96u << 20)
 wide_status_t wide_ffn_forward_noalloc(const void* X, const void* Wgate, const void* Wup,
                                        const void* Wdown, const uint8_t* mask, int32_t T,
                                        int32_t d, int32_t d_ff, int32_t G, wide_dtype_t dtype,

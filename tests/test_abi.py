@@ -376,9 +376,13 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     assert "WIDE_NOALLOC_SCRATCH_BYTES" in lib.wide_last_error().decode()
     assert lib.wide_ffn_workspace_size_for(1 << 19, 256, 1024, 16, _lib.WIDE_BF16, 1) > \
         _lib.WIDE_NOALLOC_SCRATCH_BYTES
-    # the largest workload of the bench fits
+    # the largest workload of the bench fits, and so does the Qwen3-14B shape,
+    # whose down projection splits its last round (64 tiles x 4 parts of
+    # fp32 partial sums in the workspace)
     assert lib.wide_ffn_workspace_size_for(16384, 4096, 14336, 128, _lib.WIDE_BF16, 1) <= \
         _lib.WIDE_NOALLOC_SCRATCH_BYTES
+    qwen = lib.wide_ffn_workspace_size_for(4096, 5120, 17408, 128, _lib.WIDE_BF16, 1)
+    assert 64 * 4 * 256 * 256 * 4 < qwen <= _lib.WIDE_NOALLOC_SCRATCH_BYTES
     # T == 0 with H_out NULL is a valid no-op
     assert call(T=0, H=None) == _lib.WIDE_OK
 

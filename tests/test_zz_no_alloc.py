@@ -110,3 +110,19 @@ def test_noalloc_rejects_without_enqueueing():
     assert st == _lib.WIDE_ERR_NULL
     torch.cuda.synchronize()
     assert bool((Y == 0).all())
+
+
+def test_noalloc_qwen14b_split_down():
+    # the down projection's last round is split (320 tiles: 64 remainder tiles
+    # x 4 parts), so its partial sums live in the static array too
+    w = dg.QWEN14B_SKEW
+    need = _lib.load().wide_ffn_workspace_size_for(w.T, w.d, w.d_ff, w.G, _lib.WIDE_BF16, 1)
+    assert need <= _lib.WIDE_NOALLOC_SCRATCH_BYTES
+    inp = dg.make_inputs(w)
+    x = {k: v.to(DEV) for k, v in inp.items()}
+    st, Y, H = noalloc_raw(x, w.G)
+    Yw, Hw = with_workspace(x, w.G)
+    torch.cuda.synchronize()
+    assert st == _lib.WIDE_OK, _lib.load().wide_last_error().decode()
+    assert same_bits(Y, Yw), "Y differs from wide_ffn_forward"
+    assert same_bits(H, Hw), "H differs from wide_ffn_forward"
