@@ -58,6 +58,7 @@ def check(X, W1, W2, act, rows=None):
     (1, 64, 16, 1, "identity"), (15, 256, 32, 3, "relu"), (16, 512, 64, 112, "silu"),
     (17, 4096, 32, 112, "silu"), (300, 1024, 16, 37, "relu"), (1000, 96, 32, 5, "silu"),
     (257, 4096, 64, 8, "identity"), (40, 5120, 32, 136, "silu"),
+    (300, 3072, 32, 24, "silu"), (100, 2048, 32, 16, "relu"),
 ])
 def test_router_small_all_outputs(T, D, r, ng, act):
     X, W1, W2 = inputs(T + D + r, T, D, r, ng)
