@@ -150,38 +150,61 @@ __device__ __forceinline__ bool ordered_tile(const int32_t* __restrict__ counts,
 // the mainloop loses its host launch stub with this toolchain.
 //   A [M, K] rows, gathered through perm; B and (SwiGLU) B2 [N, K]; C [M, N].
 //   Group g's row list is perm[g*M .. g*M + M), its active prefix counts[g].
-template <int CW, bool SWIGLU, int TT>
+//
+// DENSE (SwiGLU only, for groups narrower than 64 channels, where a group's
+// own tile would give the MFMA an A side of 16 or 32 rows and its row lists
+// skip almost nothing under random masks): tiles are 128-channel blocks of
+// every group over natural-order rows (no gather, no reorder); every product
+// is computed, and the store writes silu(gate) * up where the row executes
+// the channel's group (bit of maskbits [ngroups, words]) and +0.0 elsewhere.
+template <int CW, bool SWIGLU, int TT, bool DENSE = false>
 __device__ __forceinline__ void mn_body(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, int M, int K, int N, int G, uint16_t* __restrict__ C,
     int zero_inactive, int ntok_tiles, int nct, int total, uint8_t* sA, uint8_t* sB,
-    int* s_tok) {
+    int* s_tok, const uint32_t* __restrict__ maskbits = nullptr, int words = 0) {
   using SH = MnShape<CW, SWIGLU, TT>;
   using S = typename SH::S;
   constexpr int kTokTile = TT;
+  static_assert(!DENSE || SWIGLU, "the dense form is the gate/up projection's");
 
   int blk, tile, count;
-  if (!ordered_tile<TT>(counts, total / ntok_tiles, nct, ntok_tiles, zero_inactive != 0, blk, tile,
-                        count))
-    return;
+  if constexpr (DENSE) {
+    // XCD-aware: each XCD a contiguous range of (channel block, token tile)
+    // pairs, so the tiles running together on one XCD share weight rows
+    const int per_xcd = (total + 7) / 8;
+    const int L = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (L >= total) return;
+    blk = L / ntok_tiles;
+    tile = L % ntok_tiles;
+    count = M;
+  } else {
+    if (!ordered_tile<TT>(counts, total / ntok_tiles, nct, ntok_tiles, zero_inactive != 0, blk,
+                          tile, count))
+      return;
+  }
   const int tile0 = tile * kTokTile;
-  const int g = blk / nct;
-  const int ct = blk % nct;
+  const int g = DENSE ? 0 : blk / nct;
+  const int ct = DENSE ? blk : blk % nct;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ch0 = g * G + ct * CW;  // first channel of this tile
-  const int32_t* __restrict__ prow = perm + (size_t)g * M + tile0;
   const int nrows = min(kTokTile, M - tile0);          // positions that exist
   const int nact = max(0, min(nrows, count - tile0));  // active positions
   if (nact == 0 && !zero_inactive) return;  // level 0, nothing to clear
 
-  if (tid < kTokTile) s_tok[tid] = tid < nrows ? prow[tid] : 0;
+  if constexpr (DENSE) {
+    if (tid < kTokTile) s_tok[tid] = tid < nrows ? tile0 + tid : 0;
+  } else {
+    const int32_t* __restrict__ prow = perm + (size_t)g * M + tile0;
+    if (tid < kTokTile) s_tok[tid] = tid < nrows ? prow[tid] : 0;
+  }
   __syncthreads();
 
   // Zeros for the positions of this tile whose row skips the group.
-  if (zero_inactive) {
+  if (!DENSE && zero_inactive) {
     constexpr int kChunks = CW / 8;  // 16-byte chunks per row segment
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int e = nact * kChunks + tid; e < nrows * kChunks; e += 512) {
@@ -320,7 +343,14 @@ __device__ __forceinline__ void mn_body(
   // active positions: 16-byte segments to C[row, ch0 .. ch0 + CW)
   for (int e = tid; e < nact * kCpr; e += 512) {
     const int r = e / kCpr, c = e % kCpr;
-    const u32x4 v = *(const u32x4*)(srow(r) + ((c ^ (r % kCpr)) << 4));
+    u32x4 v = *(const u32x4*)(srow(r) + ((c ^ (r % kCpr)) << 4));
+    if constexpr (DENSE) {
+      // a 16-byte segment (8 channels) lies in one group: G is a multiple of 16
+      const int t = s_tok[r];
+      const uint32_t bit = (maskbits[(size_t)((ch0 + c * 8) / G) * words + (t >> 5)] >> (t & 31)) & 1u;
+      const uint32_t m = 0u - bit;
+      v &= u32x4{m, m, m, m};
+    }
     *(u32x4*)(C + (size_t)s_tok[r] * N + ch0 + c * 8) = v;
   }
 }
@@ -352,6 +382,18 @@ WIDE_MN_KERNEL(gemm_mn_bf16_kernel_256_t128, 256, false, 128)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_128_t128, 128, false, 128)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_64_t128, 64, false, 128)
 #undef WIDE_MN_KERNEL
+
+__global__ __launch_bounds__(512, 1) void gate_up_dense_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const uint16_t* __restrict__ B2, const uint32_t* __restrict__ maskbits, int words, int M,
+    int K, int N, int G, uint16_t* __restrict__ C, int ntok_tiles, int total) {
+  using SH = MnShape<128, true, 256>;
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[SH::S::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[SH::S::STAGE];
+  __shared__ int s_tok[256];
+  mn_body<128, true, 256, true>(A, B, B2, nullptr, nullptr, M, K, N, G, C, 1, ntok_tiles, 1, total,
+                                sA, sB, s_tok, maskbits, words);
+}
 
 typedef void (*MnKernel)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*,
                          const int32_t*, int, int, int, int, uint16_t*, int, int, int, int);
@@ -388,9 +430,17 @@ hipError_t launch_mn(MnKernel kernel, int CW, int TT, const uint16_t* A, const u
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
-                               const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
-                               int G, uint16_t* H, bool zero_inactive, hipStream_t stream) {
+                               const int32_t* perm, const int32_t* counts,
+                               const uint32_t* maskbits, int T, int d, int d_ff, int G,
+                               uint16_t* H, bool zero_inactive, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (gate_up_dense(G, d_ff)) {
+    const int ntok_tiles = (T + 255) / 256;
+    const int total = (d_ff / 128) * ntok_tiles;
+    hipLaunchKernelGGL(gate_up_dense_bf16_kernel, dim3((total + 7) / 8 * 8), dim3(512), 0, stream, X,
+                       Wg, Wu, maskbits, (T + 31) / 32, T, d, d_ff, G, H, ntok_tiles, total);
+    return hipGetLastError();
+  }
   const int cw = G % 128 == 0 ? 128 : G % 64 == 0 ? 64 : G % 32 == 0 ? 32 : 16;
   const int tt = mn_token_tile(T, d_ff, G, cw, true);
   MnKernel k = tt == 128 ? (cw == 128 ? gate_up_bf16_kernel_128_t128 : gate_up_bf16_kernel_64_t128)

@@ -201,6 +201,9 @@ wide_status_t run_stage(int32_t stage, const Args& a) {
       // partition from each group's contiguous bit row
       e = wide::launch_pack_mask_bits(a.mask, a.T, ng, maskbits, a.stream);
       if (e != hipSuccess) return hip_status(e, "mask pack launch");
+      // the dense-masked gate/up (narrow groups, bf16) and the down read
+      // only the bits
+      if (a.dt == WIDE_BF16 && wide::gate_up_dense(a.G, a.d_ff)) return ok();
       e = wide::launch_reorder_from_bits(maskbits, a.T, ng, WIDE_TOKEN_TILE, perm, counts, padded,
                                          a.stream);
       return hip_status(e, "mask reorder launch");
@@ -209,8 +212,8 @@ wide_status_t run_stage(int32_t stage, const Args& a) {
         // zeros at skipped pairs only when H is returned: the down kernel
         // never reads H at an inactive (token, group)
         e = wide::launch_gate_up_bf16((const uint16_t*)a.X, (const uint16_t*)a.Wg,
-                                      (const uint16_t*)a.Wu, perm, counts, a.T, a.d, a.d_ff, a.G,
-                                      (uint16_t*)H, zero_h, a.stream);
+                                      (const uint16_t*)a.Wu, perm, counts, maskbits, a.T, a.d,
+                                      a.d_ff, a.G, (uint16_t*)H, zero_h, a.stream);
       else
         e = wide::launch_gate_up_f32((const float*)a.X, (const float*)a.Wg, (const float*)a.Wu,
                                      perm, counts, a.T, a.d, a.d_ff, a.G, (float*)H, zero_h,

@@ -94,14 +94,19 @@ hipError_t launch_attention_decode_bf16(const uint16_t* q, const uint16_t* K, co
   return hipSuccess;
 }
 hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
-                               const int32_t* perm, const int32_t* counts, int T, int d, int d_ff,
-                               int G, uint16_t* H, bool, hipStream_t) {
+                               const int32_t* perm, const int32_t* counts,
+                               const uint32_t* maskbits, int T, int d, int d_ff, int G,
+                               uint16_t* H, bool, hipStream_t) {
   ++g_launches;
   rd(X, (size_t)T * d * 2);
   rd(Wg, (size_t)d_ff * d * 2);
   rd(Wu, (size_t)d_ff * d * 2);
-  rd(perm, (size_t)(d_ff / G) * T * 4);
-  rd(counts, (size_t)(d_ff / G) * 4);
+  if (gate_up_dense(G, d_ff)) {
+    rd(maskbits, (size_t)(d_ff / G) * words(T) * 4);
+  } else {
+    rd(perm, (size_t)(d_ff / G) * T * 4);
+    rd(counts, (size_t)(d_ff / G) * 4);
+  }
   wr(H, (size_t)T * d_ff * 2);
   return hipSuccess;
 }
