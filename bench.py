@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
     "down": ["gemm_k.hip", "mfma_core.h", "common.h"],
     "reorder": ["reorder.hip", "common.h"],
     "decode_gate_up": ["decode.hip", "common.h"],
+    "decode_gate_up_xlds": ["decode.hip", "common.h"],
+    "down_split_reduce": ["gemm_k.hip", "mfma_core.h", "common.h"],
     "gemm_mn": ["gemm_mn.hip", "mfma_core.h", "common.h"],
     "pack_mask_bits": ["reorder.hip", "common.h"],
     "reorder_bits": ["reorder.hip", "common.h"],
@@ -75,6 +77,8 @@ KERNEL_SYMBOLS = {
     "down": "down_bf16_kernel",
     "reorder": "reorder_kernel",
     "decode_gate_up": "decode_gate_up_kernel",
+    "decode_gate_up_xlds": "decode_gate_up_xlds_kernel",
+    "down_split_reduce": "down_split_reduce_kernel",
     "gemm_mn": "gemm_mn_bf16_kernel",
     "pack_mask_bits": "pack_mask_bits_kernel",
     "reorder_bits": "reorder_bits_kernel",
@@ -928,14 +932,16 @@ def profile_plan(dg, steps: int):
     plan = [(pre, "pack_mask_bits", n), (pre, "reorder_bits", n), (pre, "gate_up", n),
             (pre, "down", n)]
     qw = dg.QWEN14B_SKEW.name
+    # the Qwen3-14B down projection splits its last round (320 tiles = 256 + 64)
     plan += [(qw, "pack_mask_bits", PROFILE_QWEN_CALLS), (qw, "reorder_bits", PROFILE_QWEN_CALLS),
-             (qw, "gate_up", PROFILE_QWEN_CALLS), (qw, "down", PROFILE_QWEN_CALLS)]
-    # T = 1 takes the whole-row VALU GEMVs; T = 16 the MFMA gate/up and the
-    # split-K down with its reduce
+             (qw, "gate_up", PROFILE_QWEN_CALLS), (qw, "down", PROFILE_QWEN_CALLS),
+             (qw, "down_split_reduce", PROFILE_QWEN_CALLS)]
+    # T = 1 takes the whole-row VALU GEMVs; T = 16 the MFMA gate/up with the
+    # activations in LDS and the split-K down with its reduce
     t1, t16 = dg.LLAMA8B_DECODE_T1.name, dg.LLAMA8B_DECODE_T16.name
     plan += [(t1, "decode_gate_up_valu", PROFILE_DECODE_CALLS),
              (t1, "decode_down_valu", PROFILE_DECODE_CALLS),
-             (t16, "decode_gate_up", PROFILE_DECODE_CALLS),
+             (t16, "decode_gate_up_xlds", PROFILE_DECODE_CALLS),
              (t16, "decode_down_splitk", PROFILE_DECODE_CALLS),
              (t16, "decode_down_reduce", PROFILE_DECODE_CALLS),
              (T16_PREPARED, "decode_gate_up_packed", PROFILE_DECODE_CALLS),
@@ -979,6 +985,7 @@ def split_by_plan(plan, dispatches):
 # flops of one MFMA instruction of each kernel (its instruction shape)
 MFMA_FLOPS = {"gate_up": 2 * 32 * 32 * 16, "down": 2 * 32 * 32 * 16, "gemm_mn": 2 * 32 * 32 * 16,
               "decode_gate_up": 2 * 16 * 16 * 32, "decode_down_splitk": 2 * 16 * 16 * 32,
+              "decode_gate_up_xlds": 2 * 16 * 16 * 32,
               "decode_gate_up_packed": 2 * 16 * 16 * 32,
               "decode_down_splitk_packed": 2 * 16 * 16 * 32,
               "router": 2 * 16 * 16 * 32, "router_small": 2 * 16 * 16 * 32,
@@ -1003,7 +1010,7 @@ def work_closed_forms(dg):
             out[(w.name, "down")] = (2.0 * w.N * w.G * a, 2.0 * w.M * w.N * w.K)
     t16 = dg.LLAMA8B_DECODE_T16
     # 16 token columns per MFMA; every group is live at T = 16
-    out[(t16.name, "decode_gate_up")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
+    out[(t16.name, "decode_gate_up_xlds")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
     out[(t16.name, "decode_down_splitk")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
     out[(T16_PREPARED, "decode_gate_up_packed")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
     out[(T16_PREPARED, "decode_down_splitk_packed")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
@@ -1058,7 +1065,7 @@ def mfma_summary(directory, command, plan, split_fn):
              "The router's ratio is not 1: its second map runs v_mfma_f32_16x16x4_f32",
              "(2048 flops), which the counter counts beside the 16x16x32 bf16 instructions of",
              "the first map and this table prices at 16384.", "",
-             "```", command.replace("PMC", "SQ_INSTS_MFMA"), "```", "",
+             "```", command.replace("PMC", "SQ_INSTS_MFMA").replace("PASS", "mfma"), "```", "",
              "| kernel | workload | counted TFLOP | algorithmic TFLOP | designed TFLOP | counted / designed |",
              "|---|---|---|---|---|---|"]
     for workload, kernel, _ in plan:
@@ -1119,7 +1126,8 @@ def busy_summary(directory, command, plan, split_fn, out_dir=None):
              f"({nsimd} x one XCD's active cycles). `peak at clock` scales the 2.5 PFLOP/s",
              "bf16 dense peak (quoted at 2.4 GHz) to the measured clock; `designed TFLOP/s`",
              "is the kernel's designed MFMA work over its duration.", "",
-             "```", command.replace("PMC", "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"), "```", "",
+             "```", command.replace("PMC", "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE").replace("PASS", "busy"),
+             "```", "",
              "| kernel | workload | duration (us) | clock (GHz) | MFMA busy | peak at clock (TFLOP/s) "
              "| designed TFLOP/s |",
              "|---|---|---|---|---|---|---|"]
@@ -1145,11 +1153,27 @@ def busy_summary(directory, command, plan, split_fn, out_dir=None):
     print(f"wrote {out}")
 
 
+def profile_commands(steps: int):
+    """The kernel-trace command and the counter-run template (PMC: the
+    counters, PASS: the output folder) of a profile run, from the repository
+    root on one MI355X."""
+    pre = "cd /tmp && export TMPDIR=/tmp && rocprofv3"
+    run = f"-o run -- python3 <repo>/bench.py --profile --steps {steps}"
+    return (f"{pre} --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof/ktrace {run}",
+            f"{pre} --pmc PMC --output-format csv -d <repo>/gpurun_out/prof/PASS {run}")
+
+
 def summarize(directory: str, command: str, steps: int):
     """Turn rocprofv3 CSVs (kernel trace, FETCH_SIZE and WRITE_SIZE counter runs) into profiles/*.md.
 
-    Dispatches are attributed to workloads by their order in the profile run."""
+    Dispatches are attributed to workloads by their order in the profile run.
+    command: the counter-run template (PMC, PASS placeholders); empty = the
+    commands of profile_commands(steps)."""
     from group_sparse_ffn_amd import datagen as dg
+    ktrace_cmd, pmc_cmd = profile_commands(steps)
+    if command:
+        ktrace_cmd = pmc_cmd = command
+    command = pmc_cmd
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     plan = profile_plan(dg, steps)
 
@@ -1168,7 +1192,7 @@ def summarize(directory: str, command: str, steps: int):
         split = split_by_plan(plan, durs)
         lines = ["# Kernel trace: Llama3.1-8B-shaped FFN (prefill T=16384, decode T=1 and T=16) "
                  "and masked GEMMs at its attention shapes",
-                 "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+                 "", "Command (from the repository root, one MI355X):", "", "```", ktrace_cmd, "```", "",
                  "Per-dispatch durations from the kernel trace, attributed to workloads by "
                  "launch order.", "",
                  "| kernel | workload | calls | median (us) | avg (us) | min (us) | max (us) |",
@@ -1225,8 +1249,8 @@ def summarize(directory: str, command: str, steps: int):
                 "WRITE_SIZE), averaged over the kernel's dispatches for this workload, in KiB,",
                 f"scaled by what the same counter reads for a device copy of {COPY_BYTES} bytes",
                 "in the same run.", "",
-                "```", command.replace("PMC", "FETCH_SIZE"), command.replace("PMC", "WRITE_SIZE"),
-                "```", "",
+                "```", command.replace("PMC", "FETCH_SIZE").replace("PASS", "fetch"),
+                command.replace("PMC", "WRITE_SIZE").replace("PASS", "write"), "```", "",
                 f"- FETCH_SIZE_KiB: {vals['FETCH_SIZE']:.1f}",
                 f"- WRITE_SIZE_KiB: {vals['WRITE_SIZE']:.1f}",
                 f"- fetch_scale: {scale['FETCH_SIZE']:.4f}",
