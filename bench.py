@@ -59,7 +59,8 @@ KERNEL_SOURCES = {
     "pack_mask_bits": ["reorder.hip", "common.h"],
     "reorder_bits": ["reorder.hip", "common.h"],
     "router": ["router.hip", "common.h"],
-    "router_small": ["router.hip", "common.h"],
+    "router_zpart": ["router.hip", "common.h"],
+    "router_decide": ["router.hip", "common.h"],
     "decode_down_splitk": ["decode.hip", "common.h"],
     "decode_gate_up_packed": ["decode.hip", "common.h"],
     "decode_down_splitk_packed": ["decode.hip", "common.h"],
@@ -83,7 +84,8 @@ KERNEL_SYMBOLS = {
     "pack_mask_bits": "pack_mask_bits_kernel",
     "reorder_bits": "reorder_bits_kernel",
     "router": "router_kernel_",
-    "router_small": "router_small_kernel_",
+    "router_zpart": "router_zpart_kernel",
+    "router_decide": "router_decide_kernel",
     "decode_down_splitk": "decode_down_splitk_kernel<false, false>",
     "decode_gate_up_packed": "decode_gate_up_packed_kernel",
     "decode_down_splitk_packed": "decode_down_splitk_kernel<false, true>",
@@ -956,7 +958,8 @@ def profile_plan(dg, steps: int):
             plan += [(w.name, "pack_mask_bits", PROFILE_GEMM_CALLS),
                      (w.name, "down", PROFILE_GEMM_CALLS)]
     plan += [(ROUTER_WORKLOADS[16384], "router", PROFILE_GEMM_CALLS),
-             (ROUTER_WORKLOADS[1], "router_small", PROFILE_GEMM_CALLS)]
+             (ROUTER_WORKLOADS[1], "router_zpart", PROFILE_GEMM_CALLS),
+             (ROUTER_WORKLOADS[1], "router_decide", PROFILE_GEMM_CALLS)]
     aw = dg.LLAMA8B_ATTN_PREFILL.name
     plan += [(aw, "pack_mask_bits", PROFILE_GEMM_CALLS), (aw, "reorder_bits", PROFILE_GEMM_CALLS),
              (aw, "attention_vt", PROFILE_GEMM_CALLS), (aw, "attention_prefill", PROFILE_GEMM_CALLS),
@@ -988,7 +991,8 @@ MFMA_FLOPS = {"gate_up": 2 * 32 * 32 * 16, "down": 2 * 32 * 32 * 16, "gemm_mn": 
               "decode_gate_up_xlds": 2 * 16 * 16 * 32,
               "decode_gate_up_packed": 2 * 16 * 16 * 32,
               "decode_down_splitk_packed": 2 * 16 * 16 * 32,
-              "router": 2 * 16 * 16 * 32, "router_small": 2 * 16 * 16 * 32,
+              "router": 2 * 16 * 16 * 32, "router_zpart": 2 * 16 * 16 * 32,
+              "router_decide": 2 * 16 * 16 * 4,
               "attention_prefill": 2 * 32 * 32 * 16}
 
 
@@ -1015,7 +1019,10 @@ def work_closed_forms(dg):
     out[(T16_PREPARED, "decode_gate_up_packed")] = (2.0 * 2 * t16.d_ff * t16.d * 16,) * 2
     out[(T16_PREPARED, "decode_down_splitk_packed")] = (2.0 * t16.d_ff * t16.d * 16,) * 2
     out[("llama3.1-8b-router-prefill", "router")] = (2.0 * 16384 * 4096 * 32,) * 2
-    out[("llama3.1-8b-router-decode-t1", "router_small")] = (2.0 * 16 * 4096 * 32,) * 2
+    # T = 1: the first map runs 16 token rows (one MFMA block); the second map
+    # 16 rows x 2 N_G columns x r
+    out[("llama3.1-8b-router-decode-t1", "router_zpart")] = (2.0 * 16 * 4096 * 32,) * 2
+    out[("llama3.1-8b-router-decode-t1", "router_decide")] = (2.0 * 16 * 224 * 32,) * 2
     aw = dg.LLAMA8B_ATTN_PREFILL
     out[(aw.name, "attention_prefill")] = attention_work(dg.make_attention_inputs(aw)["mask"], aw)
     return out

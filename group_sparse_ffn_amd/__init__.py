@@ -19,7 +19,7 @@ from ._lib import (WIDE_BF16, WIDE_DECODE_T_LIMIT, WIDE_F32, WIDE_FLAG_FORCE_DEC
 
 __all__ = ["reorder_masks", "ffn_forward", "ffn_stage", "workspace_size", "decode_max_t",
            "gemm_mn", "gemm_k", "gemm_workspace_size", "router_forward", "router_reorder",
-           "RouterReorderCall", "router_reorder_workspace_size",
+           "RouterReorderCall", "router_reorder_workspace_size", "router_workspace_size",
            "FfnCall", "WideError", "WIDE_TOKEN_TILE", "WIDE_DECODE_T_LIMIT",
            "WIDE_FLAG_FORCE_PREFILL", "WIDE_FLAG_FORCE_DECODE", "WIDE_STAGE_REORDER",
            "WIDE_STAGE_GATE_UP", "WIDE_STAGE_DOWN", "WIDE_STAGE_DECODE_GATE_UP",
@@ -254,9 +254,15 @@ def gemm_k(A, B, mask, G: int, C=None, workspace=None):
 _ACTS = {"identity": _lib.WIDE_ACT_IDENTITY, "relu": _lib.WIDE_ACT_RELU, "silu": _lib.WIDE_ACT_SILU}
 
 
+def router_workspace_size(T: int, r: int) -> int:
+    return int(_lib.load().wide_router_workspace_size(T, r))
+
+
 def router_forward(X, W1, W2, act: str = "silu", return_logits: bool = False, mask=None,
-                   logits=None):
-    """Bottleneck router -> mask [T, N_G] uint8 (1 = execute), and logits [T, N_G, 2] fp32."""
+                   logits=None, workspace=None):
+    """Bottleneck router -> mask [T, N_G] uint8 (1 = execute), and logits [T, N_G, 2] fp32.
+    `workspace` (uint8 device tensor of router_workspace_size(T, r) bytes) is allocated when
+    not given and needed (1 <= T <= 16)."""
     for name, t in (("X", X), ("W1", W1), ("W2", W2)):
         _need_cuda(name, t)
     if any(t.dtype != torch.bfloat16 for t in (X, W1, W2)):
@@ -271,9 +277,14 @@ def router_forward(X, W1, W2, act: str = "silu", return_logits: bool = False, ma
         mask = torch.empty((T, ng), dtype=torch.uint8, device=dev)
     if return_logits and logits is None:
         logits = torch.empty((T, ng, 2), dtype=torch.float32, device=dev)
+    need = router_workspace_size(T, r)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _lib.check(_lib.load().wide_router_forward(
         X.data_ptr(), W1.data_ptr(), W2.data_ptr(), T, D, r, ng, _ACTS[act], WIDE_BF16,
-        mask.data_ptr(), None if logits is None else logits.data_ptr(), _stream_ptr(dev)))
+        mask.data_ptr(), None if logits is None else logits.data_ptr(),
+        None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel(), _stream_ptr(dev)))
     return (mask, logits) if return_logits else mask
 
 

@@ -63,8 +63,9 @@ SIGNATURES = {
     "wide_gemm_workspace_size": (_sz, [_i32, _i32]),
     "wide_gemm_mn": (ctypes.c_int, _GEMM_ARGS),
     "wide_gemm_k": (ctypes.c_int, _GEMM_ARGS),
+    "wide_router_workspace_size": (_sz, [_i32, _i32]),
     "wide_router_forward": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int,
-                                           ctypes.c_int, _p, _p, _p]),
+                                           ctypes.c_int, _p, _p, _p, _sz, _p]),
     "wide_router_reorder_workspace_size": (_sz, [_i32, _i32]),
     "wide_router_reorder": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int,
                                            ctypes.c_int, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),

@@ -209,10 +209,18 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
 // Bottleneck router: mask[t, g] = argmax over the two logits of group g is
 // class 0 (act 0 identity, 1 relu, 2 silu). Each output is optional (NULL =
 // not written): mask bytes [T, ng], logits [T, ng, 2], and the decisions packed
-// as maskbits [ng, ceil(T/32)] (the layout of launch_pack_mask_bits).
+// as maskbits [ng, ceil(T/32)] (the layout of launch_pack_mask_bits). For
+// 1 <= T <= kRouterSmallT the first map's partial sums go to `zpart`
+// (router_zpart_bytes(T, r) bytes of workspace, 16-byte aligned; contents on
+// entry ignored); otherwise zpart is not used and may be null.
+constexpr int kRouterSmallT = 16;
+constexpr int kRouterSlices = 8;  // workgroups (slices of D) of the small-T first map
 hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
                               int D, int r, int ng, int act, uint8_t* mask, float* logits,
-                              uint32_t* maskbits, hipStream_t stream);
+                              uint32_t* maskbits, float* zpart, hipStream_t stream);
+inline size_t router_zpart_bytes(int T, int r) {
+  return T >= 1 && T <= kRouterSmallT ? (size_t)kRouterSlices * 16 * r * sizeof(float) : 0;
+}
 
 // Device address of the no-allocation entry point's scratch array
 // (WIDE_NOALLOC_SCRATCH_BYTES, 256-byte aligned) on the device that runs

@@ -10,7 +10,7 @@
 //   mask[t,g]    = logit[t,g,0] >= logit[t,g,1]
 //
 // The first map reads every activation byte once and is bound by HBM, so the
-// kernel is built to stream X: a workgroup owns 64 tokens and its eight waves
+// many-token kernel is built to stream X: a workgroup owns 64 tokens and its eight waves
 // split D; each wave reads 16-byte pieces of X in the layout of a
 // v_mfma_f32_16x16x32_bf16 operand (16 tokens x 32 channels per load) against
 // the r / 16 matching fragments of W1 (shared by every workgroup, served from
@@ -25,10 +25,9 @@ namespace wide {
 
 namespace {
 
-// Two shapes of workgroup: for many tokens, 8 waves over 64 tokens (every W1
-// fragment serves four 16-token blocks; measured against 4 and 16 waves and
-// 16- or 32-token workgroups); for at most 16 tokens, 16 waves over one
-// block, so that the chain of dependent loads along D is 16 times shorter.
+// The many-token workgroup: 8 waves over 64 tokens (every W1 fragment serves
+// four 16-token blocks; measured against 4 and 16 waves and 16- or 32-token
+// workgroups).
 constexpr int kRtGC = 64;  // groups whose mask bytes gather in LDS at a time
 
 // X pieces are read in the MFMA operand layout (half of a 128-byte line per
@@ -53,9 +52,8 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   constexpr int kRtTok = 16 * kRtRB;
   constexpr int kRtThreads = 64 * kRtWaves;
   constexpr int NF = R / 16;  // W1 fragments of 16 outputs
-  // k-steps per load batch: the many-token shape keeps two batches of four
-  // blocks in flight; the one-block shape loads a quarter of its D slice at once
-  constexpr int kU = kRtRB == 1 ? (R >= 64 ? 2 : 4) : (R >= 64 ? 1 : 2);
+  // k-steps per load batch: two batches of kRtRB blocks in flight
+  constexpr int kU = R >= 64 ? 1 : 2;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -245,28 +243,178 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
 WIDE_ROUTER_KERNEL(router_kernel_16, 16, 4, 8)
 WIDE_ROUTER_KERNEL(router_kernel_32, 32, 4, 8)
 WIDE_ROUTER_KERNEL(router_kernel_64, 64, 4, 8)
-WIDE_ROUTER_KERNEL(router_small_kernel_16, 16, 1, 16)
-WIDE_ROUTER_KERNEL(router_small_kernel_32, 32, 1, 16)
-WIDE_ROUTER_KERNEL(router_small_kernel_64, 64, 1, 16)
 #undef WIDE_ROUTER_KERNEL
+
+// ---- At most 16 tokens: two kernels instead of one workgroup.
+// One workgroup streaming all of W1 (r * D * 2 bytes, 256 KB at D = 4096,
+// r = 32) is bound by the misses a single CU keeps in flight: its last wave
+// finished the first map 8 us after the first (timestamps inside the kernel,
+// T = 1). So the first map is split over kRtSlices workgroups, each taking a
+// slice of D for all tokens and outputs and writing fp32 partial sums
+// [kRtSlices][16][r] (D = 4096, r = 32, per call in a graph at T = 1: one
+// workgroup 12.9 us; 4, 8, 16 and 32 slices 6.7, 5.8, 6.3 and 6.9 us; 8
+// slices of 8 waves 6.6 us); a second kernel with one wave per 16 logit columns
+// (8 groups) requests its W2 rows at once, adds the partial sums in slice
+// order (fixed order: the same z every call), applies the activation and takes
+// the decisions as the many-token kernel does.
+constexpr int kRtSlices = kRouterSlices;
+
+template <int R>
+__global__ __launch_bounds__(256) void router_zpart_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ W1, int T,
+                                                           int D, float* __restrict__ zpart) {
+  constexpr int NF = R / 16;
+  __shared__ float s_part[4][16][R];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nsub = D / 32;  // 32-channel k-steps
+  const int sbeg = (int)(((long long)blockIdx.x * nsub) / kRtSlices);
+  const int send = (int)(((long long)(blockIdx.x + 1) * nsub) / kRtSlices);
+  // A operand row = token (rows past T - 1 repeat token T - 1; never stored),
+  // B operand row = output 16 f + lane % 16; lane group lane / 16 holds k 8 (lane / 16) ..
+  const int kof = 8 * (lane >> 4);
+  const uint16_t* px = X + (size_t)min(lane & 15, T - 1) * D + kof;
+  const uint16_t* pw[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) pw[f] = W1 + (size_t)(16 * f + (lane & 15)) * D + kof;
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // wave w takes k-steps sbeg + w, + 4, + 8, ...: four per pass, loads clamped
+  // into the slice (so none sits under a condition), MFMAs only for real steps
+  for (int s0 = sbeg + wave; s0 < send; s0 += 16) {
+    u32x4 xa[4], wb[4][NF];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 32 * min(s0 + 4 * i, send - 1);
+      xa[i] = *(const u32x4*)(px + k);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) wb[i][f] = *(const u32x4*)(pw[f] + k);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s0 + 4 * i < send)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[i]),
+                                                           __builtin_bit_cast(bf16x8, wb[i][f]),
+                                                           acc[f], 0, 0, 0);
+  }
+  // lane holds the partial z of token 4 (lane / 16) + e, output 16 f + lane % 16
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_part[wave][4 * (lane >> 4) + e][16 * f + (lane & 15)] = acc[f][e];
+  __syncthreads();
+  float* out = zpart + (size_t)blockIdx.x * 16 * R;
+  for (int e = tid; e < 16 * R; e += 256) {
+    const int t = e / R, j = e % R;
+    out[e] = ((s_part[0][t][j] + s_part[1][t][j]) + s_part[2][t][j]) + s_part[3][t][j];
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(64) void router_decide_kernel(
+    const uint16_t* __restrict__ W2, const float* __restrict__ zpart, int T, int ng, int act,
+    uint8_t* __restrict__ mask, float* __restrict__ logits, uint32_t* __restrict__ maskbits,
+    int words) {
+  constexpr int KQ = R / 4;
+  const int lane = threadIdx.x, q = lane >> 4, c16 = lane & 15;
+  const int col = 16 * (int)blockIdx.x + c16;  // logit column 2 g + c
+  const bool colok = col < 2 * ng;
+  // this lane's W2 piece: row col, k = KQ q .. KQ q + KQ (row 0 stands in past the end)
+  const uint32_t* pw2 = (const uint32_t*)(W2 + (size_t)(colok ? col : 0) * R + KQ * q);
+  uint32_t wv[KQ / 2];
+#pragma unroll
+  for (int i = 0; i < KQ / 2; ++i) wv[i] = pw2[i];
+  // z of token c16 at k = KQ q .. KQ q + KQ: the slices' partial sums (in slice
+  // order), CS slices' loads in flight at a time (64 floats per lane)
+  constexpr int CS = 64 / KQ < kRtSlices ? 64 / KQ : kRtSlices;
+  static_assert(kRtSlices % CS == 0, "slice chunks");
+  float z[KQ];
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) z[i] = 0.0f;
+#pragma unroll
+  for (int s0 = 0; s0 < kRtSlices; s0 += CS) {
+    f32x4 zp[CS][KQ / 4];
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+      for (int i = 0; i < KQ / 4; ++i)
+        zp[s][i] = *(const f32x4*)(zpart + ((size_t)(s0 + s) * 16 + c16) * R + KQ * q + 4 * i);
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+      for (int i = 0; i < KQ / 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[4 * i + e] += zp[s][i][e];
+  }
+  // logits of tokens 4 q + e, column c16 (v_mfma_f32_16x16x4_f32 with the k
+  // slot permuted as in the many-token kernel)
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KQ; ++kk) {
+    const uint32_t w = colok ? wv[kk >> 1] : 0u;
+    const uint32_t bits = (kk & 1) ? (w & 0xFFFF0000u) : (w << 16);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(router_act(z[kk], act),
+                                               __builtin_bit_cast(float, bits), acc, 0, 0, 0);
+  }
+  // lane ^ 1 holds the other class of the same group and tokens
+  const int g = col >> 1;
+  const bool dec_lane = colok && (c16 & 1) == 0;
+  uint64_t bal[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float other = __shfl_xor(acc[e], 1);
+    const int t = 4 * q + e;
+    const bool exec = acc[e] >= other;
+    if (mask && dec_lane && t < T) mask[(size_t)t * ng + g] = exec ? 1 : 0;
+    if (logits && colok && t < T) logits[(size_t)t * ng * 2 + col] = acc[e];
+    bal[e] = __ballot(dec_lane && t < T && exec);
+  }
+  // packed decisions: lane gl < 8 builds the word of group 8 blockIdx.x + gl
+  // (T <= 16: one word per group, bit t = token t)
+  if (maskbits) {
+    const int gg = 8 * (int)blockIdx.x + lane;
+    if (lane < 8 && gg < ng) {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= (uint32_t)((bal[e] >> (16 * qq + 2 * lane)) & 1u) << (4 * qq + e);
+      maskbits[(size_t)gg * words] = w;
+    }
+  }
+}
 
 }  // namespace
 
 hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
                               int D, int r, int ng, int act, uint8_t* mask, float* logits,
-                              uint32_t* maskbits, hipStream_t stream) {
+                              uint32_t* maskbits, float* zpart, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int words = (T + 31) / 32;
+  if (T <= kRouterSmallT) {
+    typedef void (*KZ)(const uint16_t*, const uint16_t*, int, int, float*);
+    typedef void (*KD)(const uint16_t*, const float*, int, int, int, uint8_t*, float*, uint32_t*,
+                       int);
+    const KZ kz = r == 16 ? router_zpart_kernel<16> : r == 32 ? router_zpart_kernel<32>
+                                                              : router_zpart_kernel<64>;
+    const KD kd = r == 16 ? router_decide_kernel<16> : r == 32 ? router_decide_kernel<32>
+                                                               : router_decide_kernel<64>;
+    hipLaunchKernelGGL(kz, dim3(kRtSlices), dim3(256), 0, stream, X, W1, T, D, zpart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kd, dim3((ng + 7) / 8), dim3(64), 0, stream, W2, zpart, T, ng, act, mask,
+                       logits, maskbits, words);
+    return hipGetLastError();
+  }
   typedef void (*K)(const uint16_t*, const uint16_t*, const uint16_t*, int, int, int, int, uint8_t*,
                     float*, uint32_t*, int);
-  const bool small = T <= 16;
-  const K k = small ? (r == 16 ? router_small_kernel_16 : r == 32 ? router_small_kernel_32
-                                                                  : router_small_kernel_64)
-                    : (r == 16 ? router_kernel_16 : r == 32 ? router_kernel_32 : router_kernel_64);
-  const dim3 grid(small ? 1 : (T + 63) / 64), block(small ? 1024 : 512);
-  hipLaunchKernelGGL(k, grid, block, 0, stream, X, W1, W2, T, D, ng, act, mask, logits, maskbits,
-                     words);
+  const K k = r == 16 ? router_kernel_16 : r == 32 ? router_kernel_32 : router_kernel_64;
+  hipLaunchKernelGGL(k, dim3((T + 63) / 64), dim3(512), 0, stream, X, W1, W2, T, D, ng, act, mask,
+                     logits, maskbits, words);
   return hipGetLastError();
 }
+
 
 }  // namespace wide

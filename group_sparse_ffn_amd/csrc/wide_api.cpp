@@ -675,28 +675,43 @@ size_t router_bits_bytes(int64_t T, int64_t ngroups) {
 
 }  // namespace
 
+WIDE_API size_t wide_router_workspace_size(int32_t T, int32_t r) {
+  if (T < 0 || (r != 16 && r != 32 && r != 64)) return 0;
+  return wide::router_zpart_bytes(T, r);
+}
+
 WIDE_API wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
                                            int32_t T, int32_t D, int32_t r, int32_t ngroups,
                                            wide_act_t act, wide_dtype_t dtype, uint8_t* mask,
-                                           float* logits, void* stream) {
+                                           float* logits, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
   const int32_t ac = raw(act);
   wide_status_t st = validate_router(X, W1, W2, T, D, r, ngroups, ac, raw(dtype));
   if (st != WIDE_OK) return st;
   if (T != 0 && !mask) return fail(WIDE_ERR_NULL, "mask must be non-NULL when T > 0");
   if ((reinterpret_cast<uintptr_t>(logits) & 7u) != 0)
     return fail(WIDE_ERR_ALIGN, "logits must be 8-byte aligned");
+  const size_t need = wide::router_zpart_bytes(T, r);
+  if (need > 0) {
+    if (!workspace) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
   if (T == 0) return ok();
-  const hipError_t e = wide::launch_router_bf16((const uint16_t*)X, (const uint16_t*)W1,
-                                                (const uint16_t*)W2, T, D, r, ngroups, ac,
-                                                mask, logits, nullptr,
-                                                static_cast<hipStream_t>(stream));
+  const hipError_t e = wide::launch_router_bf16(
+      (const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)W2, T, D, r, ngroups, ac, mask,
+      logits, nullptr, need > 0 ? static_cast<float*>(workspace) : nullptr,
+      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "router launch");
   return ok();
 }
 
+// [bits][partial sums of the first map for T <= 16, sized for r = 64]
 WIDE_API size_t wide_router_reorder_workspace_size(int32_t T, int32_t ngroups) {
   if (T < 0 || ngroups < 1) return 0;
-  return router_bits_bytes(T, ngroups);
+  return router_bits_bytes(T, ngroups) + wide::router_zpart_bytes(T, 64);
 }
 
 WIDE_API wide_status_t wide_router_reorder(const void* X, const void* W1, const void* W2,
@@ -713,7 +728,7 @@ WIDE_API wide_status_t wide_router_reorder(const void* X, const void* W1, const 
   if (tile < 1) return fail(WIDE_ERR_SHAPE, "need tile >= 1 (tile=%d)", tile);
   if ((reinterpret_cast<uintptr_t>(logits) & 7u) != 0)
     return fail(WIDE_ERR_ALIGN, "logits must be 8-byte aligned");
-  const size_t need = router_bits_bytes(T, ngroups);
+  const size_t need = router_bits_bytes(T, ngroups) + wide::router_zpart_bytes(T, 64);
   if (!workspace) return fail(WIDE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(WIDE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -721,10 +736,12 @@ WIDE_API wide_status_t wide_router_reorder(const void* X, const void* W1, const 
     return fail(WIDE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* maskbits = static_cast<uint32_t*>(workspace);
+  float* zpart = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                          router_bits_bytes(T, ngroups));
   hipError_t e = hipSuccess;
   if (T > 0) {
     e = wide::launch_router_bf16((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)W2, T, D,
-                                 r, ngroups, ac, mask, logits, maskbits, s);
+                                 r, ngroups, ac, mask, logits, maskbits, zpart, s);
     if (e != hipSuccess) return hip_status(e, "router launch");
   }
   // T == 0: the partition still writes counts = padded = 0

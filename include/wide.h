@@ -313,13 +313,21 @@ wide_status_t wide_gemm_k(const void* A, const void* B, const uint8_t* mask, int
  *   act     WIDE_ACT_*.
  *   mask    [T, ngroups]    device, uint8, written.
  *   logits  [T, ngroups, 2] device, fp32, written when non-NULL.
+ *   workspace  device scratch of wide_router_workspace_size(T, r) bytes,
+ *              256-byte aligned, contents on entry ignored, owned by the
+ *              caller; may be NULL when that size is 0 (T > 16 or T == 0).
+ *              For 1 <= T <= 16 it holds the first map's partial sums: that
+ *              map is split over D into 8 workgroups, so that W1 streams
+ *              through 8 CUs instead of one.
  * z and the logits are computed in fp32 from bf16 operands (fp32 products and
- * sums, fixed order), and the argmax is taken on those fp32 logits.
+ * sums, fixed order: the same result every call), and the argmax is taken on
+ * those fp32 logits.
  * Sizes: T >= 0 (T == 0 enqueues nothing; X, mask and logits may then be
  * NULL), ngroups >= 1; the kernels need D % 32 == 0, r in {16, 32, 64} and
  * T*D, T*ngroups < 2^31, else WIDE_ERR_UNSUPPORTED. bf16 only.
  * Errors: WIDE_ERR_NULL, WIDE_ERR_SHAPE, WIDE_ERR_DTYPE, WIDE_ERR_ALIGN,
- * WIDE_ERR_UNSUPPORTED, WIDE_ERR_HIP.
+ * WIDE_ERR_WORKSPACE (workspace NULL or smaller than its size while that size
+ * is not 0), WIDE_ERR_UNSUPPORTED, WIDE_ERR_HIP.
  */
 typedef enum {
   WIDE_ACT_IDENTITY = 0,
@@ -327,9 +335,13 @@ typedef enum {
   WIDE_ACT_SILU = 2  /* a / (1 + exp(-a)) */
 } wide_act_t;
 
+/* Workspace bytes of wide_router_forward: 8 * 16 * r * 4 for 1 <= T <= 16,
+   else 0 (also 0 for T < 0 or r not in {16, 32, 64}). */
+size_t wide_router_workspace_size(int32_t T, int32_t r);
 wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2, int32_t T,
                                   int32_t D, int32_t r, int32_t ngroups, wide_act_t act,
-                                  wide_dtype_t dtype, uint8_t* mask, float* logits, void* stream);
+                                  wide_dtype_t dtype, uint8_t* mask, float* logits,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * wide_router_reorder - the router of wide_router_forward fused with the mask
@@ -350,7 +362,9 @@ wide_status_t wide_router_forward(const void* X, const void* W1, const void* W2,
  *   perm, counts, padded: as wide_reorder_masks (perm may be NULL when T == 0):
  *                   exactly wide_reorder_masks applied to the mask above.
  *   workspace       device, 256-byte aligned, at least
- *                   wide_router_reorder_workspace_size(T, ngroups) bytes.
+ *                   wide_router_reorder_workspace_size(T, ngroups) bytes
+ *                   (the packed bits, and for T <= 16 the first map's
+ *                   partial sums as in wide_router_forward).
  * Errors: as wide_router_forward, plus WIDE_ERR_SHAPE (tile < 1),
  * WIDE_ERR_WORKSPACE.
  */

@@ -29,11 +29,11 @@ int c_caller_bad_enums(void* p) {
   if (wide_ffn_stage(sg, p, p, p, p, (const uint8_t*)p, 64, 64, 128, 64, WIDE_BF16, p, NULL, p,
                      1u << 30, 0, NULL) != WIDE_ERR_SHAPE)
     ++fails;
-  if (wide_router_forward(p, p, p, 4, 64, 16, 2, ac, WIDE_BF16, (uint8_t*)p, NULL, NULL) !=
-      WIDE_ERR_SHAPE)
+  if (wide_router_forward(p, p, p, 4, 64, 16, 2, ac, WIDE_BF16, (uint8_t*)p, NULL, p, 1u << 20,
+                          NULL) != WIDE_ERR_SHAPE)
     ++fails;
-  if (wide_router_forward(p, p, p, 4, 64, 16, 2, WIDE_ACT_SILU, dt, (uint8_t*)p, NULL, NULL) !=
-      WIDE_ERR_DTYPE)
+  if (wide_router_forward(p, p, p, 4, 64, 16, 2, WIDE_ACT_SILU, dt, (uint8_t*)p, NULL, p, 1u << 20,
+                          NULL) != WIDE_ERR_DTYPE)
     ++fails;
   if (wide_attention_prefill(p, p, p, (const uint8_t*)p, 4, 2, 1, 128, dt, p, 0, p, 1u << 30,
                              NULL) != WIDE_ERR_DTYPE)

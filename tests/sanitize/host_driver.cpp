@@ -165,11 +165,12 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
 }
 hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* W2, int T,
                               int D, int r, int ng, int, uint8_t* mask, float* logits,
-                              uint32_t* maskbits, hipStream_t) {
+                              uint32_t* maskbits, float* zpart, hipStream_t) {
   ++g_launches;
   rd(X, (size_t)T * D * 2);
   rd(W1, (size_t)r * D * 2);
   rd(W2, (size_t)2 * ng * r * 2);
+  if (T <= kRouterSmallT) wr(zpart, router_zpart_bytes(T, r));
   if (mask) wr(mask, (size_t)T * ng);
   if (logits) wr(logits, (size_t)T * ng * 2 * 4);
   if (maskbits) wr(maskbits, (size_t)ng * words(T) * 4);
@@ -333,10 +334,17 @@ void router_reorder_case(int T, int D, int r, int ng, bool mask_out) {
 void router_case(int T, int D, int r, int ng, bool logits) {
   Buf X((size_t)T * D * 2), W1((size_t)r * D * 2), W2((size_t)2 * ng * r * 2), mask((size_t)T * ng),
       lg((size_t)T * ng * 2 * 4);
+  const size_t need = wide_router_workspace_size(T, r);
+  Buf ws(need);
   EXPECT(wide_router_forward(X.p, W1.p, W2.p, T, D, r, ng, WIDE_ACT_SILU, WIDE_BF16,
-                             (uint8_t*)mask.p, logits ? (float*)lg.p : nullptr, nullptr) == WIDE_OK);
+                             (uint8_t*)mask.p, logits ? (float*)lg.p : nullptr,
+                             need ? ws.p : nullptr, need, nullptr) == WIDE_OK);
+  if (need > 0)
+    EXPECT(wide_router_forward(X.p, W1.p, W2.p, T, D, r, ng, WIDE_ACT_SILU, WIDE_BF16,
+                               (uint8_t*)mask.p, nullptr, ws.p, need - 1,
+                               nullptr) == WIDE_ERR_WORKSPACE);
   EXPECT(wide_router_forward(X.p, W1.p, W2.p, T, D, 24, ng, WIDE_ACT_SILU, WIDE_BF16,
-                             (uint8_t*)mask.p, nullptr, nullptr) == WIDE_ERR_UNSUPPORTED);
+                             (uint8_t*)mask.p, nullptr, ws.p, need, nullptr) == WIDE_ERR_UNSUPPORTED);
 }
 }  // namespace
 
@@ -369,9 +377,13 @@ int main() {
   router_case(100, 256, 32, 7, true);
   router_case(1, 512, 16, 40, false);
   router_case(0, 64, 64, 3, false);
+  router_case(16, 4096, 64, 112, true);
+  router_case(17, 4096, 32, 112, false);
   router_reorder_case(1000, 256, 32, 37, true);
   router_reorder_case(33, 64, 16, 1, false);
   router_reorder_case(0, 64, 16, 5, false);
+  router_reorder_case(16, 256, 64, 9, true);
+  router_reorder_case(1, 4096, 32, 112, false);
   // rejected arguments: nothing launched, a message set
   const int before = g_launches;
   std::vector<uint8_t> small(4096);

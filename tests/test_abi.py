@@ -218,10 +218,11 @@ def test_gemm_workspace_size(lib):
 
 def router_call(lib, **kw):
     a = dict(X=FAKE, W1=FAKE, W2=FAKE, T=64, D=256, r=32, ng=8, act=_lib.WIDE_ACT_SILU,
-             dtype=_lib.WIDE_BF16, mask=FAKE, logits=None, stream=None)
+             dtype=_lib.WIDE_BF16, mask=FAKE, logits=None, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.wide_router_forward(a["X"], a["W1"], a["W2"], a["T"], a["D"], a["r"], a["ng"],
-                                   a["act"], a["dtype"], a["mask"], a["logits"], a["stream"])
+                                   a["act"], a["dtype"], a["mask"], a["logits"], a["ws"],
+                                   a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -248,6 +249,22 @@ def test_router_validation(lib, kw, status):
 
 def test_router_t0_is_a_no_op(lib):
     assert router_call(lib, T=0, X=None, mask=None) == _lib.WIDE_OK
+
+
+def test_router_workspace(lib):
+    # partial sums of the split first map: 8 slices x 16 token rows x r floats, for 1 <= T <= 16
+    for r in (16, 32, 64):
+        for T in (1, 7, 16):
+            assert lib.wide_router_workspace_size(T, r) == 8 * 16 * r * 4
+        for T in (0, 17, 16384, -1):
+            assert lib.wide_router_workspace_size(T, r) == 0
+    assert lib.wide_router_workspace_size(4, 24) == 0
+    need = 8 * 16 * 32 * 4
+    assert router_call(lib, T=16, ws=None) == _lib.WIDE_ERR_WORKSPACE
+    assert router_call(lib, T=1, ws=FAKE, ws_bytes=need - 1) == _lib.WIDE_ERR_WORKSPACE
+    assert router_call(lib, T=1, ws=FAKE + 16, ws_bytes=need) == _lib.WIDE_ERR_ALIGN
+    # T > 16 needs none (validation of such a call is covered above)
+    assert lib.wide_router_workspace_size(17, 32) == 0
 
 
 def attn_call(lib, fn, **kw):
@@ -390,6 +407,8 @@ def test_noalloc_rejects_before_any_hip_call(lib):
 def test_router_reorder_validation(lib):
     ws = lib.wide_router_reorder_workspace_size(1000, 112)
     assert ws == (112 * 32 * 4 + 255) // 256 * 256
+    # T <= 16: one bit word per group, then the first map's partial sums (sized for r = 64)
+    assert lib.wide_router_reorder_workspace_size(16, 112) == (112 * 4 + 255) // 256 * 256 + 8 * 16 * 64 * 4
     assert lib.wide_router_reorder_workspace_size(-1, 4) == 0
     base = [FAKE, FAKE, FAKE, 64, 256, 32, 8, _lib.WIDE_ACT_SILU, _lib.WIDE_BF16, 256, None, None,
             FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
