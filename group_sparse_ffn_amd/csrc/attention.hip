@@ -31,10 +31,11 @@
 //     straight from registers as the B operand.
 //   * V^T (per KV head, [dh, keys], zero past T) is built once per call by a
 //     transpose kernel, so the A operand of O^T reads 16 contiguous bytes.
-//   * K and V^T tiles (64 keys) go global -> registers -> LDS, double
-//     buffered: the loads of tile k+1 are in flight during the MFMAs of tile k.
-//     16-byte chunks are XOR-swizzled by row so that 16 lanes reading one chunk
-//     column hit distinct banks.
+//   * K and V^T tiles (64 keys) go global -> LDS with register-bypassing
+//     copies, double buffered: the copies of tile k+1 are in flight during
+//     the MFMAs of tile k. 16-byte chunks are XOR-swizzled by row so that 16
+//     lanes reading one chunk column hit distinct banks (each copying lane
+//     fetches the chunk that the swizzle puts at its position).
 //   * Level-2 skipping: a wave with no active query, or past its own last key
 //     tile, skips its MFMAs but joins every barrier.
 #include "common.h"
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     const uint16_t* __restrict__ Vt, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, int T, int Tpad, int Hq, int Hk, float scale_log2,
     uint16_t* __restrict__ O, int zero_inactive) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
   const int h = blockIdx.y;
   const int g = h / (Hq / Hk);  // KV head = routing group
   const int count = counts[g];
@@ -122,46 +123,41 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // copies: K tile 64 rows x 16 chunks, V^T tile 128 rows x 8 chunks; 4 + 4 per thread
-  u32x4 rk[4], rv[4];
+  // copies: register-bypassing global -> LDS copies of 1 KB per instruction
+  // (lane l writes 16 bytes at l * 16). K slot: 64 key rows of 256 bytes, 4
+  // rows per copy; V^T slot: 128 dim rows of 128 bytes, 8 rows per copy. Each
+  // lane fetches the logical chunk that the swizzle puts at its physical
+  // position. Every wave issues 4 + 4 of the 16 + 16 copies of a tile.
   const uint16_t* kbase = K + (size_t)g * kAtDh;
   const uint16_t* vbase = Vt + (size_t)g * kAtDh * Tpad;
-  auto gload = [&](int kt) {
+  auto issue_k = [&](int kt, int slot) {
+    uint8_t* sk = smem + slot * kStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = i * kAtThreads + tid;
-      const int key = min(kt * kAtBK + idx / 16, T - 1);  // rows past T: never valid keys
-      rk[i] = at_ld(kbase + (size_t)key * ldk + (idx % 16) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = i * kAtThreads + tid;
-      rv[i] = at_ld(vbase + (size_t)(idx / 8) * Tpad + kt * kAtBK + (idx % 8) * 8);
+      const int blk = wave + 4 * i;
+      const int row = 4 * blk + (lane >> 4);
+      const int key = min(kt * kAtBK + row, T - 1);  // rows past T: never valid keys
+      const int c = (lane & 15) ^ kswz(row);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (size_t)key * ldk + c * 8),
+                                       (void*)(sk + blk * 1024), 16, 0, 0);
     }
   };
-  auto swrite = [&](int buf) {
-    uint8_t* sk = smem + buf * kStage;
-    uint8_t* sv = sk + kKBytes;
+  auto issue_v = [&](int kt, int slot) {
+    uint8_t* sv = smem + slot * kStage + kKBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = i * kAtThreads + tid;
-      const int row = idx / 16, c = idx % 16;
-      *(u32x4*)(sk + row * 256 + ((c ^ kswz(row)) << 4)) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = i * kAtThreads + tid;
-      const int row = idx / 8, c = idx % 8;
-      *(u32x4*)(sv + row * 128 + ((c ^ vswz(row)) << 4)) = rv[i];
+      const int blk = wave + 4 * i;
+      const int row = 8 * blk + (lane >> 3);
+      const int c = (lane & 7) ^ vswz(row);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)row * Tpad + kt * kAtBK + c * 8),
+                                       (void*)(sv + blk * 1024), 16, 0, 0);
     }
   };
 
   const int krow0 = key_of_row(q);
-  auto compute = [&](int buf, int kt) {
-    const uint8_t* sk = smem + buf * kStage;
-    const uint8_t* sv = sk + kKBytes;
-    // S^T for the tile's two 32-key blocks
-    f32x16 s[2];
+  // S^T of key tile in K slot `slot` (its two 32-key blocks)
+  auto s_mfma = [&](f32x16 (&s)[2], int slot) {
+    const uint8_t* sk = smem + slot * kStage;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -175,12 +171,16 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[b], 0, 0, 0);
       }
     }
-    // online softmax in base 2; element e of block b is key
-    // kt*64 + 32 b + 16 (e / 8) + 8 hh + e % 8. Keys past a query's position
-    // get -inf (only on the wave's diagonal tiles).
-    // The maximum is taken on the raw scores (the scale is positive, so the
-    // order is the same) and the scale and the subtraction of the maximum meet
-    // in one fma inside exp2: p = 2^(s c - m c), c = log2(e) / sqrt(dh).
+  };
+  // online softmax of tile kt's scores s: P (bf16 MFMA operands) and the
+  // rescale factor of O; the running max and sum are updated
+  auto mask_diag = [&](f32x16 (&s)[2], int kt) {
+    // element e of block b is key kt*64 + 32 b + 16 (e / 8) + 8 hh + e % 8.
+    // Keys past a query's position get -inf (only on the wave's diagonal
+    // tiles). The maximum is taken on the raw scores (the scale is positive,
+    // so the order is the same) and the scale and the subtraction of the
+    // maximum meet in one fma inside exp2: p = 2^(s c - m c), c = log2(e) /
+    // sqrt(dh).
     if (kt >= wave_full) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -190,12 +190,17 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
           s[b][e] = key <= qpos ? s[b][e] : -INFINITY;
         }
     }
-    float mt = -INFINITY;
+  };
+  auto softmax_p = [&](f32x16 (&s)[2], bf16x8 (&pf)[2][2], float& alpha) {
+    // the row maximum as a tree (a chain of 32 dependent maxima otherwise)
+    float mx[16];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int e = 0; e < 16; ++e) mx[e] = fmaxf(s[0][e], s[1][e]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[b][e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+      for (int e = 0; e < w; ++e) mx[e] = fmaxf(mx[e], mx[e + w]);
+    const float mt = fmaxf(mx[0], __shfl_xor(mx[0], 32));
     const float m_new = fmaxf(m_run, mt);  // raw-score units
     // While no key is valid the running max is -inf: the exponent base 0
     // then gives exp2(-inf) = 0 for every P and for alpha, never NaN (O and l
@@ -203,9 +208,8 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     const float mc = (m_new == -INFINITY ? 0.0f : m_new) * scale_log2;
     // exactly 1 when the maximum did not move (the fma would leave m c's
     // rounding error in the exponent)
-    const float alpha = m_run == m_new ? 1.0f : __builtin_amdgcn_exp2f(fmaf(m_run, scale_log2, -mc));
+    alpha = m_run == m_new ? 1.0f : __builtin_amdgcn_exp2f(fmaf(m_run, scale_log2, -mc));
     float psum = 0.0f;
-    bf16x8 pf[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -223,13 +227,17 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // the running max of most queries stops moving after the first tiles:
-    // rescale only when some lane's max changed
+  };
+  // O^T = alpha O^T + V^T P^T with the V^T tile in V slot `slot`; the
+  // running max of most queries stops moving after the first tiles, so the
+  // rescale runs only when some lane's max changed
+  auto o_update = [&](const bf16x8 (&pf)[2][2], float alpha, int slot) {
     if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int j = 0; j < kAtDh / 32; ++j) o[j] *= alpha;
     }
     // O^T += V^T P^T: A = V^T rows (dims), B = P^T (k-step (b, c): keys 32 b + 16 c + 8 hh ..)
+    const uint8_t* sv = smem + slot * kStage + kKBytes;
 #pragma unroll
     for (int j = 0; j < kAtDh / 32; ++j) {
       const int vrow = 32 * j + q;
@@ -245,18 +253,44 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     }
   };
 
-  // K/V mainloop: loads of tile kt+1 in flight during the MFMAs of tile kt.
-  // (The last iteration reloads its own tile into the idle buffer, so no load
-  // sits under a condition.)
-  gload(0);
-  swrite(0);
+  // K/V mainloop, software-pipelined over key tiles: iteration i runs the
+  // scores of tile i + 1 on the matrix core while the softmax of tile i runs
+  // on the VALU (independent instructions of one wave), then O += V_i P_i.
+  // Two K slots and two V slots: tile m's K and V live in slot m % 2. After
+  // the barrier that ends iteration i, K_{i+1} (its scores are done) and V_i
+  // are free, and K_{i+3} and V_{i+2} are requested into them; both are used
+  // an iteration later, after the next end-of-iteration wait and barrier.
+  // Tile indices past the last are clamped (a valid tile reloaded into a free
+  // slot), so no copy sits under a condition.
+  // K/V mainloop: tile i lives in slot i % 2; after the barrier that ends
+  // iteration i, tile i + 2 is requested into that slot (used an iteration
+  // later, after the next end-of-iteration wait and barrier). Tile indices
+  // past the last are clamped (a valid tile reloaded into a free slot), so
+  // no copy sits under a condition.
+  const int last = nkt - 1;
+  issue_k(0, 0);
+  issue_v(0, 0);
+  issue_k(min(1, last), 1);
+  issue_v(min(1, last), 1);
+  __builtin_amdgcn_s_waitcnt(WIDE_VMCNT(0));  // this wave's copies have landed
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    gload(min(kt + 1, nkt - 1));
-    if (kt < wave_nkt) compute(kt & 1, kt);
-    swrite((kt + 1) & 1);
+  for (int i = 0; i < nkt; ++i) {
+    if (i < wave_nkt) {
+      f32x16 sc[2];
+      bf16x8 pf[2][2];
+      float alpha;
+      s_mfma(sc, i & 1);
+      mask_diag(sc, i);
+      softmax_p(sc, pf, alpha);
+      o_update(pf, alpha, i & 1);
+    }
+    __builtin_amdgcn_s_waitcnt(WIDE_VMCNT(0));  // tile i + 1 (requested after barrier i - 1)
     __syncthreads();
+    issue_k(min(i + 2, last), i & 1);
+    issue_v(min(i + 2, last), i & 1);
   }
+  __builtin_amdgcn_s_waitcnt(WIDE_VMCNT(0));  // no copy outlives the loop
+  __syncthreads();  // the epilogue reuses the slots
 
   // epilogue: O = O^T / l, staged in LDS as [row][dims] (16-byte chunks
   // swizzled by row), then whole 256-byte rows go to their tokens

@@ -10,6 +10,9 @@ namespace wide {
 
 // ---------------------------------------------------------------- device helpers
 
+// s_waitcnt immediate that waits only for the vector-memory counter to reach n.
+#define WIDE_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -35,8 +35,6 @@ constexpr int kRowBytes = 128;  // one LDS row holds 64 bf16 of K
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// s_waitcnt immediate that waits only for the vector-memory counter to reach n.
-#define WIDE_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 template <int TP_, int TQ_, int WP_, int WQ_>
 struct Shape {
