@@ -48,7 +48,6 @@ namespace wide {
 namespace {
 
 constexpr int kUnroll = 8;      // gate/up loads in flight per lane
-constexpr int kDownUnroll = 8;  // down loads in flight per lane
 constexpr int kMaxGroups = 4096;  // d_ff / 16
 constexpr int kDecodeSmallT = 4;  // largest T that uses 8-channel gate/up units
 constexpr int kValuMaxT = 2;      // largest T of the contiguous VALU kernels
@@ -598,7 +597,6 @@ __global__ __launch_bounds__(kSkThreads) void decode_down_splitk_kernel(
   constexpr int kScale = PACKED ? 16 : 1;
   // token columns past T - 1 repeat token T - 1 (never stored, see gate/up)
   const uint16_t* ph = H + (size_t)min(tok, T - 1) * d_ff + koff;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
   f32x4 acc[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
