@@ -771,7 +771,7 @@ def bench_decode_cell(torch, wide, w, inp, steps: int, copies: int = 8, dense: b
 def bench_configs(torch, wide, dg, steps: int):
     """Every workload of the measured set beside the headline: the tiny fp32
     SwiGLU, the Llama3.2-3B-shaped G x sparsity sweep (every G at 50% for
-    T = 8192 and T = 1, every sparsity level at G = 128), and the
+    T = 8192, 2048 and 1, every sparsity level at G = 128), and the
     Qwen3-14B-shaped skewed masks with the all-ones and all-zero limits."""
     import dataclasses
     out = {}
@@ -788,11 +788,11 @@ def bench_configs(torch, wide, dg, steps: int):
     del call, d
     # Llama3.2-3B sweep
     cells = {(c.G, round((1 - c.density) * 100), c.T): c for c in dg.llama3b_sweep_cells()}
-    want = [(G, 50, T) for T in (8192, 1) for G in (16, 32, 64, 128, 256, 512)]
+    want = [(G, 50, T) for T in (8192, 2048, 1) for G in (16, 32, 64, 128, 256, 512)]
     want += [(128, s, 8192) for s in (10, 25, 70)]
     base = cells[(128, 50, 8192)]
     wts = dg.make_inputs(base, T=1)  # weights depend only on the workload id
-    xs = {T: dg.make_inputs(base, T=T, weights=False)["X"] for T in (8192, 1)}
+    xs = {T: dg.make_inputs(base, T=T, weights=False)["X"] for T in (8192, 2048, 1)}
     sweep = []
     for key in want:
         c = cells[key]
@@ -1361,7 +1361,8 @@ def summarize_baselines(directory: str, command: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; with --summarize: the profile run's, 5)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -1376,8 +1377,10 @@ def main():
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.command, args.steps)
+        summarize(args.summarize, args.command, 5 if args.steps is None else args.steps)
         return
+    if args.steps is None:
+        args.steps = 20
     if args.summarize_baselines:
         summarize_baselines(args.summarize_baselines, args.command)
         return
