@@ -45,22 +45,39 @@ namespace wide {
 namespace {
 
 constexpr int kAtBQ = 128;   // queries per workgroup (4 waves x 32)
-constexpr int kAtBK = 64;    // keys per tile
+// keys per tile (a multiple of 32). 32-key tiles (160 registers, 32 KB of
+// LDS: three workgroups per CU) measured 1.70 against 1.65 ms at the
+// Llama3.1-8B shape, so 64 it is.
+constexpr int kAtBK = 64;
+constexpr int kAtNB = kAtBK / 32;  // 32-key MFMA blocks per tile
+constexpr int kAtTpadAlign = 64;   // V^T rows are padded to multiples of 64 keys
 constexpr int kAtDh = 128;   // head dimension
 constexpr int kAtThreads = 256;
-constexpr int kKBytes = kAtBK * kAtDh * 2;  // K tile [64 keys][128]: 256 B rows
-constexpr int kVBytes = kAtDh * kAtBK * 2;  // V^T tile [128][64 keys]: 128 B rows
+constexpr int kKBytes = kAtBK * kAtDh * 2;  // K tile [keys][128]: 256 B rows
+constexpr int kVBytes = kAtDh * kAtBK * 2;  // V^T tile [128][keys]: kVRow B rows
+constexpr int kVRow = kAtBK * 2;
+constexpr int kVChunks = kVRow / 16;        // 16-byte chunks per V^T row
 constexpr int kStage = kKBytes + kVBytes;
+// workgroups per CU: the LDS of two stages and the registers allow three with
+// 32-key tiles, two with 64-key tiles
+constexpr int kAtMinBlocks = kAtBK == 32 ? 3 : 2;
+static_assert(kAtBK % 32 == 0 && kAtTpadAlign % kAtBK == 0, "key tiles");
+static_assert(2 * kStage >= 128 * 256, "the epilogue stages 128 rows of 256 bytes in the slots");
 
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
-__device__ __forceinline__ int vswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// V^T rows of 8 chunks (64 keys): 16 consecutive rows read one chunk column
+// on distinct banks with (row & 7) ^ ((row >> 3) & 1); rows of 4 chunks (32
+// keys) with (row >> 2) & 3 (rows r and r + 4 share a 256-byte bank line)
+__device__ __forceinline__ int vswz(int row) {
+  return kVChunks == 8 ? (row & 7) ^ ((row >> 3) & 1) : (row >> 2) & 3;
+}
 // key row read by MFMA row i of a 32-key block: bits 2 and 3 of i swapped
 __device__ __forceinline__ int key_of_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 __device__ __forceinline__ u32x4 at_ld(const uint16_t* p) { return *(const u32x4*)p; }
 
 
-__global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
+__global__ __launch_bounds__(kAtThreads, kAtMinBlocks) void attention_prefill_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, int T, int Tpad, int Hq, int Hk, float scale_log2,
@@ -124,16 +141,16 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
   float m_run = -INFINITY, l_run = 0.0f;
 
   // copies: register-bypassing global -> LDS copies of 1 KB per instruction
-  // (lane l writes 16 bytes at l * 16). K slot: 64 key rows of 256 bytes, 4
-  // rows per copy; V^T slot: 128 dim rows of 128 bytes, 8 rows per copy. Each
-  // lane fetches the logical chunk that the swizzle puts at its physical
-  // position. Every wave issues 4 + 4 of the 16 + 16 copies of a tile.
+  // (lane l writes 16 bytes at l * 16). K slot: kAtBK key rows of 256 bytes,
+  // 4 rows per copy; V^T slot: 128 dim rows of kVRow bytes. Each lane fetches
+  // the logical chunk that the swizzle puts at its physical position. The
+  // four waves share a tile's copies.
   const uint16_t* kbase = K + (size_t)g * kAtDh;
   const uint16_t* vbase = Vt + (size_t)g * kAtDh * Tpad;
   auto issue_k = [&](int kt, int slot) {
     uint8_t* sk = smem + slot * kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKBytes / 4096; ++i) {
       const int blk = wave + 4 * i;
       const int row = 4 * blk + (lane >> 4);
       const int key = min(kt * kAtBK + row, T - 1);  // rows past T: never valid keys
@@ -145,21 +162,21 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
   auto issue_v = [&](int kt, int slot) {
     uint8_t* sv = smem + slot * kStage + kKBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kVBytes / 4096; ++i) {
       const int blk = wave + 4 * i;
-      const int row = 8 * blk + (lane >> 3);
-      const int c = (lane & 7) ^ vswz(row);
+      const int row = (64 / kVChunks) * blk + lane / kVChunks;
+      const int c = (lane % kVChunks) ^ vswz(row);
       __builtin_amdgcn_global_load_lds((const void*)(vbase + (size_t)row * Tpad + kt * kAtBK + c * 8),
                                        (void*)(sv + blk * 1024), 16, 0, 0);
     }
   };
 
   const int krow0 = key_of_row(q);
-  // S^T of key tile in K slot `slot` (its two 32-key blocks)
-  auto s_mfma = [&](f32x16 (&s)[2], int slot) {
+  // S^T of key tile in K slot `slot` (its 32-key blocks)
+  auto s_mfma = [&](f32x16 (&s)[kAtNB], int slot) {
     const uint8_t* sk = smem + slot * kStage;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kAtNB; ++b) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[b][e] = 0.0f;
       const int krow = 32 * b + krow0;
@@ -174,8 +191,8 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
   };
   // online softmax of tile kt's scores s: P (bf16 MFMA operands) and the
   // rescale factor of O; the running max and sum are updated
-  auto mask_diag = [&](f32x16 (&s)[2], int kt) {
-    // element e of block b is key kt*64 + 32 b + 16 (e / 8) + 8 hh + e % 8.
+  auto mask_diag = [&](f32x16 (&s)[kAtNB], int kt) {
+    // element e of block b is key kt*kAtBK + 32 b + 16 (e / 8) + 8 hh + e % 8.
     // Keys past a query's position get -inf (only on the wave's diagonal
     // tiles). The maximum is taken on the raw scores (the scale is positive,
     // so the order is the same) and the scale and the subtraction of the
@@ -183,7 +200,7 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     // sqrt(dh).
     if (kt >= wave_full) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < kAtNB; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kt * kAtBK + 32 * b + 16 * (e >> 3) + 8 * hh + (e & 7);
@@ -191,11 +208,15 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
         }
     }
   };
-  auto softmax_p = [&](f32x16 (&s)[2], bf16x8 (&pf)[2][2], float& alpha) {
-    // the row maximum as a tree (a chain of 32 dependent maxima otherwise)
+  auto softmax_p = [&](f32x16 (&s)[kAtNB], bf16x8 (&pf)[kAtNB][2], float& alpha) {
+    // the row maximum as a tree (a chain of dependent maxima otherwise)
     float mx[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx[e] = fmaxf(s[0][e], s[1][e]);
+    for (int e = 0; e < 16; ++e) {
+      mx[e] = s[0][e];
+#pragma unroll
+      for (int b = 1; b < kAtNB; ++b) mx[e] = fmaxf(mx[e], s[b][e]);
+    }
 #pragma unroll
     for (int w = 8; w >= 1; w /= 2)
 #pragma unroll
@@ -211,7 +232,7 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     alpha = m_run == m_new ? 1.0f : __builtin_amdgcn_exp2f(fmaf(m_run, scale_log2, -mc));
     float psum = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kAtNB; ++b)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         uint32_t w[4];
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
   // O^T = alpha O^T + V^T P^T with the V^T tile in V slot `slot`; the
   // running max of most queries stops moving after the first tiles, so the
   // rescale runs only when some lane's max changed
-  auto o_update = [&](const bf16x8 (&pf)[2][2], float alpha, int slot) {
+  auto o_update = [&](const bf16x8 (&pf)[kAtNB][2], float alpha, int slot) {
     if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int j = 0; j < kAtDh / 32; ++j) o[j] *= alpha;
@@ -241,10 +262,10 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < kAtDh / 32; ++j) {
       const int vrow = 32 * j + q;
-      const uint8_t* pv = sv + vrow * 128;
+      const uint8_t* pv = sv + vrow * kVRow;
       const int sw = vswz(vrow);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < kAtNB; ++b)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x8 a = *(const bf16x8*)(pv + (((4 * b + 2 * c + hh) ^ sw) << 4));
@@ -253,15 +274,6 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
     }
   };
 
-  // K/V mainloop, software-pipelined over key tiles: iteration i runs the
-  // scores of tile i + 1 on the matrix core while the softmax of tile i runs
-  // on the VALU (independent instructions of one wave), then O += V_i P_i.
-  // Two K slots and two V slots: tile m's K and V live in slot m % 2. After
-  // the barrier that ends iteration i, K_{i+1} (its scores are done) and V_i
-  // are free, and K_{i+3} and V_{i+2} are requested into them; both are used
-  // an iteration later, after the next end-of-iteration wait and barrier.
-  // Tile indices past the last are clamped (a valid tile reloaded into a free
-  // slot), so no copy sits under a condition.
   // K/V mainloop: tile i lives in slot i % 2; after the barrier that ends
   // iteration i, tile i + 2 is requested into that slot (used an iteration
   // later, after the next end-of-iteration wait and barrier). Tile indices
@@ -276,8 +288,8 @@ __global__ __launch_bounds__(kAtThreads, 2) void attention_prefill_kernel(
   __syncthreads();
   for (int i = 0; i < nkt; ++i) {
     if (i < wave_nkt) {
-      f32x16 sc[2];
-      bf16x8 pf[2][2];
+      f32x16 sc[kAtNB];
+      bf16x8 pf[kAtNB][2];
       float alpha;
       s_mfma(sc, i & 1);
       mask_diag(sc, i);
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(256) void attention_vt_kernel(const uint16_t* __res
 
 }  // namespace
 
-int64_t attention_tpad(int64_t T) { return (T + kAtBK - 1) / kAtBK * kAtBK; }
+int64_t attention_tpad(int64_t T) { return (T + kAtTpadAlign - 1) / kAtTpadAlign * kAtTpadAlign; }
 
 hipError_t launch_attention_prefill_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                          const int32_t* perm, const int32_t* counts, int T, int Hq,
