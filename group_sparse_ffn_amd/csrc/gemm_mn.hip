@@ -23,9 +23,10 @@
 // full (TT active positions), at most one boundary tile (fewer), and tiles
 // past its count (only zeros to write, and only with zero_inactive). Every
 // workgroup scans the active counts and takes, on its XCD (workgroup ids go
-// to the XCDs in turn), first an eighth of all full tiles in group-major
-// order (the tiles that run at the same time on one XCD share their weight
-// rows in its L2), then an eighth of the boundary tiles, then an eighth of
+// to the XCDs in turn), first an eighth of all full tiles in the sparse
+// super-tile order below (the tiles that run at the same time on one XCD
+// share the weight rows of two blocks in its L2, and row lists in token
+// order share activation rows), then an eighth of the boundary tiles, then an eighth of
 // the tiles past the counts. The last round of the grid is then filled by
 // the short boundary tiles, workgroups with no work are dispatched after all
 // of the real ones, and skewed counts spread evenly over the XCDs.
@@ -86,31 +87,58 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // (about a third of the fabric traffic of 32 tiles of one block). Measured
 // against the block-major order: Llama3.2-3B T = 8192 gate/up 0.738 -> 0.658
 // ms at G = 16 and 0.737 -> 0.650 ms at G = 32; at the Llama3.1-8B prefill
-// shape 3.19 -> 3.01 ms. The same order for the sparse tiles (whose row lists
-// are in token order) halves their fabric traffic but measured 1.662 -> 1.706
-// ms at the Llama3.1-8B shape, so those keep the group-major order below.
+// shape 3.19 -> 3.01 ms. The same 8 x 4 order for the sparse tiles (whose row
+// lists are in token order) halves their fabric traffic but measured 1.662 ->
+// 1.706 ms at the Llama3.1-8B shape; they use the narrower super-tiles below.
 constexpr int kSuperBlocks = 8, kSuperTiles = 4;
+
+// The sparse tiles' full tiles go in super-tiles of 2 blocks x 16 token tiles
+// (super-row r: blocks 2r, 2r + 1; column q: their full tiles 16q .. 16q + 15),
+// listed super-row by super-row, column by column, block by block, tile by
+// tile, each XCD taking a contiguous eighth of that list. Measured against
+// block-major (32 tiles of one block per XCD round): Llama3.1-8B gate/up
+// 1.695 -> 1.656 ms, Llama3.2-3B T = 2048 0.147 -> 0.142 ms, G = 64 0.478 ->
+// 0.487 ms, the other shapes within noise; 4 x 8 measured 1.666 ms and the
+// 8 x 4 of the dense form 1.706 ms.
+constexpr int kSparseSuperBlocks = 2, kSparseSuperTiles = 16;
+
+// Full tiles of a block with f full tiles that fall in sparse super-tile
+// column q.
+__device__ __forceinline__ int in_column(int f, int q) {
+  return min(max(f - kSparseSuperTiles * q, 0), kSparseSuperTiles);
+}
 
 // This workgroup's tile in the order above (blk, tile index and the group's
 // active count), or false when it has none. Every wave computes it on its
-// own, with no barrier: lane l scans a contiguous run of blocks, the run that
-// holds the wanted index is found by a ballot, and its lane's answer is read
-// by every lane.
+// own, with no barrier: lane l scans a contiguous run of blocks (boundary and
+// past-count tiles) and of sparse super-rows (full tiles), the run that holds
+// the wanted index is found by a ballot, and its lane's answer is read by
+// every lane.
 template <int TT>
 __device__ __forceinline__ bool ordered_tile(const int32_t* __restrict__ counts, int nblk, int nct,
                                              int ntok_tiles, bool with_zero, int& blk, int& tile,
                                              int& count) {
+  constexpr int SM = kSparseSuperBlocks, SN = kSparseSuperTiles;
   const int lane = (int)(threadIdx.x & 63);
   const int per = (nblk + 63) / 64;
   const int b0 = lane * per;
-  int sf = 0, sb = 0, sz = 0;
+  int sb = 0, sz = 0;
   for (int k = 0; k < per && b0 + k < nblk; ++k) {
     const int c = counts[(b0 + k) / nct];
     const int f = c / TT, b = c % TT != 0;
-    sf += f;
     sb += b;
     sz += ntok_tiles - f - b;
   }
+  const int nsr = (nblk + SM - 1) / SM;
+  const int rper = (nsr + 63) / 64;
+  const int r0 = lane * rper;
+  int sf = 0;
+  for (int k = 0; k < rper && r0 + k < nsr; ++k)
+#pragma unroll
+    for (int m = 0; m < SM; ++m) {
+      const int b = (r0 + k) * SM + m;
+      if (b < nblk) sf += counts[b / nct] / TT;
+    }
   const int pf = wave_incl_scan(sf), pb = wave_incl_scan(sb), pz = wave_incl_scan(sz);
   const int F = __builtin_amdgcn_readlane(pf, 63);
   const int B = __builtin_amdgcn_readlane(pb, 63);
@@ -140,17 +168,55 @@ __device__ __forceinline__ bool ordered_tile(const int32_t* __restrict__ counts,
   const int owner = (int)__builtin_ctzll(own);
   int rb = 0, rt = 0, rc = 0;
   if (lane == owner) {
-    for (int k = 0; k < per && b0 + k < nblk; ++k) {
-      const int c = counts[(b0 + k) / nct];
-      const int f = c / TT, b = c % TT != 0;
-      const int n = cls == 0 ? f : cls == 1 ? b : ntok_tiles - f - b;
-      if (i < acc + n) {
-        rb = b0 + k;
-        rt = cls == 0 ? i - acc : cls == 1 ? f : f + b + (i - acc);
-        rc = c;
-        break;
+    if (cls == 0) {
+      for (int k = 0; k < rper && r0 + k < nsr; ++k) {
+        const int r = r0 + k;
+        int f[SM], c[SM], tot = 0;
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+          const int b = r * SM + m;
+          c[m] = b < nblk ? counts[b / nct] : 0;
+          f[m] = c[m] / TT;
+          tot += f[m];
+        }
+        if (i < acc + tot) {
+          int ii = i - acc;
+          for (int q = 0; q * SN < ntok_tiles; ++q) {
+            int cq = 0;
+#pragma unroll
+            for (int m = 0; m < SM; ++m) cq += in_column(f[m], q);
+            if (ii < cq) {
+#pragma unroll
+              for (int m = 0; m < SM; ++m) {
+                const int n = in_column(f[m], q);
+                if (ii >= 0 && ii < n) {
+                  rb = r * SM + m;
+                  rt = q * SN + ii;
+                  rc = c[m];
+                }
+                ii -= n;
+              }
+              break;
+            }
+            ii -= cq;
+          }
+          break;
+        }
+        acc += tot;
       }
-      acc += n;
+    } else {
+      for (int k = 0; k < per && b0 + k < nblk; ++k) {
+        const int c = counts[(b0 + k) / nct];
+        const int f = c / TT, b = c % TT != 0;
+        const int n = cls == 1 ? b : ntok_tiles - f - b;
+        if (i < acc + n) {
+          rb = b0 + k;
+          rt = cls == 1 ? f : f + b + (i - acc);
+          rc = c;
+          break;
+        }
+        acc += n;
+      }
     }
   }
   blk = __builtin_amdgcn_readlane(rb, owner);
