@@ -43,8 +43,8 @@ namespace {
 
 constexpr int kCopyWaves = 4;
 
-// TT: positions of the reordered row list per tile, 256 for large problems or
-// 128 (with channel blocks of 64 or more) when 256-tiles would leave CUs idle.
+// TT: positions of the reordered row list per tile, 256 or 128 (with channel
+// blocks of 64 or more); mn_token_tile (SwiGLU) and plain_mn_tile choose.
 template <int CW, bool SWIGLU, int TT = 256>
 struct MnShape {
   // a 16-channel plain block is padded to one 32-row fragment (zero rows)
@@ -461,11 +461,8 @@ WIDE_MN_KERNEL(gate_up_bf16_kernel_16, 16, true, 256)
 WIDE_MN_KERNEL(gate_up_bf16_kernel_128_t128, 128, true, 128)
 WIDE_MN_KERNEL(gate_up_bf16_kernel_64_t128, 64, true, 128)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_256, 256, false, 256)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_128, 128, false, 256)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_64, 64, false, 256)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_32, 32, false, 256)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_16, 16, false, 256)
-WIDE_MN_KERNEL(gemm_mn_bf16_kernel_256_t128, 256, false, 128)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_128_t128, 128, false, 128)
 WIDE_MN_KERNEL(gemm_mn_bf16_kernel_64_t128, 64, false, 128)
 #undef WIDE_MN_KERNEL
@@ -485,19 +482,43 @@ __global__ __launch_bounds__(512, 1) void gate_up_dense_bf16_kernel(
 typedef void (*MnKernel)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*,
                          const int32_t*, int, int, int, int, uint16_t*, int, int, int, int);
 
-// 128-position tiles when the 256-position grid (before level-0 exits) would
-// leave CUs idle: fewer than 1024 workgroups (about two active per CU at 50%
-// masks) for an A side of up to 128 rows, fewer than 256 for a 256-row A side
-// (SwiGLU with 128 channels, plain with 256), whose 128-position tile reads
-// four A fragments per B fragment from LDS. They need channel blocks of at
-// least 64. Measured at 50% masks: N axis (128 channels) 2048^3 46 -> 39 us,
-// 4096^3 128 -> 119 us; dynamic depth (256 channels) 2048^3 54 -> 43 us, but
-// 4096^3 100 -> 127 us.
-int mn_token_tile(int M, int N, int G, int CW, bool swiglu) {
+// Token tile of the SwiGLU gate/up: 128 positions when the 256-position grid
+// (before level-0 exits) would leave CUs idle, i.e. fewer than 256 workgroups
+// with 128-channel blocks (a 256-row A side) or fewer than 1024 with 64-channel
+// blocks; channel blocks under 64 always take 256 positions.
+int mn_token_tile(int M, int N, int G, int CW) {
   const long long t256 = (long long)(N / G) * (G / CW) * ((M + 255) / 256);
-  const int tp = swiglu ? 2 * CW : CW;
   if (CW < 64) return 256;
-  return t256 < (tp >= 256 ? 256 : 1024) ? 128 : 256;
+  return t256 < (2 * CW >= 256 ? 256 : 1024) ? 128 : 256;
+}
+
+// Tile of the plain GEMM (channel block cw x token tile tt). Measured on
+// MI355X over square shapes 2048-8192 and the Llama3.1-8B W_q shapes, 50%
+// masks, every shape timed with each tile in one process (outputs bit-equal):
+//   * 256 x 256 wins wherever G allows it and the full grid has at least one
+//     such tile per CU (4096^3 N axis G = 512: 97.9 us against 117.8 for
+//     128 x 128), even when half its tiles are idle;
+//   * otherwise 128-position tiles win at every size: a 128-channel block with
+//     128 positions against 256 positions, 120 against 137 us at 4096^3 and
+//     703 against 762 us at 8192^3 (G = 128); at 3072^3 on the M axis 53
+//     against 62-75 us for the 256-wide tiles;
+//   * where the full grid of 128 x 128 tiles is at most one tile per CU (about
+//     half of them active at 50% masks), 64-channel blocks double the
+//     workgroups: 2048^3 M axis 36.4 against 37.8 (43.9 with 256 x 128), N axis
+//     37.2 against 40.0 us.
+void plain_mn_tile(int M, int N, int G, int* cw, int* tt) {
+  const long long rows128 = (M + 127) / 128, rows256 = (M + 255) / 256;
+  const int ncu = 256;  // MI355X compute units
+  if (G % 256 == 0 && (long long)(N / 256) * rows256 >= ncu) {
+    *cw = 256;
+    *tt = 256;
+  } else if (G % 64 == 0) {
+    *cw = G % 128 == 0 && (long long)(N / 128) * rows128 > ncu ? 128 : 64;
+    *tt = 128;
+  } else {
+    *cw = G % 32 == 0 ? 32 : 16;
+    *tt = 256;
+  }
 }
 
 hipError_t launch_mn(MnKernel kernel, int CW, int TT, const uint16_t* A, const uint16_t* B,
@@ -529,7 +550,7 @@ hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint
     return hipGetLastError();
   }
   const int cw = G % 128 == 0 ? 128 : G % 64 == 0 ? 64 : G % 32 == 0 ? 32 : 16;
-  const int tt = mn_token_tile(T, d_ff, G, cw, true);
+  const int tt = mn_token_tile(T, d_ff, G, cw);
   MnKernel k = tt == 128 ? (cw == 128 ? gate_up_bf16_kernel_128_t128 : gate_up_bf16_kernel_64_t128)
                : cw == 128 ? gate_up_bf16_kernel_128
                : cw == 64  ? gate_up_bf16_kernel_64
@@ -542,14 +563,11 @@ hipError_t launch_gemm_mn_bf16(const uint16_t* A, const uint16_t* B, const int32
                                const int32_t* counts, int M, int K, int N, int G, uint16_t* C,
                                hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const int cw = G % 256 == 0 ? 256 : G % 128 == 0 ? 128 : G % 64 == 0 ? 64 : G % 32 == 0 ? 32 : 16;
-  const int tt = mn_token_tile(M, N, G, cw, false);
-  MnKernel k = tt == 128 ? (cw == 256   ? gemm_mn_bf16_kernel_256_t128
-                            : cw == 128 ? gemm_mn_bf16_kernel_128_t128
-                                        : gemm_mn_bf16_kernel_64_t128)
-               : cw == 256 ? gemm_mn_bf16_kernel_256
-               : cw == 128 ? gemm_mn_bf16_kernel_128
-               : cw == 64  ? gemm_mn_bf16_kernel_64
+  int cw, tt;
+  plain_mn_tile(M, N, G, &cw, &tt);
+  MnKernel k = cw == 256   ? gemm_mn_bf16_kernel_256
+               : cw == 128 ? gemm_mn_bf16_kernel_128_t128
+               : cw == 64  ? gemm_mn_bf16_kernel_64_t128
                : cw == 32  ? gemm_mn_bf16_kernel_32
                            : gemm_mn_bf16_kernel_16;
   return launch_mn(k, cw, tt, A, B, nullptr, perm, counts, M, K, N, G, C, true, stream);
