@@ -455,7 +455,6 @@ __device__ __forceinline__ void mn_body(
                             nct, total, sA, sB, s_tok);                                       \
   }
 WIDE_MN_KERNEL(gate_up_bf16_kernel_128, 128, true, 256)
-WIDE_MN_KERNEL(gate_up_bf16_kernel_64, 64, true, 256)
 WIDE_MN_KERNEL(gate_up_bf16_kernel_32, 32, true, 256)
 WIDE_MN_KERNEL(gate_up_bf16_kernel_16, 16, true, 256)
 WIDE_MN_KERNEL(gate_up_bf16_kernel_128_t128, 128, true, 128)
@@ -482,14 +481,21 @@ __global__ __launch_bounds__(512, 1) void gate_up_dense_bf16_kernel(
 typedef void (*MnKernel)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*,
                          const int32_t*, int, int, int, int, uint16_t*, int, int, int, int);
 
-// Token tile of the SwiGLU gate/up: 128 positions when the 256-position grid
-// (before level-0 exits) would leave CUs idle, i.e. fewer than 256 workgroups
-// with 128-channel blocks (a 256-row A side) or fewer than 1024 with 64-channel
-// blocks; channel blocks under 64 always take 256 positions.
+// Token tile of the SwiGLU gate/up. 64-channel blocks (a 128-row A side)
+// take 128 positions: measured at 50% top-k masks on the Llama3.2-3B shape,
+// G = 64, 0.246 against 0.265 ms at T = 4096, 0.481 against 0.496 at 8192 and
+// 0.99 against 1.06 at 16384. 128-channel blocks take 128 positions only when
+// the 256-position grid (before level-0 exits) has fewer than 256 tiles;
+// otherwise 256 (the Llama3.1-8B and Qwen3-14B shapes: 1.68 against 2.10 and
+// 0.71 against 0.91 ms with 128 positions; whether 64-channel blocks of 128
+// positions gain at mid sizes depends on how the active tiles fill the last
+// round: 0.132 against 0.143 ms at T = 2048 on the 3B shape, 0.184 against
+// 0.164 at T = 3072). Blocks under 64 channels take 256 positions.
 int mn_token_tile(int M, int N, int G, int CW) {
-  const long long t256 = (long long)(N / G) * (G / CW) * ((M + 255) / 256);
   if (CW < 64) return 256;
-  return t256 < (2 * CW >= 256 ? 256 : 1024) ? 128 : 256;
+  if (CW == 64) return 128;
+  const long long t256 = (long long)(N / G) * (G / CW) * ((M + 255) / 256);
+  return t256 < 256 ? 128 : 256;
 }
 
 // Tile of the plain GEMM (channel block cw x token tile tt). Measured on
@@ -553,7 +559,6 @@ hipError_t launch_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, const uint
   const int tt = mn_token_tile(T, d_ff, G, cw);
   MnKernel k = tt == 128 ? (cw == 128 ? gate_up_bf16_kernel_128_t128 : gate_up_bf16_kernel_64_t128)
                : cw == 128 ? gate_up_bf16_kernel_128
-               : cw == 64  ? gate_up_bf16_kernel_64
                : cw == 32  ? gate_up_bf16_kernel_32
                            : gate_up_bf16_kernel_16;
   return launch_mn(k, cw, tt, X, Wg, Wu, perm, counts, T, d, d_ff, G, H, zero_inactive, stream);
