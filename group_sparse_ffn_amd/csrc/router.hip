@@ -57,7 +57,15 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t0 = (int)blockIdx.x * kRtTok;
+  // XCD-aware: workgroup ids go to the 8 XCDs in turn, and XCD x takes the
+  // x-th contiguous range of token blocks, so the neighbouring blocks whose
+  // 8-byte pieces of a group's packed-bit row share a 128-byte line write it
+  // through one L2
+  const int nblk = (T + kRtTok - 1) / kRtTok;
+  const int per_xcd = (nblk + 7) / 8;
+  const int blk = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (blk >= nblk) return;
+  const int t0 = blk * kRtTok;
 
   // ---- z partials: wave w takes the 32-wide K slices [s_lo, s_hi) of D / 32;
   // every W1 fragment it loads serves the workgroup's kRtRB token blocks
@@ -137,6 +145,35 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
             xv, __builtin_bit_cast(bf16x8, *(const u32x4*)(pw[f] + 32 * s)), acc[b][f], 0, 0, 0);
     }
   }
+  // W2 rows of one chunk of kRtGC groups (2 kRtGC rows of R bf16) pass
+  // through registers into LDS; each chunk's rows are requested one step
+  // ahead (the first chunk's now, while the partial sums meet in LDS), so the
+  // products below read W2 from LDS. (Read from global memory inside the
+  // item loop they cost each wave one L2 round trip per item: about 10 of
+  // the kernel's 41 us at the Llama3.1-8B prefill shape.)
+  constexpr int kW2Vec = 2 * kRtGC * R / 8;  // 16-byte pieces of a full chunk
+  constexpr int kW2Per = (kW2Vec + kRtThreads - 1) / kRtThreads;
+  u32x4 w2r[kW2Per];
+  auto w2_pieces = [&](int g0) { return 2 * min(kRtGC, ng - g0) * R / 8; };
+  auto load_w2 = [&](int g0) {
+    const int n = w2_pieces(g0);
+    const u32x4* src = (const u32x4*)(W2 + (size_t)2 * g0 * R);
+#pragma unroll
+    for (int i = 0; i < kW2Per; ++i) w2r[i] = src[min(tid + kRtThreads * i, n - 1)];
+  };
+  // the chunk's rows in LDS, in the partial-sum array (free once z is formed)
+  uint16_t* s_w2 = reinterpret_cast<uint16_t*>(&s_part[0][0][0]);
+  static_assert(2 * kRtGC * R * 2 <= kRtWaves * kRtTok * R * 4, "a W2 chunk fits the partial sums");
+  auto store_w2 = [&](int g0) {
+    const int n = w2_pieces(g0);
+#pragma unroll
+    for (int i = 0; i < kW2Per; ++i) {
+      const int e = tid + kRtThreads * i;
+      if (e < n) *(u32x4*)(s_w2 + 8 * e) = w2r[i];
+    }
+  };
+  load_w2(0);
+
   // lane holds z for token 16 b + 4 (lane / 16) + e and output 16 f + lane % 16
 #pragma unroll
   for (int b = 0; b < kRtRB; ++b)
@@ -164,35 +201,60 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
   constexpr int KQ = R / 4;
   const int ntok = min(kRtTok, T - t0);
   const int q = lane >> 4, c16 = lane & 15;
-  lds_barrier();  // s_z complete
+  lds_barrier();  // s_z complete; the partial sums are no longer read
   for (int g0 = 0; g0 < ng; g0 += kRtGC) {
     const int gc = min(kRtGC, ng - g0);
-    const int nob = (gc + 7) / 8;  // 16-column blocks of the chunk
-    for (int it = wave; it < kRtRB * nob; it += kRtWaves) {
-      const int tb = it / nob, ob = it % nob;
-      const int col = 16 * ob + c16;  // chunk-local column: group col / 2, class col % 2
+    store_w2(g0);
+    if (g0 + kRtGC < ng) load_w2(g0 + kRtGC);
+    lds_barrier();  // the chunk's W2 rows in LDS
+    // A wave keeps one 16-token block (its z operands are read from LDS once)
+    // and takes every kWpb-th 16-column block of the chunk; the MFMA chains
+    // of its blocks run interleaved, one k-step at a time. (One item at a
+    // time, with z re-read per item, these products took about 6 us of the
+    // kernel's 40 at the Llama3.1-8B prefill shape.) Blocks past the chunk multiply zeros and
+    // store nothing.
+    static_assert(kRtWaves % kRtRB == 0, "waves per token block");
+    constexpr int kWpb = kRtWaves / kRtRB;
+    constexpr int kObMax = (2 * kRtGC / 16 + kWpb - 1) / kWpb;
+    const int tb = wave % kRtRB, ob0 = wave / kRtRB;
+    float zv[KQ];
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) zv[kk] = s_z[16 * tb + c16][KQ * q + kk];
+    uint32_t wv[kObMax][KQ / 2];
+    f32x4 acc[kObMax];
+#pragma unroll
+    for (int j = 0; j < kObMax; ++j) {
+      const int col = 16 * (ob0 + kWpb * j) + c16;  // chunk-local column: group col / 2, class col % 2
       const bool colok = col < 2 * gc;
-      // W2 row of this column (row 2 g0 stands in past the chunk; zeroed)
-      const uint32_t* pw2 =
-          (const uint32_t*)(W2 + (size_t)(2 * g0 + (colok ? col : 0)) * R + KQ * q);
-      uint32_t wv[KQ / 2];
+      // W2 row of this column from LDS (row 0 stands in past the chunk; zeroed)
+      const uint32_t* pw2 = (const uint32_t*)(s_w2 + (colok ? col : 0) * R + KQ * q);
 #pragma unroll
-      for (int i = 0; i < KQ / 2; ++i) wv[i] = colok ? pw2[i] : 0u;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < KQ / 2; ++i) wv[j][i] = colok ? pw2[i] : 0u;
+      acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) {
-        const uint32_t bits = (kk & 1) ? (wv[kk >> 1] & 0xFFFF0000u) : (wv[kk >> 1] << 16);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(s_z[16 * tb + c16][KQ * q + kk],
-                                                   __builtin_bit_cast(float, bits), acc, 0, 0, 0);
+    for (int kk = 0; kk < KQ; ++kk)
+#pragma unroll
+      for (int j = 0; j < kObMax; ++j) {
+        const uint32_t bits =
+            (kk & 1) ? (wv[j][kk >> 1] & 0xFFFF0000u) : (wv[j][kk >> 1] << 16);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[kk], __builtin_bit_cast(float, bits),
+                                                      acc[j], 0, 0, 0);
       }
+#pragma unroll
+    for (int j = 0; j < kObMax; ++j) {
+      const int col = 16 * (ob0 + kWpb * j) + c16;
+      const bool colok = col < 2 * gc;
       // lane holds tokens 16 tb + 4 q + e of column col; lane ^ 1 holds the
-      // other class of the same group and tokens
+      // other class of the same group and tokens. (A DPP quad permute here,
+      // reading the MFMA result a few cycles after the MFMA, gave wrong
+      // values with this toolchain; the permute through LDS is correct.)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float other = __shfl_xor(acc[e], 1);
+        const float other = __shfl_xor(acc[j][e], 1);
         const int t = 16 * tb + 4 * q + e;
-        if (colok && (c16 & 1) == 0) s_mask[t][col >> 1] = acc[e] >= other ? 1 : 0;
-        if (logits && colok && t < ntok) logits[((size_t)(t0 + t) * ng + g0) * 2 + col] = acc[e];
+        if (colok && (c16 & 1) == 0) s_mask[t][col >> 1] = acc[j][e] >= other ? 1 : 0;
+        if (logits && colok && t < ntok) logits[((size_t)(t0 + t) * ng + g0) * 2 + col] = acc[j][e];
       }
     }
     lds_barrier();
@@ -203,28 +265,21 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
       }
     }
     if (maskbits != nullptr) {
-      // packed bits straight from the decisions in LDS: thread (j, h) reads
-      // the 4-group words of tokens 32 h .. 32 h + 31 (consecutive threads,
-      // consecutive words: no bank conflict) and builds the bit words of
-      // groups 4 j .. 4 j + 3; tokens past T give 0 bits.
-      // maskbits[g, w] bit b = decision of token 32 w + b.
-      constexpr int kHalves = (kRtTok + 31) / 32;
-      const int nj = (gc + 3) / 4;
-      const int j = tid / kHalves, h = tid % kHalves;
-      const int nt = min(32, ntok - 32 * h);  // <= 0: the word lies past T (none stored)
-      if (tid < nj * kHalves && nt > 0) {
-        uint32_t b[4] = {0u, 0u, 0u, 0u};
-        for (int t = 0; t < nt; ++t) {
-          const uint32_t w = *(const uint32_t*)&s_mask[32 * h + t][4 * j];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) b[q] |= ((w >> (8 * q)) & 0xFFu) != 0 ? (1u << t) : 0u;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (4 * j + q < gc) maskbits[(size_t)(g0 + 4 * j + q) * words + (t0 >> 5) + h] = b[q];
+      // packed bits straight from the decisions in LDS, one wave ballot per
+      // group: lane t holds token t0 + t (a workgroup owns 64 tokens, one
+      // per lane), and the 64 decision bits are the group's two words of
+      // this workgroup. maskbits[g, w] bit b = decision of token 32 w + b;
+      // tokens past T give 0 bits and words past T are not stored.
+      static_assert(kRtTok == 64, "one token per lane");
+      for (int gl = wave; gl < gc; gl += kRtWaves) {
+        const bool bit = lane < ntok && s_mask[lane][gl] != 0;
+        const uint64_t b = __ballot(bit);
+        if (lane < 2 && 32 * lane < ntok)
+          maskbits[(size_t)(g0 + gl) * words + (t0 >> 5) + lane] =
+              (uint32_t)(lane == 0 ? b : b >> 32);
       }
     }
-    lds_barrier();  // s_mask is refilled by the next chunk
+    lds_barrier();  // s_mask and the W2 rows are refilled by the next chunk
   }
 }
 
@@ -411,8 +466,9 @@ hipError_t launch_router_bf16(const uint16_t* X, const uint16_t* W1, const uint1
   typedef void (*K)(const uint16_t*, const uint16_t*, const uint16_t*, int, int, int, int, uint8_t*,
                     float*, uint32_t*, int);
   const K k = r == 16 ? router_kernel_16 : r == 32 ? router_kernel_32 : router_kernel_64;
-  hipLaunchKernelGGL(k, dim3((T + 63) / 64), dim3(512), 0, stream, X, W1, W2, T, D, ng, act, mask,
-                     logits, maskbits, words);
+  const int nblk = (T + 63) / 64;
+  hipLaunchKernelGGL(k, dim3((nblk + 7) / 8 * 8), dim3(512), 0, stream, X, W1, W2, T, D, ng, act,
+                     mask, logits, maskbits, words);
   return hipGetLastError();
 }
 
