@@ -40,6 +40,31 @@ __device__ __forceinline__ float router_act(float a, int act) {
   return a;
 }
 
+// Copies the decisions of tokens t0 .. t0 + ntok - 1 for groups g0 .. g0 + gc
+// - 1 from the LDS tile to mask rows, VW bytes per lane (VW divides ng, gc,
+// g0 and the mask address).
+template <int VW>
+__device__ __forceinline__ void store_mask_rows(uint8_t* __restrict__ mask,
+                                                const uint8_t (*s_mask)[kRtGC], int t0, int ntok,
+                                                int ng, int g0, int gc, int tid, int nthreads) {
+  typedef uint32_t vec4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t vec2 __attribute__((ext_vector_type(2)));
+  const int per_row = gc / VW;
+  for (int e = tid; e < ntok * per_row; e += nthreads) {
+    const int t = e / per_row, c = VW * (e % per_row);
+    uint8_t* dst = mask + (size_t)(t0 + t) * ng + g0 + c;
+    const uint8_t* src = &s_mask[t][c];
+    if constexpr (VW == 16)
+      *(vec4*)dst = *(const vec4*)src;
+    else if constexpr (VW == 8)
+      *(vec2*)dst = *(const vec2*)src;
+    else if constexpr (VW == 4)
+      *(uint32_t*)dst = *(const uint32_t*)src;
+    else
+      *dst = *src;
+  }
+}
+
 template <int R, int kRtRB, int kRtWaves>
 __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
                                             const uint16_t* __restrict__ W1,
@@ -259,10 +284,20 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
     }
     lds_barrier();
     if (mask != nullptr) {
-      for (int e = tid; e < ntok * gc; e += kRtThreads) {
-        const int t = e / gc, gl = e % gc;
-        mask[(size_t)(t0 + t) * ng + g0 + gl] = s_mask[t][gl];
-      }
+      // row segments of the chunk in pieces of vw bytes: the widest of 16, 8
+      // and 4 that divides the row length and the mask address (g0 and a
+      // full chunk are multiples of 64), else single bytes. (One byte per
+      // lane these stores took about 2.4 us of the kernel at the Llama3.1-8B
+      // prefill shape.)
+      const uintptr_t am = reinterpret_cast<uintptr_t>(mask) | (uintptr_t)ng;
+      if ((am & 15) == 0)
+        store_mask_rows<16>(mask, s_mask, t0, ntok, ng, g0, gc, tid, kRtThreads);
+      else if ((am & 7) == 0)
+        store_mask_rows<8>(mask, s_mask, t0, ntok, ng, g0, gc, tid, kRtThreads);
+      else if ((am & 3) == 0)
+        store_mask_rows<4>(mask, s_mask, t0, ntok, ng, g0, gc, tid, kRtThreads);
+      else
+        store_mask_rows<1>(mask, s_mask, t0, ntok, ng, g0, gc, tid, kRtThreads);
     }
     if (maskbits != nullptr) {
       // packed bits straight from the decisions in LDS, one wave ballot per
@@ -291,7 +326,7 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
       int words) {                                                                             \
     __shared__ float s_part[NW][16 * RB][R];                                                   \
     __shared__ float s_z[16 * RB][R + 1];                                                      \
-    __shared__ uint8_t s_mask[16 * RB][kRtGC];                                                 \
+    __shared__ __attribute__((aligned(16))) uint8_t s_mask[16 * RB][kRtGC];                    \
     router_body<R, RB, NW>(X, W1, W2, T, D, ng, act, mask, logits, maskbits, words, s_part,    \
                            s_z, s_mask);                                                       \
   }
