@@ -305,13 +305,23 @@ __device__ __forceinline__ void router_body(const uint16_t* __restrict__ X,
       // per lane), and the 64 decision bits are the group's two words of
       // this workgroup. maskbits[g, w] bit b = decision of token 32 w + b;
       // tokens past T give 0 bits and words past T are not stored.
-      static_assert(kRtTok == 64, "one token per lane");
-      for (int gl = wave; gl < gc; gl += kRtWaves) {
-        const bool bit = lane < ntok && s_mask[lane][gl] != 0;
-        const uint64_t b = __ballot(bit);
-        if (lane < 2 && 32 * lane < ntok)
-          maskbits[(size_t)(g0 + gl) * words + (t0 >> 5) + lane] =
-              (uint32_t)(lane == 0 ? b : b >> 32);
+      // Wave w takes the chunk's groups 8 w .. 8 w + 7: one 8-byte LDS read
+      // per token gives its 8 decisions, 8 ballots give the 16 words, and
+      // lanes 2 i + h store word h of group 8 w + i in one instruction.
+      static_assert(kRtTok == 64 && kRtGC == 8 * kRtWaves, "one token per lane, 8 groups per wave");
+      const int gw0 = 8 * wave;
+      if (gw0 < gc) {
+        const uint64_t row8 = lane < ntok ? *(const uint64_t*)&s_mask[lane][gw0] : 0ull;
+        uint32_t word = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint64_t b = __ballot(((row8 >> (8 * i)) & 0xFFull) != 0ull);
+          if (lane == 2 * i) word = (uint32_t)b;
+          if (lane == 2 * i + 1) word = (uint32_t)(b >> 32);
+        }
+        const int gi = lane >> 1, h = lane & 1;
+        if (lane < 16 && gw0 + gi < gc && 32 * h < ntok)
+          maskbits[(size_t)(g0 + gw0 + gi) * words + (t0 >> 5) + h] = word;
       }
     }
     lds_barrier();  // s_mask and the W2 rows are refilled by the next chunk
