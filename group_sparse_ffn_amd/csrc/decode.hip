@@ -25,11 +25,15 @@
 //     workgroups and spread evenly over the CUs; workgroups past the last
 //     unit exit. Four waves split K and meet in LDS.
 //     Output: H[t, c] = silu(gate)*up, or +0.0 where token t skips the group.
-//   * down: a workgroup owns 16 output rows; it lists the 32-channel chunks
-//     whose group is in U and its eight waves split that list. Only those
-//     segments of each Wdown row are read; one writer per output. H is never
-//     read at a group no token executes (such a group may share a 32-channel
-//     chunk with an executed one when G = 16): those lanes use zeros.
+//   * down: every workgroup lists the 32-channel chunks whose group is in U;
+//     a workgroup owns 64 output rows and one of kDecodeDownSplit slices of
+//     that list, its four waves take every fourth chunk of the slice, and
+//     each H fragment feeds four 16-row blocks of Wdown. Only those segments
+//     of each Wdown row are read. The slices' fp32 partial sums are added in
+//     a fixed order by a second kernel, which rounds Y once. H is never read
+//     at a group no token executes (when G is not a multiple of 32 such a
+//     group may share a 32-channel chunk with an executed one): those lanes
+//     use zeros.
 // For one or two tokens the matrix core gains nothing and its operand layout
 // (16 rows x 64 bytes per load) costs HBM efficiency, so a second pair of
 // kernels streams whole weight rows with contiguous 1 KB loads and VALU dot
@@ -971,7 +975,8 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
                        zero_inactive ? 1 : 0);
     return hipGetLastError();
   }
-  // operand-order weights: 32-channel units (16 with G = 16) for any T
+  // operand-order weights: 32-channel units (16 when G is not a multiple of
+  // 32) for any T
   if (Wg_op != nullptr) {
     if (G % 32 == 0)
       hipLaunchKernelGGL(decode_gate_up_packed_kernel_32, dim3(d_ff / 32), dim3(kGuThreads), 0,
@@ -982,8 +987,8 @@ hipError_t launch_decode_gate_up_bf16(const uint16_t* X, const uint16_t* Wg, con
     return hipGetLastError();
   }
   // few tokens: 8-channel units (finest balance); more tokens: 32-channel
-  // units (16 with G = 16) whose gate and up operands share each activation
-  // fragment
+  // units (16 when G is not a multiple of 32) whose gate and up operands
+  // share each activation fragment
   if (T <= kDecodeSmallT)
     hipLaunchKernelGGL(decode_gate_up_kernel_8, dim3(d_ff / 8), dim3(kGuThreads), 0, stream, X, Wg,
                        Wu, mask, T, d, d_ff, G, H, zero_inactive ? 1 : 0);
