@@ -191,13 +191,13 @@ wide_status_t validate(const Args& a, bool* decode) {
 // N-axis GEMM (50% masks, graph replay): 2048^3 37.9 -> 34.5 us (N axis) and
 // 36.9 -> 33.9 us (M axis), 3072^3 M axis 58 -> 53 us, 4096^3 unchanged.
 constexpr int kOneLaunchRows = 4096;
-hipError_t reorder_rows(const uint8_t* mask, int T, int ng, int32_t* perm, int32_t* counts,
-                        int32_t* padded, uint32_t* maskbits, hipStream_t s) {
+hipError_t reorder_rows(const uint8_t* mask, int T, int ng, int tile, int32_t* perm,
+                        int32_t* counts, int32_t* padded, uint32_t* maskbits, hipStream_t s) {
   if (T <= kOneLaunchRows)
-    return wide::launch_reorder(mask, T, ng, WIDE_TOKEN_TILE, perm, counts, padded, maskbits, s);
+    return wide::launch_reorder(mask, T, ng, tile, perm, counts, padded, maskbits, s);
   hipError_t e = wide::launch_pack_mask_bits(mask, T, ng, maskbits, s);
   if (e != hipSuccess) return e;
-  return wide::launch_reorder_from_bits(maskbits, T, ng, WIDE_TOKEN_TILE, perm, counts, padded, s);
+  return wide::launch_reorder_from_bits(maskbits, T, ng, tile, perm, counts, padded, s);
 }
 
 wide_status_t run_stage(int32_t stage, const Args& a) {
@@ -220,7 +220,7 @@ wide_status_t run_stage(int32_t stage, const Args& a) {
         e = wide::launch_pack_mask_bits(a.mask, a.T, ng, maskbits, a.stream);
         return hip_status(e, "mask pack launch");
       }
-      e = reorder_rows(a.mask, a.T, ng, perm, counts, padded, maskbits, a.stream);
+      e = reorder_rows(a.mask, a.T, ng, WIDE_TOKEN_TILE, perm, counts, padded, maskbits, a.stream);
       return hip_status(e, "mask reorder launch");
     case WIDE_STAGE_GATE_UP:
       if (a.dt == WIDE_BF16)
@@ -521,7 +521,7 @@ WIDE_API wide_status_t wide_gemm_mn(const void* A, const void* B, const uint8_t*
   int32_t* padded = reinterpret_cast<int32_t*>(ws + L.padded);
   uint32_t* maskbits = reinterpret_cast<uint32_t*>(ws + L.maskbits);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = reorder_rows(mask, M, ng, perm, counts, padded, maskbits, s);
+  hipError_t e = reorder_rows(mask, M, ng, WIDE_TOKEN_TILE, perm, counts, padded, maskbits, s);
   if (e != hipSuccess) return hip_status(e, "mask reorder launch");
   e = wide::launch_gemm_mn_bf16((const uint16_t*)A, (const uint16_t*)B, perm, counts, M, K, N, G,
                                 (uint16_t*)C, s);
@@ -607,9 +607,7 @@ WIDE_API wide_status_t wide_attention_prefill(const void* Q, const void* K, cons
   int32_t* padded = reinterpret_cast<int32_t*>(ws + L.g.padded);
   uint32_t* maskbits = reinterpret_cast<uint32_t*>(ws + L.g.maskbits);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = wide::launch_pack_mask_bits(mask, T, Hk, maskbits, s);
-  if (e != hipSuccess) return hip_status(e, "mask pack launch");
-  e = wide::launch_reorder_from_bits(maskbits, T, Hk, kAttnTile, perm, counts, padded, s);
+  hipError_t e = reorder_rows(mask, T, Hk, kAttnTile, perm, counts, padded, maskbits, s);
   if (e != hipSuccess) return hip_status(e, "mask reorder launch");
   e = wide::launch_attention_prefill_bf16(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, counts, T, Hq, Hk, dh,
