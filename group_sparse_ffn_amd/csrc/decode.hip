@@ -705,6 +705,11 @@ __global__ __launch_bounds__(256) void decode_down_reduce_kernel(const float* __
 
 constexpr int kValuThreads = 256;
 constexpr int kValuWaves = kValuThreads / 64;
+// Threads of a VALU down workgroup: one token, 8 waves (two workgroups per
+// CU, so at d = 4096 each wave takes exactly one output row, and one chunk
+// list per 8 waves; measured 13.2 us against 13.4 for three 4-wave
+// workgroups per CU and 13.9 for one of 16 waves); two tokens, 4 waves.
+__host__ __device__ constexpr int down_valu_threads(int nt) { return nt == 1 ? 512 : 256; }
 
 // gate/up for T <= NT tokens. Wave items are the channels of the groups some
 // token executes; lane l reads 16 bytes at k = 8 l + 512 j of the item's gate
@@ -806,7 +811,7 @@ __device__ __forceinline__ void gate_up_valu(const uint16_t* __restrict__ X,
 // chunks are listed once, and H over them is compacted into LDS (zeros for
 // groups no token executes and for tokens past T). Lane l reads 16 bytes of
 // chunk 16 i + l / 4, piece l % 4, of the item's row.
-template <int NT>
+template <int NT, int kTh>
 __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
                                           const uint16_t* __restrict__ Wd,
                                           const uint8_t* __restrict__ mask, int T, int d, int d_ff,
@@ -815,11 +820,11 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
   constexpr int kBatch = 16;  // loads in flight per lane (a whole row of 256 live chunks)
   const int ng = d_ff / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = list_active_chunks<kValuThreads, NT>(mask, T, ng, G, d_ff / 32, s_gact, s_chunks,
-                                                      s_wave_cnt);
+  const int nch =
+      list_active_chunks<kTh, NT>(mask, T, ng, G, d_ff / 32, s_gact, s_chunks, s_wave_cnt);
   const int stride = nch * 32;  // compacted channels per token
   const int ninstr = (nch + 15) / 16;
-  const int gw = blockIdx.x * kValuWaves + wave, nw = gridDim.x * kValuWaves;
+  const int gw = blockIdx.x * (kTh / 64) + wave, nw = gridDim.x * (kTh / 64);
   const int piece = 8 * (lane & 3);
   // chunk slots past the list's end re-read its last chunk (never used), so
   // no load sits in a branch
@@ -836,7 +841,7 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
   // compacted, so the two latencies overlap (a wave without rows re-reads
   // the last row; the values are never used)
   if (nch > 0) load_row(min(gw, d - 1), 0);
-  for (int e = tid; e < NT * nch * 4; e += kValuThreads) {
+  for (int e = tid; e < NT * nch * 4; e += kTh) {
     const int t = e / (nch * 4), r = e % (nch * 4);
     const int j = r >> 2, q = r & 3;
     const int ch = (int)s_chunks[j] * 32 + 8 * q;
@@ -885,15 +890,16 @@ __device__ __forceinline__ void down_valu(const uint16_t* __restrict__ H,
     gate_up_valu<NT>(X, Wg, Wu, mask, T, d, d_ff, G, H, zero_inactive, s_groups, s_wave_cnt,    \
                      s_x);                                                                      \
   }                                                                                             \
-  __global__ __launch_bounds__(kValuThreads) void decode_down_valu_kernel_##NT(                  \
+  __global__ __launch_bounds__(down_valu_threads(NT)) void decode_down_valu_kernel_##NT(        \
       const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wd,                          \
       const uint8_t* __restrict__ mask, int T, int d, int d_ff, int G,                          \
       uint16_t* __restrict__ Y) {                                                               \
     __shared__ uint16_t s_chunks[valu_cap(NT) / 32];                                            \
     __shared__ uint8_t s_gact[valu_cap(NT) / 16];                                               \
-    __shared__ int s_wave_cnt[kValuWaves];                                                      \
+    __shared__ int s_wave_cnt[down_valu_threads(NT) / 64];                                      \
     __shared__ __attribute__((aligned(16))) uint16_t s_h[NT * valu_cap(NT)];                    \
-    down_valu<NT>(H, Wd, mask, T, d, d_ff, G, Y, s_chunks, s_gact, s_wave_cnt, s_h);           \
+    down_valu<NT, down_valu_threads(NT)>(H, Wd, mask, T, d, d_ff, G, Y, s_chunks, s_gact,       \
+                                         s_wave_cnt, s_h);                                      \
   }
 WIDE_DECODE_VALU_KERNELS(1)
 WIDE_DECODE_VALU_KERNELS(2)
@@ -1007,15 +1013,14 @@ hipError_t launch_decode_down_bf16(const uint16_t* H, const uint16_t* Wd, const 
                                    float* part, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (valu_shape(T, d, d_ff)) {
-    // waves strided over the output rows; one token: three workgroups per CU
-    // (measured best of two, three and four), two tokens: two (the LDS copy
-    // of H holds two workgroups per CU)
+    // waves strided over the output rows, two workgroups per CU (the LDS
+    // copy of H holds two per CU with two tokens)
     if (T == 1)
-      hipLaunchKernelGGL(decode_down_valu_kernel_1, dim3(3 * num_cus()), dim3(kValuThreads), 0,
-                         stream, H, Wd, mask, T, d, d_ff, G, Y);
+      hipLaunchKernelGGL(decode_down_valu_kernel_1, dim3(2 * num_cus()), dim3(down_valu_threads(1)),
+                         0, stream, H, Wd, mask, T, d, d_ff, G, Y);
     else
-      hipLaunchKernelGGL(decode_down_valu_kernel_2, dim3(2 * num_cus()), dim3(kValuThreads), 0,
-                         stream, H, Wd, mask, T, d, d_ff, G, Y);
+      hipLaunchKernelGGL(decode_down_valu_kernel_2, dim3(2 * num_cus()), dim3(down_valu_threads(2)),
+                         0, stream, H, Wd, mask, T, d, d_ff, G, Y);
     return hipGetLastError();
   }
   // G is a multiple of 16; unless it is a multiple of 32, a 32-channel chunk
