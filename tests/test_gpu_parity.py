@@ -464,6 +464,37 @@ def test_sweep_cells_cover_every_g_and_sparsity():
 
 # ----------------------------------------------------------------------------- down projection
 
+# The gate/up with 128-channel blocks and 256-position tiles over 1024-1280
+# tiles (four to five rounds of the chip, so every XCD's share holds full,
+# boundary and past-count tiles): ragged T, K of one to four 64-wide stages, a
+# group no token executes and one every token executes; Y and H against the
+# oracle, with and without H returned (past-count tiles are cleared only when
+# it is), and two calls bit-identical.
+@pytest.mark.parametrize("T,d,d_ff,G,density", [
+    (2048, 256, 16384, 128, 0.5), (2000, 192, 16384, 128, 0.5), (1100, 64, 32768, 256, 0.6),
+    (2500, 128, 16384, 128, 0.2),
+])
+def test_gate_up_many_tiles(T, d, d_ff, G, density):
+    inp = dg.random_small(53 * T + G, T, d, d_ff, G, "bf16", density, wscale=0.05)
+    m = inp["mask"].clone()
+    m[:, 3] = 0
+    m[:, 5] = 1
+    inp["mask"] = m
+    Y, H = run_ffn(inp, G)
+    Href, Yref = oracle.ffn(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], m, G)
+    assert rel_err(Y, Yref) <= TOL["bf16"]
+    assert rel_err(H, Href) <= TOL["bf16"]
+    check_h_zeros(H, m, G)
+    x = to_dev(inp)
+    a = wide.FfnCall(x["X"], x["Wg"], x["Wu"], x["Wd"], x["mask"], G)
+    a.workspace.fill_(0xFF)
+    Ya = a.run().clone()
+    Ya2 = a.run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(Ya.view(torch.int16), Ya2.view(torch.int16)), "not deterministic"
+    assert torch.equal(Ya.view(torch.int16), Y.view(torch.int16)), "H returned or not differ"
+
+
 # The down kernel on ragged shapes: T not a multiple of the 256-token tile, d
 # not a multiple of the 256-column tile, G from 64 to 512 (one to eight
 # 64-channel K-blocks per group), densities from nearly empty to full, a
