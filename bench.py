@@ -38,6 +38,7 @@ import json
 import os
 import re
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -559,7 +560,7 @@ def cpu_baseline(oracle, inp, w, target_s: float = 12.0):
     import numpy as np
     build = "gcc -O2 (prebuilt)"
     try:
-        oracle.use_library(oracle.build_native(os.path.join(ROOT, "gpurun_out", "oracle_native")))
+        oracle.use_library(oracle.build_native(tempfile.mkdtemp(prefix="wide_oracle_native_")))
         build = "gcc -O3 -march=native -fopenmp, built on this host"
     except Exception as e:  # noqa: BLE001 - report, keep the -O2 build
         log(f"native oracle build failed ({e}); timing the -O2 build")
@@ -1072,7 +1073,7 @@ def mfma_summary(directory, command, plan, split_fn):
              "The router's ratio is not 1: its second map runs v_mfma_f32_16x16x4_f32",
              "(2048 flops), which the counter counts beside the 16x16x32 bf16 instructions of",
              "the first map and this table prices at 16384.", "",
-             "```", command.replace("PMC", "SQ_INSTS_MFMA").replace("PASS", "mfma"), "```", "",
+             "```", command.replace("PMC", "SQ_INSTS_MFMA").replace("PASS", "mfma"), "```", CMD_NOTE, "",
              "| kernel | workload | counted TFLOP | algorithmic TFLOP | designed TFLOP | counted / designed |",
              "|---|---|---|---|---|---|"]
     for workload, kernel, _ in plan:
@@ -1134,7 +1135,7 @@ def busy_summary(directory, command, plan, split_fn, out_dir=None):
              "bf16 dense peak (quoted at 2.4 GHz) to the measured clock; `designed TFLOP/s`",
              "is the kernel's designed MFMA work over its duration.", "",
              "```", command.replace("PMC", "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE").replace("PASS", "busy"),
-             "```", "",
+             "```", CMD_NOTE, "",
              "| kernel | workload | duration (us) | clock (GHz) | MFMA busy | peak at clock (TFLOP/s) "
              "| designed TFLOP/s |",
              "|---|---|---|---|---|---|---|"]
@@ -1160,14 +1161,18 @@ def busy_summary(directory, command, plan, split_fn, out_dir=None):
     print(f"wrote {out}")
 
 
+CMD_NOTE = "(<repo>: the repository root; <out>: the folder the runs write to, given to --summarize.)"
+
+
 def profile_commands(steps: int):
     """The kernel-trace command and the counter-run template (PMC: the
-    counters, PASS: the output folder) of a profile run, from the repository
-    root on one MI355X."""
+    counters, PASS: the output folder) of a profile run on one MI355X. <repo>
+    is the repository root, <out> the folder the runs write to (the one later
+    given to --summarize)."""
     pre = "cd /tmp && export TMPDIR=/tmp && rocprofv3"
     run = f"-o run -- python3 <repo>/bench.py --profile --steps {steps}"
-    return (f"{pre} --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof/ktrace {run}",
-            f"{pre} --pmc PMC --output-format csv -d <repo>/gpurun_out/prof/PASS {run}")
+    return (f"{pre} --kernel-trace --stats --output-format csv -d <out>/ktrace {run}",
+            f"{pre} --pmc PMC --output-format csv -d <out>/PASS {run}")
 
 
 def summarize(directory: str, command: str, steps: int):
@@ -1199,7 +1204,7 @@ def summarize(directory: str, command: str, steps: int):
         split = split_by_plan(plan, durs)
         lines = ["# Kernel trace: Llama3.1-8B-shaped FFN (prefill T=16384, decode T=1 and T=16) "
                  "and masked GEMMs at its attention shapes",
-                 "", "Command (from the repository root, one MI355X):", "", "```", ktrace_cmd, "```", "",
+                 "", "Command (one MI355X):", "", "```", ktrace_cmd, "```", CMD_NOTE, "",
                  "Per-dispatch durations from the kernel trace, attributed to workloads by "
                  "launch order.", "",
                  "| kernel | workload | calls | median (us) | avg (us) | min (us) | max (us) |",
@@ -1257,7 +1262,7 @@ def summarize(directory: str, command: str, steps: int):
                 f"scaled by what the same counter reads for a device copy of {COPY_BYTES} bytes",
                 "in the same run.", "",
                 "```", command.replace("PMC", "FETCH_SIZE").replace("PASS", "fetch"),
-                command.replace("PMC", "WRITE_SIZE").replace("PASS", "write"), "```", "",
+                command.replace("PMC", "WRITE_SIZE").replace("PASS", "write"), "```", CMD_NOTE, "",
                 f"- FETCH_SIZE_KiB: {vals['FETCH_SIZE']:.1f}",
                 f"- WRITE_SIZE_KiB: {vals['WRITE_SIZE']:.1f}",
                 f"- fetch_scale: {scale['FETCH_SIZE']:.4f}",
@@ -1321,7 +1326,7 @@ def summarize_baselines(directory: str, command: str):
              f"two marker kernels, scaled by what each counter reads for a {COPY_BYTES}-byte",
              "device copy in the same run. Closed form: the pipeline's data-tensor traffic",
              "(masks, indices and offsets excluded), bf16 elements.", "",
-             "```", command.replace("PMC", "FETCH_SIZE"), command.replace("PMC", "WRITE_SIZE"), "```", "",
+             "```", command.replace("PMC", "FETCH_SIZE"), command.replace("PMC", "WRITE_SIZE"), "```", CMD_NOTE, "",
              "The gather reads the weight matrix (S * S * 2 bytes, on-chip-cache sized) once per",
              "token, so HBM sees two of the closed form's three p*M*N*K terms (the gathered",
              "subset written, then read by the batched product); the last two columns drop",
